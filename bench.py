@@ -1,0 +1,234 @@
+"""Benchmark of the single-GPU Ulysses sequence-parallel hot path on MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input,
+at the 64K workload (global Q [4][1][16384][32][128], K/V [4][1][16384][8][128]
+bf16; one GPU's P=4 share = 8 query heads and 2 KV heads over n = 65536):
+
+  seq2head(Q, K, V)          the first all-to-all, emulated (full 4-shard tensors)
+  attn_fwd  (rank 0 share)   O (bf16), LSE
+  seq2head(dO)               the backward's first exchange
+  attn_bwd  (rank 0 share)   dQ, dK, dV (fp32)
+  head2seq(O)                the second all-to-all (bf16)
+  head2seq(dQ, dK, dV)       the backward's second exchange (fp32)
+
+Inputs are resident in HBM before timing starts.  ``value`` is the step's
+algorithmic attention work (4*D flops per visible (query, key) pair per query
+head for the forward, 10*D for the backward) divided by the measured step
+time.  Per-call durations come from HIP events recorded on the stream the
+library launches on (torch's current stream).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Prints ONE JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2516.6     # 256 CU x 4096 flop/clk x 2.4 GHz (dense)
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def causal_pairs(n: int) -> int:
+    return n * (n + 1) // 2
+
+
+def cpu_baseline(workload, budget_s: float = 12.0):
+    """The oracle (as it stands) on a bounded sample of the same workload:
+    full causal forward rows at seeded positions, timed on the host cores."""
+    import oracle
+    import synth
+    d = synth.local_attention_inputs(workload)
+    w = d["workload"]
+    q = synth.bf16_bits_to_f64(d["q"])
+    k = synth.bf16_bits_to_f64(d["k"])
+    v = synth.bf16_bits_to_f64(d["v"])
+    gen = np.random.Generator(np.random.PCG64(12345))
+    workers = oracle.attention._workers(None)
+    done_rows, flops, spent = 0, 0.0, 0.0
+    batch = 64
+    while spent < budget_s:
+        rows = np.sort(gen.choice(w.n, size=batch, replace=False))
+        t0 = time.perf_counter()
+        oracle.attn_fwd(q, k, v, w.scale, True, rows=rows, block=16, workers=workers)
+        spent += time.perf_counter() - t0
+        flops += float(4 * w.D * w.hq * np.sum(rows + 1))
+        done_rows += batch
+    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+            "sample": f"{done_rows} seeded query rows x {w.hq} heads of the n={w.n} causal forward "
+                      f"(fp64 NumPy, {spent:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's share of the Ulysses hot path; the all-to-all is emulated on a "
+              "single device, so only --gpus 1 is supported.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import ulysses_sequence_parallelism_head_amd as U
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    U.load_library()
+    dev = torch.device("cuda:0")
+    w = synth.WORKLOADS[args.workload]
+    P, nl, n, D = w.P, w.n_local, w.n, w.D
+    hq, hkv = w.hq, w.hkv
+
+    log(f"[bench] generating workload {w.name}")
+    g = synth.streams(w.number)
+
+    def dev_bits(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q_seq = dev_bits(synth.normal_bf16(g[synth.STREAM_Q], (P, 1, nl, w.Hq_global, D)))
+    k_seq = dev_bits(synth.normal_bf16(g[synth.STREAM_K], (P, 1, nl, w.Hkv_global, D)))
+    v_seq = dev_bits(synth.normal_bf16(g[synth.STREAM_V], (P, 1, nl, w.Hkv_global, D)))
+    do_seq = dev_bits(synth.normal_bf16(g[synth.STREAM_DO], (P, 1, nl, w.Hq_global, D)))
+
+    # buffers (allocated once; the library allocates nothing)
+    bf, f32 = torch.bfloat16, torch.float32
+    q_h = torch.empty((P, 1, n, hq, D), dtype=bf, device=dev)
+    k_h = torch.empty((P, 1, n, hkv, D), dtype=bf, device=dev)
+    v_h = torch.empty((P, 1, n, hkv, D), dtype=bf, device=dev)
+    do_h = torch.empty((P, 1, n, hq, D), dtype=bf, device=dev)
+    o_h = torch.zeros((P, 1, n, hq, D), dtype=bf, device=dev)       # rank 0's slot written by attn_fwd
+    lse = torch.empty((1, hq, n), dtype=f32, device=dev)
+    dq_h = torch.zeros((P, 1, n, hq, D), dtype=f32, device=dev)
+    dk_h = torch.zeros((P, 1, n, hkv, D), dtype=f32, device=dev)
+    dv_h = torch.zeros((P, 1, n, hkv, D), dtype=f32, device=dev)
+    o_seq = torch.empty((P, 1, nl, w.Hq_global, D), dtype=bf, device=dev)
+    dq_seq = torch.empty((P, 1, nl, w.Hq_global, D), dtype=f32, device=dev)
+    dk_seq = torch.empty((P, 1, nl, w.Hkv_global, D), dtype=f32, device=dev)
+    dv_seq = torch.empty((P, 1, nl, w.Hkv_global, D), dtype=f32, device=dev)
+    ws = torch.empty(max(256, U.ulysses_attn_bwd_workspace_bytes(1, n, hq, hkv, D)), dtype=torch.uint8, device=dev)
+
+    names = ["seq2head_qkv", "attn_fwd", "seq2head_do", "attn_bwd", "head2seq_o", "head2seq_dqkv"]
+    Ev = torch.cuda.Event
+
+    def step(events=None):
+        def mark(i):
+            if events is not None:
+                events[i].record()
+        mark(0)
+        U.ulysses_repack_seq2head(q_seq, q_h)
+        U.ulysses_repack_seq2head(k_seq, k_h)
+        U.ulysses_repack_seq2head(v_seq, v_h)
+        mark(1)
+        U.ulysses_attn_fwd(q_h[0], k_h[0], v_h[0], None, w.scale, True, out=o_h[0], lse=lse)
+        mark(2)
+        U.ulysses_repack_seq2head(do_seq, do_h)
+        mark(3)
+        U.ulysses_attn_bwd(q_h[0], k_h[0], v_h[0], o_h[0], lse, do_h[0], None, w.scale, True,
+                           dq=dq_h[0], dk=dk_h[0], dv=dv_h[0], workspace=ws)
+        mark(4)
+        U.ulysses_repack_head2seq(o_h, o_seq)
+        mark(5)
+        U.ulysses_repack_head2seq(dq_h, dq_seq)
+        U.ulysses_repack_head2seq(dk_h, dk_seq)
+        U.ulysses_repack_head2seq(dv_h, dv_seq)
+        mark(6)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    log(f"[bench] timing {args.steps} steps")
+    per = {k: [] for k in names}
+    evs = [[Ev(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = []
+    for s in range(args.steps):
+        e = evs[s]
+        for i, k in enumerate(names):
+            per[k].append(e[i].elapsed_time(e[i + 1]))
+        step_ms.append(e[0].elapsed_time(e[6]))
+    ms_step = wall * 1e3 / args.steps
+    avg = {k: float(np.mean(v)) for k, v in per.items()}
+
+    pairs = causal_pairs(n)
+    fwd_flops = 4.0 * D * hq * pairs
+    bwd_flops = 10.0 * D * hq * pairs
+    bf2, f4 = 2, 4
+    bytes_qkv = 2 * bf2 * P * nl * (w.Hq_global + 2 * w.Hkv_global) * D       # read + write
+    bytes_do = 2 * bf2 * P * nl * w.Hq_global * D
+    bytes_o = bytes_do
+    bytes_dqkv = 2 * f4 * P * nl * (w.Hq_global + 2 * w.Hkv_global) * D
+    fwd_tf = fwd_flops / (avg["attn_fwd"] * 1e-3) / 1e12
+    bwd_tf = bwd_flops / (avg["attn_bwd"] * 1e-3) / 1e12
+    rep = {
+        "seq2head_qkv_GBs": bytes_qkv / (avg["seq2head_qkv"] * 1e-3) / 1e9,
+        "seq2head_do_GBs": bytes_do / (avg["seq2head_do"] * 1e-3) / 1e9,
+        "head2seq_o_GBs": bytes_o / (avg["head2seq_o"] * 1e-3) / 1e9,
+        "head2seq_dqkv_GBs": bytes_dqkv / (avg["head2seq_dqkv"] * 1e-3) / 1e9,
+    }
+    value = (fwd_flops + bwd_flops) / (ms_step * 1e-3) / 1e12
+
+    # dominant launch: the call with the largest share of the step
+    dom = max(("attn_fwd", "attn_bwd"), key=lambda k: avg[k])
+    dom_flops = fwd_flops if dom == "attn_fwd" else bwd_flops
+    achieved = dom_flops / (avg[dom] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
+
+    result = {
+        "metric": "causal attn TFLOP/s @64K, 8q/2kv heads d128 bf16; % MFMA peak; repack GB/s",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "n": n, "P": P, "q_heads": hq, "kv_heads": hkv, "head_dim": D,
+                   "global_q_shape": [P, 1, nl, w.Hq_global, D], "causal": True},
+        "breakdown_ms": {k: round(v, 4) for k, v in avg.items()},
+        "attn_fwd_tflops": round(fwd_tf, 2),
+        "attn_fwd_frac_mfma_peak": round(fwd_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+        "attn_bwd_tflops": round(bwd_tf, 2),
+        "attn_bwd_frac_mfma_peak": round(bwd_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+        "repack_GBs": {k: round(v, 1) for k, v in rep.items()},
+        "repack_frac_hbm_peak": {k: round(v / HBM_PEAK_GBS, 4) for k, v in rep.items()},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle sample)")
+        result["cpu_baseline"] = cpu_baseline(args.workload)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

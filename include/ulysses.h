@@ -1,0 +1,211 @@
+/*
+ * ulysses.h -- C ABI of the single-GPU Ulysses sequence-parallel hot path
+ * (MI355X / gfx950).
+ *
+ * The hot path is one GPU's share of an attention layer under Ulysses
+ * sequence parallelism:
+ *   1. the first all-to-all, sequence shard -> head shard, emulated on one
+ *      device as a layout permutation          (ulysses_repack_seq2head)
+ *   2. exact softmax attention over the full sequence for the heads this
+ *      GPU holds, forward with logsumexp        (ulysses_attn_fwd)
+ *      and backward for dQ, dK, dV              (ulysses_attn_bwd)
+ *   3. the second all-to-all, head shard -> sequence shard
+ *                                               (ulysses_repack_head2seq)
+ *
+ * Sources (web pages, cited by title and section):
+ *   [ALST]  "Paralelismul de Secvență Ulysses: Antrenarea modelelor AI cu
+ *           contexte de un milion de token-uri" (world.tibi.club)
+ *   [HFSUM] "Ulysses 序列平行化：突破百萬標記長上下文的訓練瓶頸"
+ *           (agents-report.net)
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every pointer is caller-owned device memory (global memory of the
+ *    current HIP device).  The library never allocates or frees device
+ *    memory, keeps no pointer after returning, and fully overwrites every
+ *    output it is given.  Inputs are never written.
+ *  - `stream` is a hipStream_t passed as void*; NULL means the default
+ *    stream.  Calls enqueue work and return without synchronising.
+ *  - Arguments are validated on the host before anything is launched; on
+ *    any error status nothing is launched and no output is touched.
+ *  - Element types: ULYSSES_DTYPE_BF16 buffers hold IEEE bfloat16 bit
+ *    patterns (uint16), ULYSSES_DTYPE_F32 buffers hold IEEE float32.
+ *  - Multi-dimensional buffers are dense and row-major (C order) in the
+ *    bracketed shape given for each argument, last index fastest.
+ *  - Zero-sized problems (B == 0, or zero tokens) are valid no-ops; pointer
+ *    arguments may then be NULL.
+ *  - Kernel faults, if any, surface at the caller's next synchronisation of
+ *    `stream` as HIP errors; ULYSSES_ERR_HIP reports a failed launch.
+ *  - The library holds no mutable global state: calls are thread-safe and
+ *    may be issued concurrently on different streams.
+ */
+#ifndef ULYSSES_H_
+#define ULYSSES_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define ULYSSES_API __attribute__((visibility("default")))
+#else
+#define ULYSSES_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ULYSSES_OK = 0,
+  ULYSSES_ERR_INVALID_ARG = 1,  /* a null pointer, a bad size, a violated constraint, misalignment, aliasing */
+  ULYSSES_ERR_UNSUPPORTED = 2,  /* valid in principle, not built: head dim, dtype combination, size limits */
+  ULYSSES_ERR_HIP = 3           /* a HIP launch failed */
+} ulysses_status_t;
+
+typedef enum {
+  ULYSSES_DTYPE_F32 = 0,
+  ULYSSES_DTYPE_BF16 = 1
+} ulysses_dtype_t;
+
+/* Version of this ABI (incremented on any incompatible change). */
+ULYSSES_API int32_t ulysses_abi_version(void);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+ULYSSES_API const char* ulysses_status_string(ulysses_status_t status);
+
+/*
+ * ulysses_repack_seq2head -- the first all-to-all of Ulysses SP, emulated.
+ *
+ * Source: [ALST] section "Mecanismul de funcționare Ulysses", step 1 (rank i
+ * holds tokens [i*n/P, (i+1)*n/P)) and step 3 (after the exchange every rank
+ * holds all positions for a subset of the heads); [HFSUM] section
+ * "Ulysses 序列平行化的原理".  Rank j's subset is the contiguous head block
+ * [j*H/P, (j+1)*H/P), and received chunks are concatenated in source-rank
+ * order, which is global token order.
+ *
+ *   src  [P][B][n_local][H][D]    the P sequence shards, rank-major
+ *   dst  [P][B][P*n_local][H/P][D]  the P head shards, rank-major
+ *   dst[j][b][i*n_local + s][h][c] = src[i][b][s][j*H/P + h][c]
+ *
+ * A pure bit copy: no arithmetic, every bit pattern (NaN payloads included)
+ * is preserved.  `dtype` only fixes the element size (2 or 4 bytes).
+ * Errors: INVALID_ARG for null src/dst (non-empty problem), P < 1, B < 0,
+ * n_local < 0, H < P or H % P != 0 (the head count may not be smaller than
+ * the shard count: [HFSUM] section "與 Ring Attention 的比較"), D < 1,
+ * an unknown dtype, pointers not aligned to the element size, or
+ * overlapping src and dst (no in-place).  UNSUPPORTED if a dimension
+ * product exceeds the 32-bit index range of the kernel (2^32 runs).
+ */
+ULYSSES_API ulysses_status_t ulysses_repack_seq2head(const void* src, void* dst,
+                                         int32_t P, int32_t B, int64_t n_local,
+                                         int32_t H, int32_t D,
+                                         ulysses_dtype_t dtype, void* stream);
+
+/*
+ * ulysses_repack_head2seq -- the second all-to-all, emulated: the exact
+ * inverse of ulysses_repack_seq2head with the same parameters.
+ *
+ * Source: [ALST] section "Mecanismul de funcționare Ulysses", step 5 (the
+ * second exchange restores the sequence-sharded layout).
+ *
+ *   src  [P][B][P*n_local][H/P][D]  the P head shards
+ *   dst  [P][B][n_local][H][D]      the P sequence shards
+ *   dst[i][b][s][j*H/P + h][c] = src[j][b][i*n_local + s][h][c]
+ *
+ * In the backward pass this same call carries dQ, dK and dV back to the
+ * sequence layout (the adjoint of a permutation is its inverse), and
+ * ulysses_repack_seq2head carries dO forward.  Errors as for seq2head.
+ */
+ULYSSES_API ulysses_status_t ulysses_repack_head2seq(const void* src, void* dst,
+                                         int32_t P, int32_t B, int64_t n_local,
+                                         int32_t H, int32_t D,
+                                         ulysses_dtype_t dtype, void* stream);
+
+/*
+ * ulysses_attn_fwd -- exact softmax attention over the full sequence for
+ * the heads resident on this GPU, with logsumexp.
+ *
+ * Source: [ALST] section "Mecanismul de funcționare Ulysses", step 4 (each
+ * rank runs ordinary scaled-dot-product attention for its heads) and its
+ * closing paragraph (heads are independent); [ALST] section "Provocarea
+ * antrenării cu secvențe lungi" (tiling keeps memory linear in n while the
+ * work stays quadratic); padding keys take no part ([ALST] section
+ * "Integrarea cu Accelerate").
+ *
+ * For batch b, query head h (KV head h / (Hq/Hkv)), query row t:
+ *   allowed keys u: (u <= t if causal) and (key_valid == NULL or key_valid[b][u] != 0)
+ *   s_u = softmax_scale * <q[b][t][h], k[b][u][kvh]>
+ *   o[b][t][h]   = sum_u softmax(s)_u v[b][u][kvh]
+ *   lse[b][h][t] = ln sum_u exp(s_u)          (natural log)
+ * A row with no allowed key gets o = 0 and lse = -inf.
+ *
+ *   q          [B][n][Hq][D]   in_dtype
+ *   k, v       [B][n][Hkv][D]  in_dtype
+ *   key_valid  [B][n] uint8 (nonzero = valid key) or NULL (all valid)
+ *   o          [B][n][Hq][D]   o_dtype             (output)
+ *   lse        [B][Hq][n]      float32             (output)
+ *
+ * Built combinations: in_dtype BF16 with o_dtype BF16 or F32 (bf16 matrix
+ * cores, fp32 accumulation and softmax); in_dtype F32 with o_dtype F32
+ * (fp32 throughout).  D must be 64 or 128.
+ * Errors: INVALID_ARG for null pointers (non-empty problem), B < 0, n < 0,
+ * Hq < 1, Hkv < 1, Hq % Hkv != 0, a non-finite scale, causal not 0/1,
+ * q/k/v/o not 16-byte aligned, lse not 4-byte aligned, or an output
+ * overlapping any input or the other output.  UNSUPPORTED for other D or
+ * dtype combinations, or n*max(Hq,Hkv)*D >= 2^40 elements.
+ */
+ULYSSES_API ulysses_status_t ulysses_attn_fwd(const void* q, const void* k, const void* v,
+                                  const uint8_t* key_valid,
+                                  void* o, float* lse,
+                                  int32_t B, int64_t n, int32_t Hq, int32_t Hkv, int32_t D,
+                                  float softmax_scale, int32_t causal,
+                                  ulysses_dtype_t in_dtype, ulysses_dtype_t o_dtype,
+                                  void* stream);
+
+/*
+ * Bytes of device workspace ulysses_attn_bwd needs for this problem
+ * (the per-row dot products dO.O, float32 [B][Hq][n], rounded up to 256 B).
+ */
+ULYSSES_API size_t ulysses_attn_bwd_workspace_bytes(int32_t B, int64_t n, int32_t Hq, int32_t Hkv, int32_t D);
+
+/*
+ * ulysses_attn_bwd -- gradients of sum(o * dout) with respect to q, k, v.
+ *
+ * Source: the operation is the backward of ulysses_attn_fwd; the pages do
+ * not spell it out (they train with it: [HFSUM] section "最佳實踐與效能結果").
+ * The probabilities are recomputed from q, k and lse (memory linear in n,
+ * [ALST] section "Provocarea antrenării cu secvențe lungi"):
+ *   P = exp(s - lse), dV = P^T dO, dP = dO V^T, Dl = rowsum(dO * O),
+ *   dS = P * (dP - Dl), dQ = scale * dS K, dK = scale * dS^T Q,
+ * with dK and dV summed over the query heads sharing a KV head.
+ *
+ *   q, k, v, key_valid   as for ulysses_attn_fwd (in_dtype)
+ *   o          [B][n][Hq][D]   o_dtype   the forward output
+ *   lse        [B][Hq][n]      float32   the forward logsumexp
+ *   dout       [B][n][Hq][D]   in_dtype  gradient of the output
+ *   dq         [B][n][Hq][D]   float32   (output, overwritten)
+ *   dk, dv     [B][n][Hkv][D]  float32   (outputs, overwritten)
+ *   workspace  device scratch of at least
+ *              ulysses_attn_bwd_workspace_bytes(...) bytes, 256-byte
+ *              aligned; contents on entry are ignored, on exit undefined.
+ *
+ * Built combinations: in_dtype BF16 with o_dtype BF16 or F32; D 64 or 128.
+ * Errors: as ulysses_attn_fwd, plus INVALID_ARG for a null or too small
+ * workspace, misaligned dq/dk/dv (16 B) or workspace (256 B), and any
+ * output (dq, dk, dv, workspace) overlapping an input or another output.
+ */
+ULYSSES_API ulysses_status_t ulysses_attn_bwd(const void* q, const void* k, const void* v,
+                                  const uint8_t* key_valid,
+                                  const void* o, const float* lse, const void* dout,
+                                  float* dq, float* dk, float* dv,
+                                  void* workspace, size_t workspace_bytes,
+                                  int32_t B, int64_t n, int32_t Hq, int32_t Hkv, int32_t D,
+                                  float softmax_scale, int32_t causal,
+                                  ulysses_dtype_t in_dtype, ulysses_dtype_t o_dtype,
+                                  void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ULYSSES_H_ */

@@ -1,0 +1,122 @@
+"""The C-ABI library on the host (no GPU needed): it loads, exports every
+symbol include/ulysses.h declares (and nothing else), and its host-side
+argument validation returns the documented status before any launch."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import ulysses_sequence_parallelism_head_amd as U
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ulysses.h")
+
+OK, INVALID, UNSUPPORTED = 0, 1, 2
+BF16, F32 = 1, 0
+
+
+def declared_symbols():
+    text = open(HEADER, encoding="utf-8").read()
+    return sorted(set(re.findall(r"ULYSSES_API\s+[\w\s\*]+?\b(ulysses_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return U.load_library()
+
+
+def test_header_declares_the_boundary():
+    syms = declared_symbols()
+    for name in ("ulysses_repack_seq2head", "ulysses_repack_head2seq", "ulysses_attn_fwd", "ulysses_attn_bwd"):
+        assert name in syms
+    assert set(syms) == set(U.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", U.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = sorted(l.split()[-1] for l in out.splitlines() if " T " in l and "ulysses_" in l)
+    assert exported == declared_symbols()
+    for name in declared_symbols():
+        assert hasattr(lib, name)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.ulysses_abi_version() == 1
+    for s in range(4):
+        assert lib.ulysses_status_string(s)
+    assert lib.ulysses_status_string(99) == b"unknown status"
+
+
+# --- validation paths: every call below is rejected before any launch
+FAKE = ctypes.c_void_p(0x10000)        # never dereferenced: the calls fail validation first
+FAKE2 = ctypes.c_void_p(0x20000000)
+
+
+@pytest.mark.parametrize("P,B,nl,H,D,dt,expect", [
+    (4, 1, 16, 2, 128, BF16, INVALID),   # H < P
+    (4, 1, 16, 6, 128, BF16, INVALID),   # H % P != 0
+    (0, 1, 16, 4, 128, BF16, INVALID),   # P < 1
+    (2, -1, 16, 4, 128, BF16, INVALID),  # B < 0
+    (2, 1, -3, 4, 128, BF16, INVALID),   # n_local < 0
+    (2, 1, 16, 4, 0, BF16, INVALID),     # D < 1
+    (2, 1, 16, 4, 8, 7, INVALID),        # unknown dtype
+    (2, 0, 16, 4, 8, BF16, OK),          # empty: no-op
+    (2, 1, 0, 4, 8, BF16, OK),           # empty: no-op
+])
+def test_repack_validation(lib, P, B, nl, H, D, dt, expect):
+    for fn in (lib.ulysses_repack_seq2head, lib.ulysses_repack_head2seq):
+        assert fn(FAKE, FAKE2, P, B, nl, H, D, dt, None) == expect
+
+
+def test_repack_null_and_overlap(lib):
+    assert lib.ulysses_repack_seq2head(None, FAKE2, 2, 1, 4, 4, 8, BF16, None) == INVALID
+    assert lib.ulysses_repack_seq2head(FAKE, None, 2, 1, 4, 4, 8, BF16, None) == INVALID
+    # src and dst ranges overlap (in-place not allowed)
+    assert lib.ulysses_repack_seq2head(FAKE, ctypes.c_void_p(0x10000 + 64), 2, 1, 4, 4, 8, BF16, None) == INVALID
+    # misaligned for the element size
+    assert lib.ulysses_repack_seq2head(ctypes.c_void_p(0x10001), FAKE2, 2, 1, 4, 4, 8, BF16, None) == INVALID
+
+
+def _fwd(lib, q=FAKE, k=ctypes.c_void_p(0x1000000), v=ctypes.c_void_p(0x2000000), valid=None,
+         o=ctypes.c_void_p(0x3000000), lse=ctypes.c_void_p(0x4000000), B=1, n=64, Hq=8, Hkv=2, D=128,
+         scale=0.1, causal=1, it=BF16, ot=BF16):
+    return lib.ulysses_attn_fwd(q, k, v, valid, o, lse, B, n, Hq, Hkv, D, scale, causal, it, ot, None)
+
+
+def test_fwd_validation(lib):
+    assert _fwd(lib, D=96) == UNSUPPORTED
+    assert _fwd(lib, it=F32, ot=BF16) == UNSUPPORTED
+    assert _fwd(lib, Hq=6, Hkv=4) == INVALID
+    assert _fwd(lib, Hkv=0) == INVALID
+    assert _fwd(lib, n=-1) == INVALID
+    assert _fwd(lib, scale=float("nan")) == INVALID
+    assert _fwd(lib, scale=float("inf")) == INVALID
+    assert _fwd(lib, causal=2) == INVALID
+    assert _fwd(lib, q=None) == INVALID
+    assert _fwd(lib, lse=None) == INVALID
+    assert _fwd(lib, q=ctypes.c_void_p(0x10008)) == INVALID               # not 16-byte aligned
+    assert _fwd(lib, o=ctypes.c_void_p(0x1000000 + 256)) == INVALID       # o overlaps k
+    assert _fwd(lib, lse=ctypes.c_void_p(0x3000000 + 64)) == INVALID      # lse overlaps o
+    assert _fwd(lib, B=0) == OK                                           # empty
+    assert _fwd(lib, n=0, q=None, k=None, v=None, o=None, lse=None) == OK
+
+
+def _bwd(lib, ws=ctypes.c_void_p(0x9000000), wsb=1 << 20, dq=ctypes.c_void_p(0x6000000), it=BF16, D=128, n=64):
+    return lib.ulysses_attn_bwd(FAKE, ctypes.c_void_p(0x1000000), ctypes.c_void_p(0x2000000), None,
+                                ctypes.c_void_p(0x3000000), ctypes.c_void_p(0x4000000), ctypes.c_void_p(0x5000000),
+                                dq, ctypes.c_void_p(0x7000000), ctypes.c_void_p(0x8000000), ws, wsb,
+                                1, n, 8, 2, D, 0.1, 1, it, BF16, None)
+
+
+def test_bwd_validation(lib):
+    need = lib.ulysses_attn_bwd_workspace_bytes(1, 64, 8, 2, 128)
+    assert need == 64 * 8 * 4 and need % 256 == 0
+    assert lib.ulysses_attn_bwd_workspace_bytes(0, 64, 8, 2, 128) == 0
+    assert _bwd(lib, wsb=need - 1) == INVALID
+    assert _bwd(lib, ws=None) == INVALID
+    assert _bwd(lib, ws=ctypes.c_void_p(0x9000000 + 16)) == INVALID        # workspace not 256-byte aligned
+    assert _bwd(lib, dq=ctypes.c_void_p(0x5000000 + 64)) == INVALID        # dq overlaps dout
+    assert _bwd(lib, it=F32) == UNSUPPORTED
+    assert _bwd(lib, D=80) == UNSUPPORTED

@@ -1,0 +1,144 @@
+"""GPU parity of the attention backward (dQ, dK, dV in float32) against the
+fp64 oracle, max-abs 1e-2, on the same bf16-rounded inputs.
+
+The oracle evaluates the backward with its own O and LSE; the GPU path uses
+its forward's O (bf16 or float32 output) and LSE, as a training step would.
+Full-size documents workload (n = 98304): dQ on stratified query rows and
+dK/dV on key rows near the end of the sequence (where the oracle needs few
+rows), plus exact properties at every key: padding keys get exactly zero
+dK/dV.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import ulysses_sequence_parallelism_head_amd as U
+from tests.gpu_helpers import say, bits_to_device, to_f64, to_host_f64, assert_close
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(seed, n, Hq, Hkv, D, masked):
+    g = synth.streams(seed)
+    q = synth.normal_bf16(g[0], (1, n, Hq, D))
+    k = synth.normal_bf16(g[1], (1, n, Hkv, D))
+    v = synth.normal_bf16(g[2], (1, n, Hkv, D))
+    do = synth.normal_bf16(g[3], (1, n, Hq, D))
+    valid = None
+    if masked:
+        valid, _ = synth.document_valid(g[4], n, 4, max(1, n // 3))
+        valid = valid.reshape(1, n)
+    return q, k, v, do, valid
+
+
+def _gpu_fwd_bwd(q, k, v, do, valid, scale, causal, o_dtype):
+    tq, tk, tv, tdo = bits_to_device(q), bits_to_device(k), bits_to_device(v), bits_to_device(do)
+    tval = None if valid is None else torch.from_numpy(valid).to("cuda:0")
+    o, lse = U.ulysses_attn_fwd(tq, tk, tv, tval, scale, causal, o_dtype=o_dtype)
+    dq, dk, dv = U.ulysses_attn_bwd(tq, tk, tv, o, lse, tdo, tval, scale, causal)
+    torch.cuda.synchronize()
+    return to_host_f64(dq), to_host_f64(dk), to_host_f64(dv)
+
+
+CASES = [
+    # n, Hq, Hkv, D, causal, masked
+    (1, 1, 1, 128, True, False),
+    (33, 4, 1, 128, True, False),
+    (130, 8, 2, 128, True, True),
+    (200, 2, 2, 64, True, False),
+    (257, 4, 4, 64, False, True),
+    (1000, 8, 2, 128, True, False),
+    (999, 6, 2, 128, True, True),     # g = 3
+    (600, 16, 2, 128, True, False),   # g = 8
+    (2048, 8, 2, 128, True, True),
+]
+
+
+@pytest.mark.parametrize("n,Hq,Hkv,D,causal,masked", CASES)
+@pytest.mark.parametrize("o_dtype", [torch.float32, torch.bfloat16])
+def test_bwd_small(n, Hq, Hkv, D, causal, masked, o_dtype):
+    say(f"bwd n={n} Hq={Hq} Hkv={Hkv} D={D} causal={causal} masked={masked} o={o_dtype}")
+    q, k, v, do, valid = _inputs(3 * n + Hq, n, Hq, Hkv, D, masked)
+    scale = D ** -0.5
+    dQ, dK, dV, _, _ = oracle.attn_bwd(to_f64(q), to_f64(k), to_f64(v), to_f64(do), scale, causal, valid)
+    dq, dk, dv = _gpu_fwd_bwd(q, k, v, do, valid, scale, causal, o_dtype)
+    assert_close("dQ", dq, dQ, 1e-2)
+    assert_close("dK", dk, dK, 1e-2)
+    assert_close("dV", dv, dV, 1e-2)
+
+
+def test_bwd_8k_docs_full():
+    """The documents workload's shapes at n = 8192 (8q/2kv, d128, padding
+    keys masked): every element of dQ, dK, dV."""
+    say("bwd documents workload at n=8192, full")
+    d = synth.local_attention_inputs(4, n=8192)
+    w = d["workload"]
+    valid = d["valid"]
+    dQ, dK, dV, _, _ = oracle.attn_bwd(to_f64(d["q"]), to_f64(d["k"]), to_f64(d["v"]), to_f64(d["do"]),
+                                       w.scale, True, valid)
+    dq, dk, dv = _gpu_fwd_bwd(d["q"], d["k"], d["v"], d["do"], valid, w.scale, True, torch.bfloat16)
+    assert_close("dQ", dq, dQ, 1e-2)
+    assert_close("dK", dk, dK, 1e-2)
+    assert_close("dV", dv, dV, 1e-2)
+
+
+def test_bwd_96k_docs_workload_sampled():
+    """Workload 4 at full size (n = 98304): dQ on stratified rows, dK/dV on
+    key rows in the last 1024 positions; zero dK/dV at every padding key."""
+    say("bwd workload 4 (96K documents) sampled")
+    d = synth.local_attention_inputs(4)
+    w = d["workload"]
+    valid = d["valid"]
+    q_rows = synth.stratified_rows(d["row_gen"], w.n, 40, valid[0])
+    k_rows = synth.sample_rows(d["row_gen"], w.n, 12, extra=(w.n - 1, w.n - 2, w.n - 1024))
+    k_rows = k_rows[k_rows >= w.n - 1024]
+    dq, dk, dv = _gpu_fwd_bwd(d["q"], d["k"], d["v"], d["do"], valid, w.scale, True, torch.bfloat16)
+    pad = valid[0] == 0
+    assert np.all(dk[0, pad] == 0.0) and np.all(dv[0, pad] == 0.0)
+    dQs, dKs, dVs = oracle.attn_bwd_sampled(to_f64(d["q"]), to_f64(d["k"]), to_f64(d["v"]), to_f64(d["do"]),
+                                            w.scale, True, valid, q_rows=q_rows, k_rows=k_rows)
+    assert_close("dQ rows", dq[:, q_rows], dQs, 1e-2)
+    assert_close("dK rows", dk[:, k_rows], dKs, 1e-2)
+    assert_close("dV rows", dv[:, k_rows], dVs, 1e-2)
+
+
+def test_bwd_deterministic():
+    say("bwd determinism")
+    q, k, v, do, valid = _inputs(77, 900, 8, 2, 128, True)
+    a = _gpu_fwd_bwd(q, k, v, do, valid, 0.1, True, torch.bfloat16)
+    b = _gpu_fwd_bwd(q, k, v, do, valid, 0.1, True, torch.bfloat16)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_bwd_pipeline_matches_unsharded():
+    """Sharded path: seq2head(Q, K, V, dO) -> fwd/bwd per rank ->
+    head2seq(dQ, dK, dV) equals the oracle's unsharded gradients (1e-2)."""
+    say("bwd sharded pipeline P=4, n=1024, 32q/8kv")
+    P, n, Hq, Hkv, D = 4, 1024, 32, 8, 128
+    g = synth.streams(31)
+    nl = n // P
+    qs = synth.normal_bf16(g[0], (P, 1, nl, Hq, D))
+    ks = synth.normal_bf16(g[1], (P, 1, nl, Hkv, D))
+    vs = synth.normal_bf16(g[2], (P, 1, nl, Hkv, D))
+    dos = synth.normal_bf16(g[3], (P, 1, nl, Hq, D))
+    scale = D ** -0.5
+    qh, kh, vh, doh = (U.ulysses_repack_seq2head(bits_to_device(x)) for x in (qs, ks, vs, dos))
+    dqs, dks, dvs = [], [], []
+    for j in range(P):
+        o, lse = U.ulysses_attn_fwd(qh[j], kh[j], vh[j], None, scale, True)
+        dq, dk, dv = U.ulysses_attn_bwd(qh[j], kh[j], vh[j], o, lse, doh[j], None, scale, True)
+        dqs.append(dq)
+        dks.append(dk)
+        dvs.append(dv)
+    dq_seq = U.ulysses_repack_head2seq(torch.stack(dqs))
+    dk_seq = U.ulysses_repack_head2seq(torch.stack(dks))
+    dv_seq = U.ulysses_repack_head2seq(torch.stack(dvs))
+    torch.cuda.synchronize()
+    dQ, dK, dV, _, _ = oracle.attn_bwd(to_f64(oracle.unshard(qs)), to_f64(oracle.unshard(ks)),
+                                       to_f64(oracle.unshard(vs)), to_f64(oracle.unshard(dos)), scale, True)
+    assert_close("dQ", oracle.unshard(to_host_f64(dq_seq)), dQ, 1e-2)
+    assert_close("dK", oracle.unshard(to_host_f64(dk_seq)), dK, 1e-2)
+    assert_close("dV", oracle.unshard(to_host_f64(dv_seq)), dV, 1e-2)

@@ -1,0 +1,201 @@
+"""Python binding of libulysses, the C-ABI HIP library of the single-GPU
+Ulysses sequence-parallel hot path (MI355X / gfx950).
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+PyTorch supplies device memory and the current stream; outputs not passed
+in are allocated here with ``torch.empty``.  The functions carry the C
+names and follow ``include/ulysses.h``; status codes become exceptions:
+INVALID_ARG -> ValueError, UNSUPPORTED -> NotImplementedError,
+HIP -> RuntimeError.
+
+There is no fallback: if ``libulysses.so`` is missing, importing the library
+raises ``ImportError`` (build it with ``python -m
+ulysses_sequence_parallelism_head_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libulysses.so")
+
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3
+
+_lib = None
+
+_SIGS = {
+    "ulysses_abi_version": (ctypes.c_int32, []),
+    "ulysses_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "ulysses_repack_seq2head": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                               ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int,
+                                               ctypes.c_void_p]),
+    "ulysses_repack_head2seq": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                               ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int,
+                                               ctypes.c_void_p]),
+    "ulysses_attn_fwd": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
+                                        ctypes.c_int32, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
+    "ulysses_attn_bwd_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                                                           ctypes.c_int32, ctypes.c_int32]),
+    "ulysses_attn_bwd": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_size_t,
+                                        ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_void_p]),
+}
+
+EXPORTED = tuple(_SIGS)
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libulysses.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} not found: build it with `python -m ulysses_sequence_parallelism_head_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int, what: str) -> None:
+    if status == OK:
+        return
+    msg = f"{what}: {load_library().ulysses_status_string(status).decode()}"
+    if status == ERR_INVALID_ARG:
+        raise ValueError(msg)
+    if status == ERR_UNSUPPORTED:
+        raise NotImplementedError(msg)
+    raise RuntimeError(msg)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need_contig_cuda(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous and on the GPU")
+
+
+def ulysses_abi_version() -> int:
+    return int(load_library().ulysses_abi_version())
+
+
+def ulysses_repack_seq2head(src: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """src ``[P][B][n_local][H][D]`` -> ``[P][B][P*n_local][H/P][D]`` (first exchange)."""
+    lib = load_library()
+    _need_contig_cuda(src, out)
+    P, B, nl, H, D = src.shape
+    if H % P != 0 or H < P:
+        _check(ERR_INVALID_ARG, "ulysses_repack_seq2head")
+    if out is None:
+        out = torch.empty((P, B, P * nl, H // P, D), dtype=src.dtype, device=src.device)
+    elif tuple(out.shape) != (P, B, P * nl, H // P, D) or out.dtype != src.dtype:
+        raise ValueError("out has the wrong shape or dtype")
+    _check(lib.ulysses_repack_seq2head(_ptr(src), _ptr(out), P, B, nl, H, D, _dtype_code(src), _stream(src.device)),
+           "ulysses_repack_seq2head")
+    return out
+
+
+def ulysses_repack_head2seq(src: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """src ``[P][B][n][H/P][D]`` -> ``[P][B][n/P][H][D]`` (second exchange)."""
+    lib = load_library()
+    _need_contig_cuda(src, out)
+    P, B, n, hp, D = src.shape
+    if n % P != 0:
+        _check(ERR_INVALID_ARG, "ulysses_repack_head2seq")
+    nl, H = n // P, hp * P
+    if out is None:
+        out = torch.empty((P, B, nl, H, D), dtype=src.dtype, device=src.device)
+    elif tuple(out.shape) != (P, B, nl, H, D) or out.dtype != src.dtype:
+        raise ValueError("out has the wrong shape or dtype")
+    _check(lib.ulysses_repack_head2seq(_ptr(src), _ptr(out), P, B, nl, H, D, _dtype_code(src), _stream(src.device)),
+           "ulysses_repack_head2seq")
+    return out
+
+
+def ulysses_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, key_valid: torch.Tensor | None = None,
+                     softmax_scale: float | None = None, causal: bool = True, o_dtype: torch.dtype | None = None,
+                     out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """Attention forward.  q ``[B][n][Hq][D]``, k/v ``[B][n][Hkv][D]``,
+    key_valid ``[B][n]`` uint8 or None.  Returns ``(o, lse)``; lse is
+    float32 ``[B][Hq][n]`` in natural log."""
+    lib = load_library()
+    _need_contig_cuda(q, k, v, key_valid, out, lse)
+    B, n, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if k.shape != v.shape or k.dtype != q.dtype or v.dtype != q.dtype or k.shape[0] != B or k.shape[1] != n:
+        raise ValueError("k, v must be [B][n][Hkv][D] with q's dtype")
+    if key_valid is not None and (key_valid.dtype != torch.uint8 or tuple(key_valid.shape) != (B, n)):
+        raise ValueError("key_valid must be uint8 [B][n]")
+    scale = D ** -0.5 if softmax_scale is None else float(softmax_scale)
+    o_dtype = q.dtype if o_dtype is None else o_dtype
+    if out is None:
+        out = torch.empty((B, n, Hq, D), dtype=o_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, n), dtype=torch.float32, device=q.device)
+    _check(lib.ulysses_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(key_valid), _ptr(out), _ptr(lse), B, n, Hq, Hkv, D,
+                                scale, int(bool(causal)), _dtype_code(q), _dtype_code(out), _stream(q.device)),
+           "ulysses_attn_fwd")
+    return out, lse
+
+
+def ulysses_attn_bwd_workspace_bytes(B: int, n: int, Hq: int, Hkv: int, D: int) -> int:
+    return int(load_library().ulysses_attn_bwd_workspace_bytes(B, n, Hq, Hkv, D))
+
+
+def ulysses_attn_bwd(q, k, v, o, lse, dout, key_valid=None, softmax_scale=None, causal=True,
+                     dq=None, dk=None, dv=None, workspace=None):
+    """Attention backward.  Returns float32 ``(dq, dk, dv)``."""
+    lib = load_library()
+    _need_contig_cuda(q, k, v, o, lse, dout, key_valid, dq, dk, dv, workspace)
+    B, n, Hq, D = q.shape
+    Hkv = k.shape[2]
+    scale = D ** -0.5 if softmax_scale is None else float(softmax_scale)
+    dev = q.device
+    dq = torch.empty((B, n, Hq, D), dtype=torch.float32, device=dev) if dq is None else dq
+    dk = torch.empty((B, n, Hkv, D), dtype=torch.float32, device=dev) if dk is None else dk
+    dv = torch.empty((B, n, Hkv, D), dtype=torch.float32, device=dev) if dv is None else dv
+    wsb = ulysses_attn_bwd_workspace_bytes(B, n, Hq, Hkv, D)
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+    _check(lib.ulysses_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(key_valid), _ptr(o), _ptr(lse), _ptr(dout),
+                                _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                B, n, Hq, Hkv, D, scale, int(bool(causal)), _dtype_code(q), _dtype_code(o),
+                                _stream(dev)),
+           "ulysses_attn_bwd")
+    return dq, dk, dv
+
+
+__all__ = [
+    "load_library", "EXPORTED", "LIB_PATH", "ulysses_abi_version", "ulysses_repack_seq2head",
+    "ulysses_repack_head2seq", "ulysses_attn_fwd", "ulysses_attn_bwd", "ulysses_attn_bwd_workspace_bytes",
+]

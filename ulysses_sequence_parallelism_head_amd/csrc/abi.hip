@@ -1,0 +1,165 @@
+// abi.hip -- the exported C entry points of libulysses: host-side argument
+// validation, then dispatch to the kernels' launchers.  Declarations and the
+// contract of every call are in include/ulysses.h.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/ulysses.h"
+#include "internal.h"
+
+namespace {
+
+using ulysses::AttnShape;
+
+constexpr int32_t kAbiVersion = 1;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Half-open byte ranges [a, a+na) and [b, b+nb) intersect.
+bool overlap(const void* a, uint64_t na, const void* b, uint64_t nb) {
+  if (a == nullptr || b == nullptr || na == 0 || nb == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+uint32_t elem_size(ulysses_dtype_t t) { return t == ULYSSES_DTYPE_BF16 ? 2u : 4u; }
+bool known_dtype(ulysses_dtype_t t) { return t == ULYSSES_DTYPE_F32 || t == ULYSSES_DTYPE_BF16; }
+
+ulysses_status_t from_hip(hipError_t e) { return e == hipSuccess ? ULYSSES_OK : ULYSSES_ERR_HIP; }
+
+ulysses_status_t repack(const void* src, void* dst, int32_t P, int32_t B, int64_t n_local, int32_t H, int32_t D,
+                        ulysses_dtype_t dtype, void* stream, int seq2head) {
+  if (P < 1 || B < 0 || n_local < 0 || H < 1 || D < 1) return ULYSSES_ERR_INVALID_ARG;
+  if (H < P || H % P != 0) return ULYSSES_ERR_INVALID_ARG;
+  if (!known_dtype(dtype)) return ULYSSES_ERR_INVALID_ARG;
+  if (B == 0 || n_local == 0) return ULYSSES_OK;
+  if (src == nullptr || dst == nullptr) return ULYSSES_ERR_INVALID_ARG;
+  const uint32_t es = elem_size(dtype);
+  if (!aligned(src, es) || !aligned(dst, es)) return ULYSSES_ERR_INVALID_ARG;
+  const uint64_t run_bytes = uint64_t(H / P) * uint64_t(D) * es;
+  const uint64_t runs = uint64_t(P) * uint64_t(B) * uint64_t(n_local) * uint64_t(P);
+  if (run_bytes >= (uint64_t(1) << 32) || runs >= (uint64_t(1) << 32)) return ULYSSES_ERR_UNSUPPORTED;
+  const uint64_t total = runs * run_bytes;
+  if (overlap(src, total, dst, total)) return ULYSSES_ERR_INVALID_ARG;
+  uint32_t vec = 16;
+  while (vec > es && (run_bytes % vec != 0 || !aligned(src, vec) || !aligned(dst, vec))) vec >>= 1;
+  if (total / vec >= (uint64_t(1) << 32)) return ULYSSES_ERR_UNSUPPORTED;
+  return from_hip(ulysses::launch_repack(src, dst, uint32_t(P), uint32_t(B), uint32_t(n_local), uint32_t(run_bytes),
+                                         vec, seq2head, static_cast<hipStream_t>(stream)));
+}
+
+// Shared checks of the attention calls.  Returns OK, or the error status;
+// sets *empty for zero-sized problems.
+ulysses_status_t check_attn_shape(int32_t B, int64_t n, int32_t Hq, int32_t Hkv, int32_t D, float scale,
+                                  int32_t causal, ulysses_dtype_t in_dtype, ulysses_dtype_t o_dtype, bool* empty) {
+  *empty = false;
+  if (B < 0 || n < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ULYSSES_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return ULYSSES_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return ULYSSES_ERR_INVALID_ARG;
+  if (!known_dtype(in_dtype) || !known_dtype(o_dtype)) return ULYSSES_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return ULYSSES_ERR_UNSUPPORTED;
+  if (n >= (int64_t(1) << 31) - 256) return ULYSSES_ERR_UNSUPPORTED;
+  const int64_t Hmax = Hq > Hkv ? Hq : Hkv;
+  if (int64_t(B) * n * Hmax * D >= (int64_t(1) << 40)) return ULYSSES_ERR_UNSUPPORTED;
+  if (B == 0 || n == 0) *empty = true;
+  return ULYSSES_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t ulysses_abi_version(void) { return kAbiVersion; }
+
+const char* ulysses_status_string(ulysses_status_t status) {
+  switch (status) {
+    case ULYSSES_OK: return "ok";
+    case ULYSSES_ERR_INVALID_ARG: return "invalid argument";
+    case ULYSSES_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ULYSSES_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+ulysses_status_t ulysses_repack_seq2head(const void* src, void* dst, int32_t P, int32_t B, int64_t n_local,
+                                         int32_t H, int32_t D, ulysses_dtype_t dtype, void* stream) {
+  return repack(src, dst, P, B, n_local, H, D, dtype, stream, 1);
+}
+
+ulysses_status_t ulysses_repack_head2seq(const void* src, void* dst, int32_t P, int32_t B, int64_t n_local,
+                                         int32_t H, int32_t D, ulysses_dtype_t dtype, void* stream) {
+  return repack(src, dst, P, B, n_local, H, D, dtype, stream, 0);
+}
+
+ulysses_status_t ulysses_attn_fwd(const void* q, const void* k, const void* v, const uint8_t* key_valid, void* o,
+                                  float* lse, int32_t B, int64_t n, int32_t Hq, int32_t Hkv, int32_t D,
+                                  float softmax_scale, int32_t causal, ulysses_dtype_t in_dtype,
+                                  ulysses_dtype_t o_dtype, void* stream) {
+  bool empty = false;
+  ulysses_status_t st = check_attn_shape(B, n, Hq, Hkv, D, softmax_scale, causal, in_dtype, o_dtype, &empty);
+  if (st != ULYSSES_OK || empty) return st;
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || lse == nullptr) return ULYSSES_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return ULYSSES_ERR_INVALID_ARG;
+  const bool bf16_in = in_dtype == ULYSSES_DTYPE_BF16;
+  if (!bf16_in && o_dtype != ULYSSES_DTYPE_F32) return ULYSSES_ERR_UNSUPPORTED;
+  const uint64_t ei = elem_size(in_dtype), eo = elem_size(o_dtype);
+  const uint64_t nq = uint64_t(B) * n * Hq * D, nkv = uint64_t(B) * n * Hkv * D;
+  const uint64_t bo = nq * eo, bl = uint64_t(B) * Hq * n * 4;
+  const void* ins[4] = {q, k, v, key_valid};
+  const uint64_t inb[4] = {nq * ei, nkv * ei, nkv * ei, key_valid ? uint64_t(B) * n : 0};
+  for (int i = 0; i < 4; ++i)
+    if (overlap(o, bo, ins[i], inb[i]) || overlap(lse, bl, ins[i], inb[i])) return ULYSSES_ERR_INVALID_ARG;
+  if (overlap(o, bo, lse, bl)) return ULYSSES_ERR_INVALID_ARG;
+  AttnShape s{B, n, Hq, Hkv, D, softmax_scale, causal};
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (bf16_in)
+    return from_hip(ulysses::launch_attn_fwd_bf16(q, k, v, key_valid, o, lse, s, o_dtype == ULYSSES_DTYPE_F32, hs));
+  return from_hip(ulysses::launch_attn_fwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
+                                               static_cast<const float*>(v), key_valid, static_cast<float*>(o), lse,
+                                               s, hs));
+}
+
+size_t ulysses_attn_bwd_workspace_bytes(int32_t B, int64_t n, int32_t Hq, int32_t Hkv, int32_t D) {
+  (void)Hkv;
+  (void)D;
+  if (B <= 0 || n <= 0 || Hq <= 0) return 0;
+  return ulysses::attn_bwd_workspace_bytes(B, n, Hq);
+}
+
+ulysses_status_t ulysses_attn_bwd(const void* q, const void* k, const void* v, const uint8_t* key_valid,
+                                  const void* o, const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                                  void* workspace, size_t workspace_bytes, int32_t B, int64_t n, int32_t Hq,
+                                  int32_t Hkv, int32_t D, float softmax_scale, int32_t causal,
+                                  ulysses_dtype_t in_dtype, ulysses_dtype_t o_dtype, void* stream) {
+  bool empty = false;
+  ulysses_status_t st = check_attn_shape(B, n, Hq, Hkv, D, softmax_scale, causal, in_dtype, o_dtype, &empty);
+  if (st != ULYSSES_OK || empty) return st;
+  if (in_dtype != ULYSSES_DTYPE_BF16) return ULYSSES_ERR_UNSUPPORTED;
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || lse == nullptr || dout == nullptr ||
+      dq == nullptr || dk == nullptr || dv == nullptr || workspace == nullptr)
+    return ULYSSES_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
+      !aligned(lse, 4) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(workspace, 256))
+    return ULYSSES_ERR_INVALID_ARG;
+  const size_t need = ulysses::attn_bwd_workspace_bytes(B, n, Hq);
+  if (workspace_bytes < need) return ULYSSES_ERR_INVALID_ARG;
+  const uint64_t nq = uint64_t(B) * n * Hq * D, nkv = uint64_t(B) * n * Hkv * D;
+  const void* ins[7] = {q, k, v, key_valid, o, lse, dout};
+  const uint64_t inb[7] = {nq * 2, nkv * 2, nkv * 2, key_valid ? uint64_t(B) * n : 0,
+                           nq * elem_size(o_dtype), uint64_t(B) * Hq * n * 4, nq * 2};
+  const void* outs[4] = {dq, dk, dv, workspace};
+  const uint64_t outb[4] = {nq * 4, nkv * 4, nkv * 4, need};
+  for (int a = 0; a < 4; ++a) {
+    for (int i = 0; i < 7; ++i)
+      if (overlap(outs[a], outb[a], ins[i], inb[i])) return ULYSSES_ERR_INVALID_ARG;
+    for (int c = a + 1; c < 4; ++c)
+      if (overlap(outs[a], outb[a], outs[c], outb[c])) return ULYSSES_ERR_INVALID_ARG;
+  }
+  AttnShape s{B, n, Hq, Hkv, D, softmax_scale, causal};
+  return from_hip(ulysses::launch_attn_bwd_bf16(q, k, v, key_valid, o, lse, dout, dq, dk, dv,
+                                                static_cast<float*>(workspace), s, o_dtype == ULYSSES_DTYPE_F32,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

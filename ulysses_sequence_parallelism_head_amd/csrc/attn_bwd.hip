@@ -1,0 +1,609 @@
+// attn_bwd.hip -- backward of exact causal grouped-query softmax attention,
+// bf16 inputs on gfx950 matrix cores, float32 gradients.
+//
+// The operation is the gradient of sum(O * dO) of the forward in
+// attn_fwd.hip ([ALST] "Paralelismul de Secvență Ulysses: Antrenarea
+// modelelor AI cu contexte de un milion de token-uri", section "Mecanismul
+// de funcționare Ulysses", step 4); the probabilities are recomputed from
+// the saved logsumexp so memory stays linear in n (same page, section
+// "Provocarea antrenării cu secvențe lungi").
+//
+//   P = exp(S - lse)      dV = P^T dO        dP = dO V^T
+//   Dl = rowsum(dO * O)   dS = P * (dP - Dl) dQ = scale dS K   dK = scale dS^T Q
+//
+// Three kernels:
+//  1. rowdot: Dl[b][h][t] = dO . O per query row (float32 workspace).
+//  2. dkdv (KV-stationary): a workgroup of 4 waves owns 128 keys of one KV
+//     head (32 per wave, K and V held in registers) and streams the 32-row
+//     query tiles of every query head of the group that can see them.  It
+//     computes S = Q K^T and dP = dO V^T with the key on the lane (so P and dS
+//     come out as MFMA B operands) and accumulates dV^T += dO^T P and
+//     dK^T += Q^T dS.  Q, dO are staged row-major and transposed (Q^T, dO^T,
+//     slot-permuted) in LDS, double-buffered.
+//  3. dq (Q-stationary, laid out like the forward): recomputes S^T = K Q^T and
+//     dP^T = V dO^T with the query on the lane and accumulates
+//     dQ^T += K^T dS^T from K^T staged in LDS.  Keeping dQ in its own pass
+//     avoids float32 atomics (whose traffic would grow as n^2 / block) and
+//     makes every gradient deterministic.
+// Rows below kSplitRows use a hi/lo bf16 split of P and dS (two MFMAs) for
+// accuracy where few keys carry large weights.
+#include "device_common.h"
+#include "internal.h"
+
+namespace ulysses {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kSplitRows = 512;
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint8_t* valid;
+  const void* o;
+  const float* lse;
+  const uint16_t* dout;
+  float* dq;
+  float* dk;
+  float* dv;
+  float* rowdot;      // [B][Hq][n]
+  int32_t B, n, Hq, Hkv, g;
+  float scale;
+  float c;            // scale * log2(e)
+  int32_t causal;
+  // dq grid (same as the forward)
+  int32_t gh, pw, n_pblocks, n_hsub;
+  // dkdv grid
+  int32_t n_kblocks;
+};
+
+// ------------------------------------------------------------------ rowdot
+template <int D, bool O_F32>
+__global__ __launch_bounds__(256) void rowdot_kernel(const BwdParams p) {
+  // 16 lanes per row, D/16 elements each
+  constexpr int PER = D / 16;
+  const int64_t rows = int64_t(p.B) * p.n * p.Hq;
+  const int64_t row = int64_t(blockIdx.x) * 16 + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;
+  float acc = 0.f;
+  if (row < rows) {
+    const uint16_t* dp = p.dout + row * D + sub * PER;
+    if (O_F32) {
+      const float* op = static_cast<const float*>(p.o) + row * D + sub * PER;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc = fmaf(__uint_as_float(uint32_t(dp[e]) << 16), op[e], acc);
+    } else {
+      const uint16_t* op = static_cast<const uint16_t*>(p.o) + row * D + sub * PER;
+#pragma unroll
+      for (int e = 0; e < PER; ++e)
+        acc = fmaf(__uint_as_float(uint32_t(dp[e]) << 16), __uint_as_float(uint32_t(op[e]) << 16), acc);
+    }
+  }
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
+  if (row < rows && sub == 0) {
+    // row = (b*n + t)*Hq + h  ->  rowdot[(b*Hq + h)*n + t]
+    const int64_t h = row % p.Hq;
+    const int64_t bt = row / p.Hq;
+    const int64_t t = bt % p.n;
+    const int64_t b = bt / p.n;
+    p.rowdot[(b * p.Hq + h) * p.n + t] = acc;
+  }
+}
+
+// Load a 4-row x 8-column bf16 block: rows r0..r0+3 of a [rows][stride]
+// tensor starting at column c0 (rows >= nrows read as zero).
+__device__ __forceinline__ void load_block4x8(u32x4* dst, const uint16_t* base, int64_t row_stride, int r0,
+                                              int nrows, int c0) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int r = r0 + e;
+    dst[e] = (r < nrows) ? *reinterpret_cast<const u32x4*>(base + int64_t(r) * row_stride + c0) : u32x4{0, 0, 0, 0};
+  }
+}
+
+// ------------------------------------------------------------------- dkdv
+template <int D>
+struct DkdvLayout {
+  static constexpr int kRows = 32;                        // query rows per tile
+  static constexpr int kStrideRM = D + 8;                 // row-major tiles, bf16 elements per row
+  static constexpr int kBytesRM = kRows * kStrideRM * 2;
+  static constexpr int kBytesT = D * kRows * 2;           // transposed tiles: D rows of 32 slots
+  static constexpr int kOffQ = 0;
+  static constexpr int kOffDO = kOffQ + kBytesRM;
+  static constexpr int kOffQT = kOffDO + kBytesRM;
+  static constexpr int kOffDOT = kOffQT + kBytesT;
+  static constexpr int kOffLSE = kOffDOT + kBytesT;
+  static constexpr int kOffDL = kOffLSE + kRows * 4;
+  static constexpr int kStage = kOffDL + kRows * 4;
+  static constexpr int kStageAligned = (kStage + 127) / 128 * 128;
+  static constexpr int kBlocks = (kRows / 4) * (D / 8);   // 4x8 staging blocks per tensor
+};
+
+struct DkdvStaging {
+  u32x4 r[4];
+  float lse2, dl;
+};
+
+template <int D>
+__device__ __forceinline__ void dkdv_load(DkdvStaging& st, const BwdParams& p, int b, int head, int t0, int tid) {
+  using L = DkdvLayout<D>;
+  const int64_t stride = int64_t(p.Hq) * D;
+  if (tid < 2 * L::kBlocks) {
+    const int which = tid / L::kBlocks;         // 0: Q, 1: dO
+    const int blk = tid % L::kBlocks;
+    const int dg = blk % (D / 8);
+    const int rg = blk / (D / 8);
+    const uint16_t* src = (which == 0 ? p.q : p.dout) + (int64_t(b) * p.n * p.Hq + head) * D;
+    load_block4x8(st.r, src, stride, t0 + rg * 4, p.n, dg * 8);
+  }
+  if (tid < L::kRows) {
+    const int t = t0 + tid;
+    if (t < p.n) {
+      const float l = p.lse[(int64_t(b) * p.Hq + head) * p.n + t];
+      st.lse2 = (l == -INFINITY) ? INFINITY : l * kLog2e;   // a row with no key contributes nothing
+      st.dl = p.rowdot[(int64_t(b) * p.Hq + head) * p.n + t];
+    } else {
+      st.lse2 = INFINITY;
+      st.dl = 0.f;
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void dkdv_store(const DkdvStaging& st, uint8_t* stage, int tid) {
+  using L = DkdvLayout<D>;
+  if (tid < 2 * L::kBlocks) {
+    const int which = tid / L::kBlocks;
+    const int blk = tid % L::kBlocks;
+    const int dg = blk % (D / 8);
+    const int rg = blk / (D / 8);
+    uint16_t* rm = reinterpret_cast<uint16_t*>(stage + (which == 0 ? L::kOffQ : L::kOffDO));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) *reinterpret_cast<u32x4*>(rm + (rg * 4 + e) * L::kStrideRM + dg * 8) = st.r[e];
+    uint8_t* tt = stage + (which == 0 ? L::kOffQT : L::kOffDOT);
+    const int slot = tslot(rg * 4);
+    const int chunk = slot >> 3, half = (slot >> 2) & 1;
+#pragma unroll
+    for (int e2 = 0; e2 < 8; ++e2)
+      *reinterpret_cast<u32x2*>(tt + t32_off(dg * 8 + e2, chunk) + half * 8) = transpose_col(st.r, e2);
+  }
+  if (tid < L::kRows) {
+    reinterpret_cast<float*>(stage + L::kOffLSE)[tid] = st.lse2;
+    reinterpret_cast<float*>(stage + L::kOffDL)[tid] = st.dl;
+  }
+}
+
+template <int D, bool HAS_MASK>
+__global__ __launch_bounds__(kThreads, 2) void dkdv_kernel(const BwdParams p) {
+  using L = DkdvLayout<D>;
+  constexpr int KK = D / 16;
+  constexpr int DJ = D / 32;
+  __shared__ __attribute__((aligned(128))) uint8_t smem[2 * L::kStageAligned];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  // block -> (key block, kv head, batch); key block 0 (the longest) first
+  const int per_kb = p.Hkv * p.B;
+  const int kb = int(blockIdx.x) / per_kb;
+  const int rem = int(blockIdx.x) % per_kb;
+  const int b = rem / p.Hkv;
+  const int kvh = rem % p.Hkv;
+  const int k0w = kb * 128 + wave * 32;          // first key of this wave
+  const int u = k0w + l32;                       // this lane's key
+  const bool wave_live = k0w < p.n;
+
+  // K and V rows of this lane's key as the B operands of S = Q K^T, dP = dO V^T
+  u32x4 kf[KK], vf[KK];
+  bool key_ok = u < p.n;
+  {
+    const int64_t off = ((int64_t(b) * p.n + (key_ok ? u : 0)) * p.Hkv + kvh) * D + 8 * hh;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      kf[kk] = key_ok ? *reinterpret_cast<const u32x4*>(p.k + off + 16 * kk) : u32x4{0, 0, 0, 0};
+      vf[kk] = key_ok ? *reinterpret_cast<const u32x4*>(p.v + off + 16 * kk) : u32x4{0, 0, 0, 0};
+    }
+    if (HAS_MASK && key_ok) key_ok = p.valid[int64_t(b) * p.n + u] != 0;
+  }
+
+  f32x16 dka[DJ], dva[DJ];
+#pragma unroll
+  for (int j = 0; j < DJ; ++j) {
+    dka[j] = f32x16{};
+    dva[j] = f32x16{};
+  }
+
+  const int q_first = p.causal ? kb * 128 : 0;
+  const int ntq = (p.n - q_first + L::kRows - 1) / L::kRows;   // query tiles per head
+  const int niter = p.g * ntq;
+
+  DkdvStaging st;
+  if (niter > 0) {
+    dkdv_load<D>(st, p, b, kvh * p.g, q_first, tid);
+    dkdv_store<D>(st, smem, tid);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < niter; ++it) {
+    uint8_t* cur = smem + (it & 1) * L::kStageAligned;
+    if (it + 1 < niter) {
+      const int nh = (it + 1) / ntq, nt = (it + 1) % ntq;
+      dkdv_load<D>(st, p, b, kvh * p.g + nh, q_first + nt * L::kRows, tid);
+    }
+    const int t0 = q_first + (it % ntq) * L::kRows;
+    // rows t0..t0+31 see this wave's keys only if t0 + 31 >= k0w
+    if (wave_live && !(p.causal && t0 + L::kRows - 1 < k0w)) {
+      const uint16_t* qs = reinterpret_cast<const uint16_t*>(cur + L::kOffQ);
+      const uint16_t* dos = reinterpret_cast<const uint16_t*>(cur + L::kOffDO);
+      const uint8_t* qts = cur + L::kOffQT;
+      const uint8_t* dots = cur + L::kOffDOT;
+      const float* lse2s = reinterpret_cast<const float*>(cur + L::kOffLSE);
+      const float* dls = reinterpret_cast<const float*>(cur + L::kOffDL);
+      const bool split = t0 < kSplitRows;
+
+      // S[q][key] and dP[q][key]: lane = key, rows q = (i/4)*8 + 4hh + i%4
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const u32x4 aq = *reinterpret_cast<const u32x4*>(qs + l32 * L::kStrideRM + kk * 16 + hh * 8);
+        s = mfma32x32x16(aq, kf[kk], s);
+        const u32x4 ad = *reinterpret_cast<const u32x4*>(dos + l32 * L::kStrideRM + kk * 16 + hh * 8);
+        dp = mfma32x32x16(ad, vf[kk], dp);
+      }
+
+      float pr[16], ds[16];
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int r0 = g4 * 8 + hh * 4;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + r0);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dls + r0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = g4 * 4 + e;
+          const int t = t0 + r0 + e;
+          const bool ok = key_ok && !(p.causal && u > t);
+          const float pv = ok ? __builtin_amdgcn_exp2f(s[i] * p.c - l4[e]) : 0.f;
+          pr[i] = pv;
+          ds[i] = pv * (dp[i] - d4[e]);
+        }
+      }
+
+      u32x4 ph[2], pl[2], dh[2], dl[2];
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const float* a = pr + 8 * f;
+        const float* c = ds + 8 * f;
+        ph[f] = u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(a[4], a[5]), pack_bf16x2(a[6], a[7])};
+        dh[f] = u32x4{pack_bf16x2(c[0], c[1]), pack_bf16x2(c[2], c[3]), pack_bf16x2(c[4], c[5]), pack_bf16x2(c[6], c[7])};
+        if (split) {
+          float ra[8], rc[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            ra[2 * e] = a[2 * e] - bf16lo_to_f32(ph[f][e]);
+            ra[2 * e + 1] = a[2 * e + 1] - bf16hi_to_f32(ph[f][e]);
+            rc[2 * e] = c[2 * e] - bf16lo_to_f32(dh[f][e]);
+            rc[2 * e + 1] = c[2 * e + 1] - bf16hi_to_f32(dh[f][e]);
+          }
+          pl[f] = u32x4{pack_bf16x2(ra[0], ra[1]), pack_bf16x2(ra[2], ra[3]), pack_bf16x2(ra[4], ra[5]),
+                        pack_bf16x2(ra[6], ra[7])};
+          dl[f] = u32x4{pack_bf16x2(rc[0], rc[1]), pack_bf16x2(rc[2], rc[3]), pack_bf16x2(rc[4], rc[5]),
+                        pack_bf16x2(rc[6], rc[7])};
+        }
+      }
+
+      // dV^T += dO^T P,  dK^T += Q^T dS   (A operands from the transposed tiles)
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const int chunk = f * 2 + hh;
+#pragma unroll
+        for (int j = 0; j < DJ; ++j) {
+          const int d = j * 32 + l32;
+          const u32x4 adt = *reinterpret_cast<const u32x4*>(dots + t32_off(d, chunk));
+          dva[j] = mfma32x32x16(adt, ph[f], dva[j]);
+          if (split) dva[j] = mfma32x32x16(adt, pl[f], dva[j]);
+          const u32x4 aqt = *reinterpret_cast<const u32x4*>(qts + t32_off(d, chunk));
+          dka[j] = mfma32x32x16(aqt, dh[f], dka[j]);
+          if (split) dka[j] = mfma32x32x16(aqt, dl[f], dka[j]);
+        }
+      }
+    }
+    if (it + 1 < niter) dkdv_store<D>(st, smem + ((it + 1) & 1) * L::kStageAligned, tid);
+    __syncthreads();
+  }
+
+  // write dK = scale * dK^T^T and dV: lane = key u, dims 32j + 8*(i/4) + 4hh + i%4
+  if (u < p.n) {
+    const int64_t base = ((int64_t(b) * p.n + u) * p.Hkv + kvh) * D;
+#pragma unroll
+    for (int j = 0; j < DJ; ++j)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d0 = j * 32 + i4 * 8 + hh * 4;
+        *reinterpret_cast<f32x4*>(p.dk + base + d0) =
+            f32x4{dka[j][i4 * 4] * p.scale, dka[j][i4 * 4 + 1] * p.scale, dka[j][i4 * 4 + 2] * p.scale,
+                  dka[j][i4 * 4 + 3] * p.scale};
+        *reinterpret_cast<f32x4*>(p.dv + base + d0) =
+            f32x4{dva[j][i4 * 4], dva[j][i4 * 4 + 1], dva[j][i4 * 4 + 2], dva[j][i4 * 4 + 3]};
+      }
+  }
+}
+
+// --------------------------------------------------------------------- dq
+template <int D>
+struct DqLayout {
+  static constexpr int kBN = 64;                          // keys per tile
+  static constexpr int kStrideRM = D + 8;
+  static constexpr int kBytesRM = kBN * kStrideRM * 2;
+  static constexpr int kBytesT = D * kBN * 2;             // K^T: D rows of 64 slots
+  static constexpr int kOffK = 0;
+  static constexpr int kOffV = kOffK + kBytesRM;
+  static constexpr int kOffKT = kOffV + kBytesRM;
+  static constexpr int kOffValid = kOffKT + kBytesT;
+  static constexpr int kStage = kOffValid + kBN;
+  static constexpr int kBlocks = (kBN / 4) * (D / 8);     // 4x8 staging blocks per tensor
+};
+
+struct DqStaging {
+  u32x4 kr[4], vr[4];
+  uint32_t vbyte;
+};
+
+template <int D, bool HAS_MASK>
+__device__ __forceinline__ void dq_load(DqStaging& st, const BwdParams& p, int b, int kvh, int tile, int tid) {
+  using L = DqLayout<D>;
+  const int key0 = tile * L::kBN;
+  if (tid < L::kBlocks) {
+    const int dg = tid % (D / 8);
+    const int kg = tid / (D / 8);
+    const int64_t stride = int64_t(p.Hkv) * D;
+    const int64_t off = (int64_t(b) * p.n * p.Hkv + kvh) * D;
+    load_block4x8(st.kr, p.k + off, stride, key0 + kg * 4, p.n, dg * 8);
+    load_block4x8(st.vr, p.v + off, stride, key0 + kg * 4, p.n, dg * 8);
+  }
+  if (HAS_MASK && tid < L::kBN) {
+    const int key = key0 + tid;
+    st.vbyte = (key < p.n) ? (p.valid[int64_t(b) * p.n + key] != 0 ? 1u : 0u) : 0u;
+  }
+}
+
+template <int D, bool HAS_MASK>
+__device__ __forceinline__ void dq_store(const DqStaging& st, uint8_t* stage, int tid) {
+  using L = DqLayout<D>;
+  if (tid < L::kBlocks) {
+    const int dg = tid % (D / 8);
+    const int kg = tid / (D / 8);
+    uint16_t* ks = reinterpret_cast<uint16_t*>(stage + L::kOffK);
+    uint16_t* vs = reinterpret_cast<uint16_t*>(stage + L::kOffV);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      *reinterpret_cast<u32x4*>(ks + (kg * 4 + e) * L::kStrideRM + dg * 8) = st.kr[e];
+      *reinterpret_cast<u32x4*>(vs + (kg * 4 + e) * L::kStrideRM + dg * 8) = st.vr[e];
+    }
+    uint8_t* kt = stage + L::kOffKT;
+    const int k4 = kg * 4;
+    const int slot = (k4 & 32) | tslot(k4 & 31);
+    const int chunk = slot >> 3, half = (slot >> 2) & 1;
+#pragma unroll
+    for (int e2 = 0; e2 < 8; ++e2)
+      *reinterpret_cast<u32x2*>(kt + t64_off(dg * 8 + e2, chunk) + half * 8) = transpose_col(st.kr, e2);
+  }
+  if (HAS_MASK && tid < L::kBN) stage[L::kOffValid + tid] = uint8_t(st.vbyte);
+}
+
+template <int D, bool HAS_MASK>
+__global__ __launch_bounds__(kThreads, 2) void dq_kernel(const BwdParams p) {
+  using L = DqLayout<D>;
+  constexpr int KK = D / 16;
+  constexpr int DJ = D / 32;
+  __shared__ __attribute__((aligned(128))) uint8_t smem[L::kStage];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  const int per_pos = p.n_hsub * p.Hkv * p.B;
+  const int pb = p.n_pblocks - 1 - int(blockIdx.x) / per_pos;
+  int rem = int(blockIdx.x) % per_pos;
+  const int b = rem / (p.n_hsub * p.Hkv);
+  rem = rem % (p.n_hsub * p.Hkv);
+  const int kvh = rem / p.n_hsub;
+  const int hs = rem % p.n_hsub;
+  const int head = kvh * p.g + hs * p.gh + (wave % p.gh);
+  const int p0 = pb * p.pw + (wave / p.gh) * 32;
+  const int t = p0 + l32;
+  const int wave_last = min(p0 + 31, p.n - 1);
+  const int wg_last = min(pb * p.pw + p.pw, p.n) - 1;
+  const int kend = p.causal ? wg_last + 1 : p.n;
+  const int ntiles = (kend + L::kBN - 1) / L::kBN;
+  const bool wave_live = p0 < p.n;
+  const bool split = p0 < kSplitRows;
+
+  u32x4 qf[KK], df[KK];
+  float lse2 = INFINITY, dl = 0.f;
+  {
+    const bool ok = t < p.n;
+    const int64_t off = ((int64_t(b) * p.n + (ok ? t : 0)) * p.Hq + head) * D + 8 * hh;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      qf[kk] = ok ? *reinterpret_cast<const u32x4*>(p.q + off + 16 * kk) : u32x4{0, 0, 0, 0};
+      df[kk] = ok ? *reinterpret_cast<const u32x4*>(p.dout + off + 16 * kk) : u32x4{0, 0, 0, 0};
+    }
+    if (ok) {
+      const float l = p.lse[(int64_t(b) * p.Hq + head) * p.n + t];
+      lse2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
+      dl = p.rowdot[(int64_t(b) * p.Hq + head) * p.n + t];
+    }
+  }
+
+  f32x16 dqa[DJ];
+#pragma unroll
+  for (int j = 0; j < DJ; ++j) dqa[j] = f32x16{};
+
+  DqStaging st;
+  if (ntiles > 0) dq_load<D, HAS_MASK>(st, p, b, kvh, 0, tid);
+
+  for (int it = 0; it < ntiles; ++it) {
+    __syncthreads();                      // previous tile fully consumed
+    dq_store<D, HAS_MASK>(st, smem, tid);
+    __syncthreads();
+    if (it + 1 < ntiles) dq_load<D, HAS_MASK>(st, p, b, kvh, it + 1, tid);   // in flight during the math
+
+    const int tile0 = it * L::kBN;
+    if (!wave_live || (p.causal && tile0 > wave_last)) continue;
+    const uint16_t* ks = reinterpret_cast<const uint16_t*>(smem + L::kOffK);
+    const uint16_t* vs = reinterpret_cast<const uint16_t*>(smem + L::kOffV);
+    const uint8_t* kts = smem + L::kOffKT;
+    const uint8_t* vb = smem + L::kOffValid;
+
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int key0 = tile0 + half * 32;
+      if (p.causal && key0 > wave_last) break;
+      // S^T[key][q] and dP^T[key][q]: lane = query row t, rows key = (i/4)*8 + 4hh + i%4
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const u32x4 ak = *reinterpret_cast<const u32x4*>(ks + (half * 32 + l32) * L::kStrideRM + kk * 16 + hh * 8);
+        s = mfma32x32x16(ak, qf[kk], s);
+        const u32x4 av = *reinterpret_cast<const u32x4*>(vs + (half * 32 + l32) * L::kStrideRM + kk * 16 + hh * 8);
+        dp = mfma32x32x16(av, df[kk], dp);
+      }
+      float ds[16];
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        uint32_t vw = 0xffffffffu;
+        if (HAS_MASK) vw = *reinterpret_cast<const uint32_t*>(vb + half * 32 + g4 * 8 + hh * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = g4 * 4 + e;
+          const int key = key0 + g4 * 8 + hh * 4 + e;
+          const bool ok = key < p.n && !(p.causal && key > t) && (!HAS_MASK || ((vw >> (8 * e)) & 0xffu));
+          const float pv = ok ? __builtin_amdgcn_exp2f(s[i] * p.c - lse2) : 0.f;
+          ds[i] = pv * (dp[i] - dl);
+        }
+      }
+      u32x4 dh[2], dlo[2];
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const float* c = ds + 8 * f;
+        dh[f] = u32x4{pack_bf16x2(c[0], c[1]), pack_bf16x2(c[2], c[3]), pack_bf16x2(c[4], c[5]), pack_bf16x2(c[6], c[7])};
+        if (split) {
+          float rc[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            rc[2 * e] = c[2 * e] - bf16lo_to_f32(dh[f][e]);
+            rc[2 * e + 1] = c[2 * e + 1] - bf16hi_to_f32(dh[f][e]);
+          }
+          dlo[f] = u32x4{pack_bf16x2(rc[0], rc[1]), pack_bf16x2(rc[2], rc[3]), pack_bf16x2(rc[4], rc[5]),
+                         pack_bf16x2(rc[6], rc[7])};
+        }
+      }
+      // dQ^T += K^T dS^T
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const int chunk = half * 4 + f * 2 + hh;
+#pragma unroll
+        for (int j = 0; j < DJ; ++j) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(kts + t64_off(j * 32 + l32, chunk));
+          dqa[j] = mfma32x32x16(a, dh[f], dqa[j]);
+          if (split) dqa[j] = mfma32x32x16(a, dlo[f], dqa[j]);
+        }
+      }
+    }
+  }
+
+  if (t < p.n) {
+    const int64_t base = ((int64_t(b) * p.n + t) * p.Hq + head) * D;
+#pragma unroll
+    for (int j = 0; j < DJ; ++j)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d0 = j * 32 + i4 * 8 + hh * 4;
+        *reinterpret_cast<f32x4*>(p.dq + base + d0) =
+            f32x4{dqa[j][i4 * 4] * p.scale, dqa[j][i4 * 4 + 1] * p.scale, dqa[j][i4 * 4 + 2] * p.scale,
+                  dqa[j][i4 * 4 + 3] * p.scale};
+      }
+  }
+}
+
+template <int D>
+hipError_t launch_bwd_d(const BwdParams& p, bool has_mask, bool o_f32, hipStream_t stream) {
+  const int64_t rows = int64_t(p.B) * p.n * p.Hq;
+  const int64_t rd_blocks = (rows + 15) / 16;
+  if (rd_blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (o_f32) hipLaunchKernelGGL((rowdot_kernel<D, true>), dim3(rd_blocks), dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL((rowdot_kernel<D, false>), dim3(rd_blocks), dim3(256), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  const int64_t kv_blocks = int64_t(p.n_kblocks) * p.Hkv * p.B;
+  const int64_t q_blocks = int64_t(p.n_pblocks) * p.n_hsub * p.Hkv * p.B;
+  if (kv_blocks > 0x7fffffff || q_blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (has_mask) {
+    hipLaunchKernelGGL((dkdv_kernel<D, true>), dim3(kv_blocks), dim3(kThreads), 0, stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((dq_kernel<D, true>), dim3(q_blocks), dim3(kThreads), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((dkdv_kernel<D, false>), dim3(kv_blocks), dim3(kThreads), 0, stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((dq_kernel<D, false>), dim3(q_blocks), dim3(kThreads), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t attn_bwd_workspace_bytes(int32_t B, int64_t n, int32_t Hq) {
+  const size_t bytes = size_t(B) * size_t(n) * size_t(Hq) * sizeof(float);
+  return (bytes + 255) / 256 * 256;
+}
+
+hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const uint8_t* valid, const void* o,
+                                const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                                float* workspace, const AttnShape& s, int o_f32, hipStream_t stream) {
+  BwdParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.valid = valid;
+  p.o = o;
+  p.lse = lse;
+  p.dout = static_cast<const uint16_t*>(dout);
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.rowdot = workspace;
+  p.B = s.B;
+  p.n = int32_t(s.n);
+  p.Hq = s.Hq;
+  p.Hkv = s.Hkv;
+  p.g = s.Hq / s.Hkv;
+  p.scale = s.scale;
+  p.c = s.scale * kLog2e;
+  p.causal = s.causal;
+  int gh = 1;
+  for (int c = kWaves; c >= 1; --c)
+    if (p.g % c == 0 && kWaves % c == 0) { gh = c; break; }
+  p.gh = gh;
+  p.pw = 32 * (kWaves / gh);
+  p.n_pblocks = int32_t((s.n + p.pw - 1) / p.pw);
+  p.n_hsub = p.g / gh;
+  p.n_kblocks = int32_t((s.n + 127) / 128);
+  if (int64_t(p.B) * p.n == 0) return hipSuccess;
+  if (s.D == 128) return launch_bwd_d<128>(p, valid != nullptr, o_f32 != 0, stream);
+  return launch_bwd_d<64>(p, valid != nullptr, o_f32 != 0, stream);
+}
+
+}  // namespace ulysses

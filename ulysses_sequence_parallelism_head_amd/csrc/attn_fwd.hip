@@ -1,0 +1,395 @@
+// attn_fwd.hip -- exact causal grouped-query softmax attention, forward with
+// logsumexp, bf16 inputs on gfx950 matrix cores.
+//
+// Operation: [ALST] "Paralelismul de Secvență Ulysses: Antrenarea modelelor
+// AI cu contexte de un milion de token-uri", section "Mecanismul de
+// funcționare Ulysses", step 4 (local attention over all positions for the
+// heads this rank holds); the tiled, never-materialised score matrix follows
+// the same page's section "Provocarea antrenării cu secvențe lungi".
+//
+// Design (gfx950, wave64):
+//  * A workgroup of 4 waves owns one KV head and a block of query rows; every
+//    32-row group is (32 consecutive positions, one query head).  With a GQA
+//    group of g >= 4 query heads per KV head the 4 waves take the same 32
+//    positions of 4 different query heads, so each K/V tile staged in LDS
+//    feeds 128 query rows with identical causal extents.
+//  * Scores are computed transposed, S^T = K Q^T (32 keys x 32 queries per
+//    32x32x16 bf16 MFMA), so each lane owns one query row: row max, row sum
+//    and the rescale of O stay in-lane (one swap between half-waves for the
+//    max).  O is accumulated transposed too, O^T += V^T P^T, with P^T used
+//    straight from the score registers as the B operand.
+//  * K tiles are stored row-major in LDS (16-byte padded rows); V tiles are
+//    transposed in registers while staging and stored as V^T with the key
+//    slots permuted to match the score registers' key order, in 16-byte
+//    chunks XOR-swizzled per row so that both the staging writes and the
+//    MFMA operand reads are free of bank conflicts.
+//  * Global->LDS staging of tile i+1 is issued before the MFMA work on tile i
+//    (double-buffered LDS, one barrier per tile).
+//  * Online softmax in base 2 (log2(e) folded into the scale).  The running
+//    max is only raised when a tile's max exceeds it by more than 8 (log2
+//    units): O and the row sum then carry factors up to 2^8, harmless in
+//    fp32, and the rescale of O is skipped on almost every tile.
+//  * Rows below kSplitRows use a hi/lo split of P (two bf16 MFMAs) to keep
+//    the error of the few-key rows, whose weights are large, far below 1e-2.
+//  * The grid is launched longest-first (last query blocks first) so the
+//    causal triangle's long blocks do not trail at the end.
+#include "device_common.h"
+#include "internal.h"
+
+namespace ulysses {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kBN = 64;                 // keys per tile
+constexpr int kSplitRows = 512;         // rows using the hi/lo split of P
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRescaleSlack = 8.0f;   // log2 units
+
+template <int D>
+struct FwdLayout {
+  static constexpr int kStrideK = D + 8;                 // bf16 elements per K row in LDS
+  static constexpr int kBytesK = kBN * kStrideK * 2;
+  static constexpr int kBytesV = D * kBN * 2;            // V^T: D rows of 64 key slots (128 B)
+  static constexpr int kBytesValid = kBN;
+  static constexpr int kStage = kBytesK + kBytesV + kBytesValid;
+  static constexpr int kStageAligned = (kStage + 127) / 128 * 128;
+  static constexpr int kKChunksPerRow = D / 8;           // 16-byte chunks per K/V row
+  static constexpr int kKChunksPerThread = kBN * kKChunksPerRow / kThreads;
+  static constexpr int kVBlocks = (kBN / 4) * (D / 8);   // 4 keys x 8 dims per staging block
+};
+
+struct FwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint8_t* valid;
+  void* o;
+  float* lse;
+  int32_t B, n, Hq, Hkv;
+  int32_t g;          // query heads per KV head
+  int32_t gh;         // query heads per workgroup
+  int32_t pw;         // positions per workgroup
+  int32_t n_pblocks;  // ceil(n / pw)
+  int32_t n_hsub;     // g / gh
+  float c;            // softmax scale * log2(e)
+  int32_t causal;
+};
+
+template <int D>
+struct Staging {
+  u32x4 kreg[FwdLayout<D>::kKChunksPerThread];
+  u32x4 vreg[4];
+  uint32_t vbyte;
+};
+
+template <int D, bool HAS_MASK>
+__device__ __forceinline__ void stage_load(Staging<D>& st, const FwdParams& p, int b, int kvh, int tile, int tid) {
+  using L = FwdLayout<D>;
+  const int key_base = tile * kBN;
+#pragma unroll
+  for (int u = 0; u < L::kKChunksPerThread; ++u) {
+    const int c = tid + u * kThreads;
+    const int row = c / L::kKChunksPerRow;
+    const int col = c % L::kKChunksPerRow;
+    const int key = key_base + row;
+    if (key < p.n) {
+      const int64_t off = ((int64_t(b) * p.n + key) * p.Hkv + kvh) * D + col * 8;
+      st.kreg[u] = *reinterpret_cast<const u32x4*>(p.k + off);
+    } else {
+      st.kreg[u] = u32x4{0, 0, 0, 0};
+    }
+  }
+  if (tid < L::kVBlocks) {
+    const int dg = tid % (D / 8);
+    const int kg = tid / (D / 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int key = key_base + kg * 4 + e;
+      if (key < p.n) {
+        const int64_t off = ((int64_t(b) * p.n + key) * p.Hkv + kvh) * D + dg * 8;
+        st.vreg[e] = *reinterpret_cast<const u32x4*>(p.v + off);
+      } else {
+        st.vreg[e] = u32x4{0, 0, 0, 0};
+      }
+    }
+  }
+  if (HAS_MASK && tid < kBN) {
+    const int key = key_base + tid;
+    st.vbyte = (key < p.n) ? (p.valid[int64_t(b) * p.n + key] != 0 ? 1u : 0u) : 0u;
+  }
+}
+
+template <int D, bool HAS_MASK>
+__device__ __forceinline__ void stage_store(const Staging<D>& st, uint8_t* stage, int tid) {
+  using L = FwdLayout<D>;
+  uint16_t* ks = reinterpret_cast<uint16_t*>(stage);
+  uint8_t* vt = stage + L::kBytesK;
+#pragma unroll
+  for (int u = 0; u < L::kKChunksPerThread; ++u) {
+    const int c = tid + u * kThreads;
+    const int row = c / L::kKChunksPerRow;
+    const int col = c % L::kKChunksPerRow;
+    *reinterpret_cast<u32x4*>(ks + row * L::kStrideK + col * 8) = st.kreg[u];
+  }
+  if (tid < L::kVBlocks) {
+    const int dg = tid % (D / 8);
+    const int kg = tid / (D / 8);
+    const int kt = kg * 4;                       // first key of the group within the tile
+    const int slot = (kt & 32) | tslot(kt & 31);
+    const int chunk = slot >> 3;
+    const int half = (slot >> 2) & 1;
+#pragma unroll
+    for (int e2 = 0; e2 < 8; ++e2) {
+      const int d = dg * 8 + e2;
+      *reinterpret_cast<u32x2*>(vt + t64_off(d, chunk) + half * 8) = transpose_col(st.vreg, e2);
+    }
+  }
+  if (HAS_MASK && tid < kBN) stage[L::kBytesK + L::kBytesV + tid] = uint8_t(st.vbyte);
+}
+
+template <int D, bool HAS_MASK, bool O_F32>
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const FwdParams p) {
+  using L = FwdLayout<D>;
+  constexpr int KK = D / 16;     // contraction slices of the score product
+  constexpr int DJ = D / 32;     // 32-row blocks of O^T
+  __shared__ __attribute__((aligned(128))) uint8_t smem[2 * L::kStageAligned];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  // ---- block coordinates (longest-first over position blocks)
+  const int per_pos = p.n_hsub * p.Hkv * p.B;
+  const int L_id = blockIdx.x;
+  const int pb = p.n_pblocks - 1 - L_id / per_pos;
+  int rem = L_id % per_pos;
+  const int b = rem / (p.n_hsub * p.Hkv);
+  rem = rem % (p.n_hsub * p.Hkv);
+  const int kvh = rem / p.n_hsub;
+  const int hs = rem % p.n_hsub;
+
+  const int head = kvh * p.g + hs * p.gh + (wave % p.gh);
+  const int p0 = pb * p.pw + (wave / p.gh) * 32;      // first position of this wave's rows
+  const int t = p0 + l32;                               // this lane's query row
+  const int wave_last = min(p0 + 31, p.n - 1);
+  const int wg_last = min(pb * p.pw + p.pw, p.n) - 1;
+  const int kend = p.causal ? wg_last + 1 : p.n;
+  const int ntiles = (kend + kBN - 1) / kBN;
+  const bool wave_live = p0 < p.n;
+
+  // ---- Q fragment (B operand of S^T = K Q^T): lane holds row t, dims 16kk + 8hh .. +7
+  u32x4 qf[KK];
+  {
+    const bool ok = t < p.n;
+    const int64_t off = ((int64_t(b) * p.n + (ok ? t : 0)) * p.Hq + head) * D + 8 * hh;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      qf[kk] = ok ? *reinterpret_cast<const u32x4*>(p.q + off + 16 * kk) : u32x4{0, 0, 0, 0};
+  }
+
+  f32x16 oacc[DJ];
+#pragma unroll
+  for (int j = 0; j < DJ; ++j) oacc[j] = f32x16{};
+  float m_ref = -INFINITY;   // running reference max (log2 units), identical in both half-waves
+  float lsum = 0.f;          // this half-wave's share of the row sum
+  const bool split = p0 < kSplitRows;
+
+  Staging<D> st;
+  stage_load<D, HAS_MASK>(st, p, b, kvh, 0, tid);
+  stage_store<D, HAS_MASK>(st, smem, tid);
+  __syncthreads();
+
+  for (int it = 0; it < ntiles; ++it) {
+    uint8_t* cur = smem + (it & 1) * L::kStageAligned;
+    if (it + 1 < ntiles) stage_load<D, HAS_MASK>(st, p, b, kvh, it + 1, tid);
+
+    const int tile0 = it * kBN;
+    if (wave_live && !(p.causal && tile0 > wave_last)) {
+      const uint16_t* ks = reinterpret_cast<const uint16_t*>(cur);
+      const uint8_t* vt = cur + L::kBytesK;
+      const bool act1 = !(p.causal && tile0 + 32 > wave_last);   // second half-tile has a visible key
+
+      // ---- S^T for the two 32-key halves
+      f32x16 s0 = f32x16{}, s1 = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(ks + l32 * L::kStrideK + kk * 16 + hh * 8);
+        s0 = mfma32x32x16(a0, qf[kk], s0);
+        if (act1) {
+          const u32x4 a1 = *reinterpret_cast<const u32x4*>(ks + (32 + l32) * L::kStrideK + kk * 16 + hh * 8);
+          s1 = mfma32x32x16(a1, qf[kk], s1);
+        }
+      }
+
+      // ---- scale to log2 units and mask
+      float x[32];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        x[i] = s0[i] * p.c;
+        x[16 + i] = act1 ? s1[i] * p.c : -INFINITY;
+      }
+      const bool diag = p.causal && (tile0 + kBN - 1 > p0);
+      const bool tail = !HAS_MASK && (tile0 + kBN > p.n);
+      if (diag || tail) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          const int key = tile0 + (i >> 4) * 32 + ((i & 15) >> 2) * 8 + hh * 4 + (i & 3);
+          const bool bad = (p.causal && key > t) || key >= p.n;
+          x[i] = bad ? -INFINITY : x[i];
+        }
+      }
+      if (HAS_MASK) {
+        const uint8_t* vb = cur + L::kBytesK + L::kBytesV;
+#pragma unroll
+        for (int grp = 0; grp < 8; ++grp) {
+          const int kt = (grp >> 2) * 32 + (grp & 3) * 8 + hh * 4;
+          const uint32_t w = *reinterpret_cast<const uint32_t*>(vb + kt);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[grp * 4 + e] = ((w >> (8 * e)) & 0xffu) ? x[grp * 4 + e] : -INFINITY;
+        }
+      }
+
+      // ---- online softmax (lazy rescale)
+      float mx = x[0];
+#pragma unroll
+      for (int i = 1; i < 32; ++i) mx = fmaxf(mx, x[i]);
+      mx = fmaxf(mx, swap_halves(mx));
+      const bool raise = mx > m_ref + kRescaleSlack;
+      if (__any(raise)) {
+        const float alpha = raise ? __builtin_amdgcn_exp2f(m_ref - mx) : 1.0f;
+        if (raise) m_ref = mx;
+        lsum *= alpha;
+#pragma unroll
+        for (int j = 0; j < DJ; ++j)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[j][i] *= alpha;
+      }
+      const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+      float pr[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        pr[i] = __builtin_amdgcn_exp2f(x[i] - m_use);
+        lsum += pr[i];
+      }
+
+      // ---- P^T as B operand: per half-tile kb and 16-key slice kk2, the lane's 8 scores
+      u32x4 phi[4], plo[4];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        const float* pp = pr + f * 8;
+        phi[f] = u32x4{pack_bf16x2(pp[0], pp[1]), pack_bf16x2(pp[2], pp[3]), pack_bf16x2(pp[4], pp[5]),
+                       pack_bf16x2(pp[6], pp[7])};
+      }
+      if (split) {
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          const float* pp = pr + f * 8;
+          float r[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            r[2 * e] = pp[2 * e] - bf16lo_to_f32(phi[f][e]);
+            r[2 * e + 1] = pp[2 * e + 1] - bf16hi_to_f32(phi[f][e]);
+          }
+          plo[f] = u32x4{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]), pack_bf16x2(r[4], r[5]),
+                         pack_bf16x2(r[6], r[7])};
+        }
+      }
+
+      // ---- O^T += V^T P^T
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        if (f >= 2 && !act1) break;
+        const int chunk = f * 2 + hh;            // slot f*16 + 8*hh within the tile
+#pragma unroll
+        for (int j = 0; j < DJ; ++j) {
+          const int d = j * 32 + l32;
+          const u32x4 a = *reinterpret_cast<const u32x4*>(vt + t64_off(d, chunk));
+          oacc[j] = mfma32x32x16(a, phi[f], oacc[j]);
+          if (split) oacc[j] = mfma32x32x16(a, plo[f], oacc[j]);
+        }
+      }
+    }
+
+    if (it + 1 < ntiles) stage_store<D, HAS_MASK>(st, smem + ((it + 1) & 1) * L::kStageAligned, tid);
+    __syncthreads();
+  }
+
+  // ---- epilogue: normalise, write O (row t, dims 32j + 8*(i/4) + 4hh + i%4) and LSE
+  if (t < p.n) {
+    const float ltot = lsum + swap_halves(lsum);
+    const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
+    const int64_t obase = ((int64_t(b) * p.n + t) * p.Hq + head) * D;
+#pragma unroll
+    for (int j = 0; j < DJ; ++j) {
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d0 = j * 32 + i4 * 8 + hh * 4;
+        const float v0 = oacc[j][i4 * 4 + 0] * inv, v1 = oacc[j][i4 * 4 + 1] * inv;
+        const float v2 = oacc[j][i4 * 4 + 2] * inv, v3 = oacc[j][i4 * 4 + 3] * inv;
+        if (O_F32) {
+          *reinterpret_cast<f32x4*>(static_cast<float*>(p.o) + obase + d0) = f32x4{v0, v1, v2, v3};
+        } else {
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.o) + obase + d0) =
+              u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+        }
+      }
+    }
+    if (hh == 0) {
+      p.lse[(int64_t(b) * p.Hq + head) * p.n + t] =
+          ltot > 0.f ? (m_ref + __log2f(ltot)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
+template <int D, bool HAS_MASK, bool O_F32>
+hipError_t launch_fwd_t(const FwdParams& p, int blocks, hipStream_t stream) {
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, HAS_MASK, O_F32>), dim3(blocks), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t dispatch_fwd(const FwdParams& p, int blocks, bool has_mask, bool o_f32, hipStream_t stream) {
+  if (has_mask) return o_f32 ? launch_fwd_t<D, true, true>(p, blocks, stream) : launch_fwd_t<D, true, false>(p, blocks, stream);
+  return o_f32 ? launch_fwd_t<D, false, true>(p, blocks, stream) : launch_fwd_t<D, false, false>(p, blocks, stream);
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, const uint8_t* valid, void* o,
+                                float* lse, const AttnShape& s, int o_f32, hipStream_t stream) {
+  FwdParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.valid = valid;
+  p.o = o;
+  p.lse = lse;
+  p.B = s.B;
+  p.n = int32_t(s.n);
+  p.Hq = s.Hq;
+  p.Hkv = s.Hkv;
+  p.g = s.Hq / s.Hkv;
+  // query heads per workgroup: the largest divisor of g that is <= 4 (the wave count)
+  int gh = 1;
+  for (int c = kWaves; c >= 1; --c)
+    if (p.g % c == 0 && kWaves % c == 0) { gh = c; break; }
+  p.gh = gh;
+  p.pw = 32 * (kWaves / gh);
+  p.n_pblocks = int32_t((s.n + p.pw - 1) / p.pw);
+  p.n_hsub = p.g / gh;
+  p.c = s.scale * kLog2e;
+  p.causal = s.causal;
+  const int64_t blocks = int64_t(p.n_pblocks) * p.n_hsub * p.Hkv * p.B;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  const bool has_mask = valid != nullptr;
+  if (s.D == 128) return dispatch_fwd<128>(p, int(blocks), has_mask, o_f32 != 0, stream);
+  return dispatch_fwd<64>(p, int(blocks), has_mask, o_f32 != 0, stream);
+}
+
+}  // namespace ulysses

@@ -1,0 +1,39 @@
+// internal.h -- launchers behind the C ABI (not exported).  Arguments are
+// already validated by abi.hip; these only pick kernel variants and launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ulysses {
+
+// The exchange permutations.  run_bytes = (H/P)*D*elem; vec_bytes divides
+// run_bytes and both pointers' alignment.
+hipError_t launch_repack(const void* src, void* dst, uint32_t P, uint32_t B, uint32_t n_local,
+                         uint32_t run_bytes, uint32_t vec_bytes, int seq2head, hipStream_t stream);
+
+struct AttnShape {
+  int32_t B;
+  int64_t n;
+  int32_t Hq, Hkv, D;
+  float scale;
+  int32_t causal;
+};
+
+// bf16 inputs, matrix cores; o_f32 selects a float32 (else bf16) output.
+hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, const uint8_t* valid, void* o,
+                                float* lse, const AttnShape& s, int o_f32, hipStream_t stream);
+
+// float32 inputs and output, fp32 arithmetic throughout.
+hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, const uint8_t* valid, float* o,
+                               float* lse, const AttnShape& s, hipStream_t stream);
+
+// bf16 inputs; o is bf16 or float32 (o_f32); gradients are float32.
+// workspace holds the per-row dO.O values, float32 [B][Hq][n].
+hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const uint8_t* valid, const void* o,
+                                const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                                float* workspace, const AttnShape& s, int o_f32, hipStream_t stream);
+
+size_t attn_bwd_workspace_bytes(int32_t B, int64_t n, int32_t Hq);
+
+}  // namespace ulysses
