@@ -55,9 +55,12 @@ def assert_close(name: str, got: np.ndarray, ref: np.ndarray, tol: float, rel_bf
     bound = tol + (2.0 ** -8) * np.abs(np.where(both_inf, 0.0, ref)) if rel_bf16_storage else tol
     worst = float(err.max()) if err.size else 0.0
     bad = err > bound
-    say(f"  {name}: max_abs_err={worst:.3e} (tol {tol:g}{' + bf16 ulp' if rel_bf16_storage else ''}), "
+    tol_txt = f"{tol:g}" if np.ndim(tol) == 0 else f"1e-2 + bound (max {float(np.max(tol)):.3g})"
+    say(f"  {name}: max_abs_err={worst:.3e} (tol {tol_txt}{' + bf16 ulp' if rel_bf16_storage else ''}), "
         f"max|ref|={float(np.abs(np.where(np.isfinite(ref), ref, 0)).max()) if ref.size else 0:.3f}")
     if np.any(bad):
         idx = np.unravel_index(int(np.argmax(np.where(bad, err, -1))), err.shape)
-        raise AssertionError(f"{name}: max error {worst:.4e} > tol at {idx}: got {got[idx]!r} ref {ref[idx]!r}")
+        lim = bound[idx] if np.ndim(bound) else bound
+        raise AssertionError(f"{name}: error {float(err[idx]):.4e} > {float(lim):.4e} at {idx}: "
+                             f"got {got[idx]!r} ref {ref[idx]!r}")
     return worst

@@ -186,7 +186,9 @@ __global__ __launch_bounds__(kThreads, 2) void dkdv_kernel(const BwdParams p) {
   __shared__ __attribute__((aligned(128))) uint8_t smem[2 * L::kStageAligned];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  // wave index as a scalar: every branch that guards a matrix-core instruction
+  // must be wave-uniform to the compiler (MFMA does not honour EXEC)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
@@ -406,7 +408,9 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const BwdParams p) {
   __shared__ __attribute__((aligned(128))) uint8_t smem[L::kStage];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  // wave index as a scalar: every branch that guards a matrix-core instruction
+  // must be wave-uniform to the compiler (MFMA does not honour EXEC)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
