@@ -79,6 +79,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="time only a plain 512 MiB device-to-device copy (torch copy_), the reference kernel "
+                         "for scaling the FETCH_SIZE / WRITE_SIZE hardware counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share of the Ulysses hot path; the all-to-all is emulated on a "
@@ -94,6 +97,20 @@ def main():
         sys.exit(2)
     U.load_library()
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.int16, device=dev).fill_(1)     # 512 MiB
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / args.steps
+        print(json.dumps({"copy_bytes_read": src.numel() * 2, "copy_bytes_written": src.numel() * 2,
+                          "ms": dt * 1e3, "GBs": 2 * src.numel() * 2 / dt / 1e9}), flush=True)
+        return
     w = synth.WORKLOADS[args.workload]
     P, nl, n, D = w.P, w.n_local, w.n, w.D
     hq, hkv = w.hq, w.hkv
