@@ -149,7 +149,8 @@ ULYSSES_API ulysses_status_t ulysses_repack_head2seq(const void* src, void* dst,
  * cores, fp32 accumulation and softmax); in_dtype F32 with o_dtype F32
  * (fp32 throughout).  D must be 64 or 128.
  * Errors: INVALID_ARG for null pointers (non-empty problem), B < 0, n < 0,
- * Hq < 1, Hkv < 1, Hq % Hkv != 0, a non-finite scale, causal not 0/1,
+ * Hq < 1, Hkv < 1, Hq % Hkv != 0, a scale that is not finite and positive,
+ * causal not 0/1,
  * q/k/v/o not 16-byte aligned, lse not 4-byte aligned, or an output
  * overlapping any input or the other output.  UNSUPPORTED for other D or
  * dtype combinations, or n*max(Hq,Hkv)*D >= 2^40 elements.

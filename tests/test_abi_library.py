@@ -93,6 +93,8 @@ def test_fwd_validation(lib):
     assert _fwd(lib, n=-1) == INVALID
     assert _fwd(lib, scale=float("nan")) == INVALID
     assert _fwd(lib, scale=float("inf")) == INVALID
+    assert _fwd(lib, scale=0.0) == INVALID
+    assert _fwd(lib, scale=-0.5) == INVALID
     assert _fwd(lib, causal=2) == INVALID
     assert _fwd(lib, q=None) == INVALID
     assert _fwd(lib, lse=None) == INVALID

@@ -54,7 +54,7 @@ ulysses_status_t check_attn_shape(int32_t B, int64_t n, int32_t Hq, int32_t Hkv,
                                   int32_t causal, ulysses_dtype_t in_dtype, ulysses_dtype_t o_dtype, bool* empty) {
   *empty = false;
   if (B < 0 || n < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ULYSSES_ERR_INVALID_ARG;
-  if (!isfinite(scale)) return ULYSSES_ERR_INVALID_ARG;
+  if (!isfinite(scale) || !(scale > 0.f)) return ULYSSES_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return ULYSSES_ERR_INVALID_ARG;
   if (!known_dtype(in_dtype) || !known_dtype(o_dtype)) return ULYSSES_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return ULYSSES_ERR_UNSUPPORTED;

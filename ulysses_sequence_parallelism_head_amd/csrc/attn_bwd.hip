@@ -14,15 +14,18 @@
 // Three kernels:
 //  1. rowdot: Dl[b][h][t] = dO . O per query row (float32 workspace).
 //  2. dkdv (KV-stationary): a workgroup of 4 waves owns 128 keys of one KV
-//     head (32 per wave, K and V held in registers) and streams the 32-row
+//     head (32 per wave, K and V held in registers) and streams the 64-row
 //     query tiles of every query head of the group that can see them.  It
 //     computes S = Q K^T and dP = dO V^T with the key on the lane (so P and dS
 //     come out as MFMA B operands) and accumulates dV^T += dO^T P and
-//     dK^T += Q^T dS.  Q, dO are staged row-major and transposed (Q^T, dO^T,
-//     slot-permuted) in LDS, double-buffered.
+//     dK^T += Q^T dS.  Q and dO are staged once, row-major with swizzled
+//     chunks; the Q^T and dO^T operands come from transposing LDS reads
+//     (ds_read_b64_tr_b16).  One wave per SIMD: 512 registers hold the K/V
+//     rows, both accumulators and two 32-row blocks in flight without spills.
 //  3. dq (Q-stationary, laid out like the forward): recomputes S^T = K Q^T and
 //     dP^T = V dO^T with the query on the lane and accumulates
-//     dQ^T += K^T dS^T from K^T staged in LDS.  Keeping dQ in its own pass
+//     dQ^T += K^T dS^T, the K^T operand read transposed from the row-major K
+//     tile.  Keeping dQ in its own pass
 //     avoids float32 atomics (whose traffic would grow as n^2 / block) and
 //     makes every gradient deterministic.
 // Rows below kSplitRows use a hi/lo bf16 split of P and dS (two MFMAs) for
@@ -95,51 +98,45 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const BwdParams p) {
   }
 }
 
-// Load a 4-row x 8-column bf16 block: rows r0..r0+3 of a [rows][stride]
-// tensor starting at column c0 (rows >= nrows read as zero).
-__device__ __forceinline__ void load_block4x8(u32x4* dst, const uint16_t* base, int64_t row_stride, int r0,
-                                              int nrows, int c0) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int r = r0 + e;
-    dst[e] = (r < nrows) ? *reinterpret_cast<const u32x4*>(base + int64_t(r) * row_stride + c0) : u32x4{0, 0, 0, 0};
-  }
-}
-
 // ------------------------------------------------------------------- dkdv
 template <int D>
 struct DkdvLayout {
-  static constexpr int kRows = 32;                        // query rows per tile
-  static constexpr int kStrideRM = D + 8;                 // row-major tiles, bf16 elements per row
-  static constexpr int kBytesRM = kRows * kStrideRM * 2;
-  static constexpr int kBytesT = D * kRows * 2;           // transposed tiles: D rows of 32 slots
+  static constexpr int kRows = 64;                        // query rows per tile
+  static constexpr int kRowBytes = 2 * D;
+  static constexpr int kChunks = D / 8;
+  static constexpr int kBytesRM = kRows * kRowBytes;
   static constexpr int kOffQ = 0;
   static constexpr int kOffDO = kOffQ + kBytesRM;
-  static constexpr int kOffQT = kOffDO + kBytesRM;
-  static constexpr int kOffDOT = kOffQT + kBytesT;
-  static constexpr int kOffLSE = kOffDOT + kBytesT;
+  static constexpr int kOffLSE = kOffDO + kBytesRM;
   static constexpr int kOffDL = kOffLSE + kRows * 4;
   static constexpr int kStage = kOffDL + kRows * 4;
   static constexpr int kStageAligned = (kStage + 127) / 128 * 128;
-  static constexpr int kBlocks = (kRows / 4) * (D / 8);   // 4x8 staging blocks per tensor
+  static constexpr int kChunksPerThread = kRows * kChunks / kThreads;   // per tensor
 };
 
+template <int D>
 struct DkdvStaging {
-  u32x4 r[4];
+  u32x4 q[DkdvLayout<D>::kChunksPerThread];
+  u32x4 d[DkdvLayout<D>::kChunksPerThread];
   float lse2, dl;
 };
 
 template <int D>
-__device__ __forceinline__ void dkdv_load(DkdvStaging& st, const BwdParams& p, int b, int head, int t0, int tid) {
+__device__ __forceinline__ void dkdv_load(DkdvStaging<D>& st, const BwdParams& p, int b, int head, int t0, int tid) {
   using L = DkdvLayout<D>;
-  const int64_t stride = int64_t(p.Hq) * D;
-  if (tid < 2 * L::kBlocks) {
-    const int which = tid / L::kBlocks;         // 0: Q, 1: dO
-    const int blk = tid % L::kBlocks;
-    const int dg = blk % (D / 8);
-    const int rg = blk / (D / 8);
-    const uint16_t* src = (which == 0 ? p.q : p.dout) + (int64_t(b) * p.n * p.Hq + head) * D;
-    load_block4x8(st.r, src, stride, t0 + rg * 4, p.n, dg * 8);
+  const int64_t base = (int64_t(b) * p.n * p.Hq + head) * D;
+#pragma unroll
+  for (int u = 0; u < L::kChunksPerThread; ++u) {
+    const int c = tid + u * kThreads;
+    const int t = t0 + c / L::kChunks;
+    if (t < p.n) {
+      const int64_t off = base + int64_t(t) * p.Hq * D + (c % L::kChunks) * 8;
+      st.q[u] = *reinterpret_cast<const u32x4*>(p.q + off);
+      st.d[u] = *reinterpret_cast<const u32x4*>(p.dout + off);
+    } else {
+      st.q[u] = u32x4{0, 0, 0, 0};
+      st.d[u] = u32x4{0, 0, 0, 0};
+    }
   }
   if (tid < L::kRows) {
     const int t = t0 + tid;
@@ -155,22 +152,14 @@ __device__ __forceinline__ void dkdv_load(DkdvStaging& st, const BwdParams& p, i
 }
 
 template <int D>
-__device__ __forceinline__ void dkdv_store(const DkdvStaging& st, uint8_t* stage, int tid) {
+__device__ __forceinline__ void dkdv_store(const DkdvStaging<D>& st, uint8_t* stage, int tid) {
   using L = DkdvLayout<D>;
-  if (tid < 2 * L::kBlocks) {
-    const int which = tid / L::kBlocks;
-    const int blk = tid % L::kBlocks;
-    const int dg = blk % (D / 8);
-    const int rg = blk / (D / 8);
-    uint16_t* rm = reinterpret_cast<uint16_t*>(stage + (which == 0 ? L::kOffQ : L::kOffDO));
 #pragma unroll
-    for (int e = 0; e < 4; ++e) *reinterpret_cast<u32x4*>(rm + (rg * 4 + e) * L::kStrideRM + dg * 8) = st.r[e];
-    uint8_t* tt = stage + (which == 0 ? L::kOffQT : L::kOffDOT);
-    const int slot = tslot(rg * 4);
-    const int chunk = slot >> 3, half = (slot >> 2) & 1;
-#pragma unroll
-    for (int e2 = 0; e2 < 8; ++e2)
-      *reinterpret_cast<u32x2*>(tt + t32_off(dg * 8 + e2, chunk) + half * 8) = transpose_col(st.r, e2);
+  for (int u = 0; u < L::kChunksPerThread; ++u) {
+    const int c = tid + u * kThreads;
+    const int off = rm_off(c / L::kChunks, c % L::kChunks, L::kRowBytes);
+    *reinterpret_cast<u32x4*>(stage + L::kOffQ + off) = st.q[u];
+    *reinterpret_cast<u32x4*>(stage + L::kOffDO + off) = st.d[u];
   }
   if (tid < L::kRows) {
     reinterpret_cast<float*>(stage + L::kOffLSE)[tid] = st.lse2;
@@ -178,8 +167,24 @@ __device__ __forceinline__ void dkdv_store(const DkdvStaging& st, uint8_t* stage
   }
 }
 
+// Pack 8 floats (x[0..7]) as the bf16 B operand of one MFMA, and optionally
+// the bf16 residual x - bf16(x) as a second operand.
+__device__ __forceinline__ u32x4 pack8(const float* x) {
+  return u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
+}
+
+__device__ __forceinline__ u32x4 pack8_residual(const float* x, const u32x4 hi) {
+  float r[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    r[2 * e] = x[2 * e] - bf16lo_to_f32(hi[e]);
+    r[2 * e + 1] = x[2 * e + 1] - bf16hi_to_f32(hi[e]);
+  }
+  return pack8(r);
+}
+
 template <int D, bool HAS_MASK>
-__global__ __launch_bounds__(kThreads, 2) void dkdv_kernel(const BwdParams p) {
+__global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdParams p) {
   using L = DkdvLayout<D>;
   constexpr int KK = D / 16;
   constexpr int DJ = D / 32;
@@ -227,7 +232,7 @@ __global__ __launch_bounds__(kThreads, 2) void dkdv_kernel(const BwdParams p) {
   const int ntq = (p.n - q_first + L::kRows - 1) / L::kRows;   // query tiles per head
   const int niter = p.g * ntq;
 
-  DkdvStaging st;
+  DkdvStaging<D> st;
   if (niter > 0) {
     dkdv_load<D>(st, p, b, kvh * p.g, q_first, tid);
     dkdv_store<D>(st, smem, tid);
@@ -241,79 +246,74 @@ __global__ __launch_bounds__(kThreads, 2) void dkdv_kernel(const BwdParams p) {
       dkdv_load<D>(st, p, b, kvh * p.g + nh, q_first + nt * L::kRows, tid);
     }
     const int t0 = q_first + (it % ntq) * L::kRows;
-    // rows t0..t0+31 see this wave's keys only if t0 + 31 >= k0w
-    if (wave_live && !(p.causal && t0 + L::kRows - 1 < k0w)) {
-      const uint16_t* qs = reinterpret_cast<const uint16_t*>(cur + L::kOffQ);
-      const uint16_t* dos = reinterpret_cast<const uint16_t*>(cur + L::kOffDO);
-      const uint8_t* qts = cur + L::kOffQT;
-      const uint8_t* dots = cur + L::kOffDOT;
+    if (wave_live) {
+      const uint8_t* qs = cur + L::kOffQ;
+      const uint8_t* dos = cur + L::kOffDO;
       const float* lse2s = reinterpret_cast<const float*>(cur + L::kOffLSE);
       const float* dls = reinterpret_cast<const float*>(cur + L::kOffDL);
-      const bool split = t0 < kSplitRows;
-
-      // S[q][key] and dP[q][key]: lane = key, rows q = (i/4)*8 + 4hh + i%4
-      f32x16 s = f32x16{}, dp = f32x16{};
+      // 32-row block rb sees this wave's keys only if its last row >= k0w
+      bool act[2];
+      f32x16 s[2], dp[2];
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const u32x4 aq = *reinterpret_cast<const u32x4*>(qs + l32 * L::kStrideRM + kk * 16 + hh * 8);
-        s = mfma32x32x16(aq, kf[kk], s);
-        const u32x4 ad = *reinterpret_cast<const u32x4*>(dos + l32 * L::kStrideRM + kk * 16 + hh * 8);
-        dp = mfma32x32x16(ad, vf[kk], dp);
+      for (int rb = 0; rb < 2; ++rb) {
+        act[rb] = !(p.causal && t0 + rb * 32 + 31 < k0w);
+        s[rb] = f32x16{};
+        dp[rb] = f32x16{};
       }
-
-      float pr[16], ds[16];
+      // S[q][key] and dP[q][key] for both row blocks: lane = key, rows q = (i/4)*8 + 4hh + i%4
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int r0 = g4 * 8 + hh * 4;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + r0);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dls + r0);
+      for (int rb = 0; rb < 2; ++rb) {
+        if (!act[rb]) continue;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = g4 * 4 + e;
-          const int t = t0 + r0 + e;
-          const bool ok = key_ok && !(p.causal && u > t);
-          const float pv = ok ? __builtin_amdgcn_exp2f(s[i] * p.c - l4[e]) : 0.f;
-          pr[i] = pv;
-          ds[i] = pv * (dp[i] - d4[e]);
+        for (int kk = 0; kk < KK; ++kk) {
+          const int off = rm_off(rb * 32 + l32, 2 * kk + hh, L::kRowBytes);
+          s[rb] = mfma32x32x16(*reinterpret_cast<const u32x4*>(qs + off), kf[kk], s[rb]);
+          dp[rb] = mfma32x32x16(*reinterpret_cast<const u32x4*>(dos + off), vf[kk], dp[rb]);
         }
       }
-
-      u32x4 ph[2], pl[2], dh[2], dl[2];
 #pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        const float* a = pr + 8 * f;
-        const float* c = ds + 8 * f;
-        ph[f] = u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(a[4], a[5]), pack_bf16x2(a[6], a[7])};
-        dh[f] = u32x4{pack_bf16x2(c[0], c[1]), pack_bf16x2(c[2], c[3]), pack_bf16x2(c[4], c[5]), pack_bf16x2(c[6], c[7])};
-        if (split) {
-          float ra[8], rc[8];
+      for (int rb = 0; rb < 2; ++rb) {
+        if (!act[rb]) continue;
+        const int r0 = t0 + rb * 32;
+        const bool split = r0 < kSplitRows;
+        float pr[16], ds[16];
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int rr = rb * 32 + g4 * 8 + hh * 4;
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + rr);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dls + rr);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            ra[2 * e] = a[2 * e] - bf16lo_to_f32(ph[f][e]);
-            ra[2 * e + 1] = a[2 * e + 1] - bf16hi_to_f32(ph[f][e]);
-            rc[2 * e] = c[2 * e] - bf16lo_to_f32(dh[f][e]);
-            rc[2 * e + 1] = c[2 * e + 1] - bf16hi_to_f32(dh[f][e]);
+            const int i = g4 * 4 + e;
+            const int t = t0 + rr + e;
+            const bool ok = key_ok && !(p.causal && u > t);
+            const float pv = ok ? __builtin_amdgcn_exp2f(fmaf(s[rb][i], p.c, -l4[e])) : 0.f;
+            pr[i] = pv;
+            ds[i] = pv * (dp[rb][i] - d4[e]);
           }
-          pl[f] = u32x4{pack_bf16x2(ra[0], ra[1]), pack_bf16x2(ra[2], ra[3]), pack_bf16x2(ra[4], ra[5]),
-                        pack_bf16x2(ra[6], ra[7])};
-          dl[f] = u32x4{pack_bf16x2(rc[0], rc[1]), pack_bf16x2(rc[2], rc[3]), pack_bf16x2(rc[4], rc[5]),
-                        pack_bf16x2(rc[6], rc[7])};
         }
-      }
-
-      // dV^T += dO^T P,  dK^T += Q^T dS   (A operands from the transposed tiles)
+        u32x4 ph[2], pl[2], dh[2], dl[2];
 #pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        const int chunk = f * 2 + hh;
+        for (int f = 0; f < 2; ++f) {
+          ph[f] = pack8(pr + 8 * f);
+          dh[f] = pack8(ds + 8 * f);
+          if (split) {
+            pl[f] = pack8_residual(pr + 8 * f, ph[f]);
+            dl[f] = pack8_residual(ds + 8 * f, dh[f]);
+          }
+        }
+        // dV^T += dO^T P,  dK^T += Q^T dS   (A operands read transposed from the row-major tiles)
 #pragma unroll
-        for (int j = 0; j < DJ; ++j) {
-          const int d = j * 32 + l32;
-          const u32x4 adt = *reinterpret_cast<const u32x4*>(dots + t32_off(d, chunk));
-          dva[j] = mfma32x32x16(adt, ph[f], dva[j]);
-          if (split) dva[j] = mfma32x32x16(adt, pl[f], dva[j]);
-          const u32x4 aqt = *reinterpret_cast<const u32x4*>(qts + t32_off(d, chunk));
-          dka[j] = mfma32x32x16(aqt, dh[f], dka[j]);
-          if (split) dka[j] = mfma32x32x16(aqt, dl[f], dka[j]);
+        for (int f = 0; f < 2; ++f) {
+#pragma unroll
+          for (int j = 0; j < DJ; ++j) {
+            const u32x4 adt = tr_operand(dos, L::kRowBytes, rb * 32 + 16 * f, 32 * j, lane);
+            dva[j] = mfma32x32x16(adt, ph[f], dva[j]);
+            if (split) dva[j] = mfma32x32x16(adt, pl[f], dva[j]);
+            const u32x4 aqt = tr_operand(qs, L::kRowBytes, rb * 32 + 16 * f, 32 * j, lane);
+            dka[j] = mfma32x32x16(aqt, dh[f], dka[j]);
+            if (split) dka[j] = mfma32x32x16(aqt, dl[f], dka[j]);
+          }
         }
       }
     }
@@ -342,33 +342,39 @@ __global__ __launch_bounds__(kThreads, 2) void dkdv_kernel(const BwdParams p) {
 template <int D>
 struct DqLayout {
   static constexpr int kBN = 64;                          // keys per tile
-  static constexpr int kStrideRM = D + 8;
-  static constexpr int kBytesRM = kBN * kStrideRM * 2;
-  static constexpr int kBytesT = D * kBN * 2;             // K^T: D rows of 64 slots
+  static constexpr int kRowBytes = 2 * D;
+  static constexpr int kChunks = D / 8;
+  static constexpr int kBytesRM = kBN * kRowBytes;
   static constexpr int kOffK = 0;
   static constexpr int kOffV = kOffK + kBytesRM;
-  static constexpr int kOffKT = kOffV + kBytesRM;
-  static constexpr int kOffValid = kOffKT + kBytesT;
+  static constexpr int kOffValid = kOffV + kBytesRM;
   static constexpr int kStage = kOffValid + kBN;
-  static constexpr int kBlocks = (kBN / 4) * (D / 8);     // 4x8 staging blocks per tensor
+  static constexpr int kStageAligned = (kStage + 127) / 128 * 128;
+  static constexpr int kChunksPerThread = kBN * kChunks / kThreads;     // per tensor
 };
 
+template <int D>
 struct DqStaging {
-  u32x4 kr[4], vr[4];
+  u32x4 kr[DqLayout<D>::kChunksPerThread], vr[DqLayout<D>::kChunksPerThread];
   uint32_t vbyte;
 };
 
 template <int D, bool HAS_MASK>
-__device__ __forceinline__ void dq_load(DqStaging& st, const BwdParams& p, int b, int kvh, int tile, int tid) {
+__device__ __forceinline__ void dq_load(DqStaging<D>& st, const BwdParams& p, int b, int kvh, int tile, int tid) {
   using L = DqLayout<D>;
   const int key0 = tile * L::kBN;
-  if (tid < L::kBlocks) {
-    const int dg = tid % (D / 8);
-    const int kg = tid / (D / 8);
-    const int64_t stride = int64_t(p.Hkv) * D;
-    const int64_t off = (int64_t(b) * p.n * p.Hkv + kvh) * D;
-    load_block4x8(st.kr, p.k + off, stride, key0 + kg * 4, p.n, dg * 8);
-    load_block4x8(st.vr, p.v + off, stride, key0 + kg * 4, p.n, dg * 8);
+#pragma unroll
+  for (int u = 0; u < L::kChunksPerThread; ++u) {
+    const int c = tid + u * kThreads;
+    const int key = key0 + c / L::kChunks;
+    if (key < p.n) {
+      const int64_t off = ((int64_t(b) * p.n + key) * p.Hkv + kvh) * D + (c % L::kChunks) * 8;
+      st.kr[u] = *reinterpret_cast<const u32x4*>(p.k + off);
+      st.vr[u] = *reinterpret_cast<const u32x4*>(p.v + off);
+    } else {
+      st.kr[u] = u32x4{0, 0, 0, 0};
+      st.vr[u] = u32x4{0, 0, 0, 0};
+    }
   }
   if (HAS_MASK && tid < L::kBN) {
     const int key = key0 + tid;
@@ -377,25 +383,14 @@ __device__ __forceinline__ void dq_load(DqStaging& st, const BwdParams& p, int b
 }
 
 template <int D, bool HAS_MASK>
-__device__ __forceinline__ void dq_store(const DqStaging& st, uint8_t* stage, int tid) {
+__device__ __forceinline__ void dq_store(const DqStaging<D>& st, uint8_t* stage, int tid) {
   using L = DqLayout<D>;
-  if (tid < L::kBlocks) {
-    const int dg = tid % (D / 8);
-    const int kg = tid / (D / 8);
-    uint16_t* ks = reinterpret_cast<uint16_t*>(stage + L::kOffK);
-    uint16_t* vs = reinterpret_cast<uint16_t*>(stage + L::kOffV);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      *reinterpret_cast<u32x4*>(ks + (kg * 4 + e) * L::kStrideRM + dg * 8) = st.kr[e];
-      *reinterpret_cast<u32x4*>(vs + (kg * 4 + e) * L::kStrideRM + dg * 8) = st.vr[e];
-    }
-    uint8_t* kt = stage + L::kOffKT;
-    const int k4 = kg * 4;
-    const int slot = (k4 & 32) | tslot(k4 & 31);
-    const int chunk = slot >> 3, half = (slot >> 2) & 1;
-#pragma unroll
-    for (int e2 = 0; e2 < 8; ++e2)
-      *reinterpret_cast<u32x2*>(kt + t64_off(dg * 8 + e2, chunk) + half * 8) = transpose_col(st.kr, e2);
+  for (int u = 0; u < L::kChunksPerThread; ++u) {
+    const int c = tid + u * kThreads;
+    const int off = rm_off(c / L::kChunks, c % L::kChunks, L::kRowBytes);
+    *reinterpret_cast<u32x4*>(stage + L::kOffK + off) = st.kr[u];
+    *reinterpret_cast<u32x4*>(stage + L::kOffV + off) = st.vr[u];
   }
   if (HAS_MASK && tid < L::kBN) stage[L::kOffValid + tid] = uint8_t(st.vbyte);
 }
@@ -405,7 +400,7 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const BwdParams p) {
   using L = DqLayout<D>;
   constexpr int KK = D / 16;
   constexpr int DJ = D / 32;
-  __shared__ __attribute__((aligned(128))) uint8_t smem[L::kStage];
+  __shared__ __attribute__((aligned(128))) uint8_t smem[2 * L::kStageAligned];
 
   const int tid = threadIdx.x;
   // wave index as a scalar: every branch that guards a matrix-core instruction
@@ -453,77 +448,66 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const BwdParams p) {
 #pragma unroll
   for (int j = 0; j < DJ; ++j) dqa[j] = f32x16{};
 
-  DqStaging st;
-  if (ntiles > 0) dq_load<D, HAS_MASK>(st, p, b, kvh, 0, tid);
+  DqStaging<D> st;
+  dq_load<D, HAS_MASK>(st, p, b, kvh, 0, tid);
+  dq_store<D, HAS_MASK>(st, smem, tid);
+  __syncthreads();
 
   for (int it = 0; it < ntiles; ++it) {
-    __syncthreads();                      // previous tile fully consumed
-    dq_store<D, HAS_MASK>(st, smem, tid);
-    __syncthreads();
+    uint8_t* cur = smem + (it & 1) * L::kStageAligned;
     if (it + 1 < ntiles) dq_load<D, HAS_MASK>(st, p, b, kvh, it + 1, tid);   // in flight during the math
 
     const int tile0 = it * L::kBN;
-    if (!wave_live || (p.causal && tile0 > wave_last)) continue;
-    const uint16_t* ks = reinterpret_cast<const uint16_t*>(smem + L::kOffK);
-    const uint16_t* vs = reinterpret_cast<const uint16_t*>(smem + L::kOffV);
-    const uint8_t* kts = smem + L::kOffKT;
-    const uint8_t* vb = smem + L::kOffValid;
-
+    if (wave_live && !(p.causal && tile0 > wave_last)) {
+      const uint8_t* ks = cur + L::kOffK;
+      const uint8_t* vs = cur + L::kOffV;
+      const uint8_t* vb = cur + L::kOffValid;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int key0 = tile0 + half * 32;
-      if (p.causal && key0 > wave_last) break;
-      // S^T[key][q] and dP^T[key][q]: lane = query row t, rows key = (i/4)*8 + 4hh + i%4
-      f32x16 s = f32x16{}, dp = f32x16{};
+      for (int half = 0; half < 2; ++half) {
+        const int key0 = tile0 + half * 32;
+        if (p.causal && key0 > wave_last) break;
+        // S^T[key][q] and dP^T[key][q]: lane = query row t, rows key = (i/4)*8 + 4hh + i%4
+        f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const u32x4 ak = *reinterpret_cast<const u32x4*>(ks + (half * 32 + l32) * L::kStrideRM + kk * 16 + hh * 8);
-        s = mfma32x32x16(ak, qf[kk], s);
-        const u32x4 av = *reinterpret_cast<const u32x4*>(vs + (half * 32 + l32) * L::kStrideRM + kk * 16 + hh * 8);
-        dp = mfma32x32x16(av, df[kk], dp);
-      }
-      float ds[16];
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        uint32_t vw = 0xffffffffu;
-        if (HAS_MASK) vw = *reinterpret_cast<const uint32_t*>(vb + half * 32 + g4 * 8 + hh * 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = g4 * 4 + e;
-          const int key = key0 + g4 * 8 + hh * 4 + e;
-          const bool ok = key < p.n && !(p.causal && key > t) && (!HAS_MASK || ((vw >> (8 * e)) & 0xffu));
-          const float pv = ok ? __builtin_amdgcn_exp2f(s[i] * p.c - lse2) : 0.f;
-          ds[i] = pv * (dp[i] - dl);
+        for (int kk = 0; kk < KK; ++kk) {
+          const int off = rm_off(half * 32 + l32, 2 * kk + hh, L::kRowBytes);
+          s = mfma32x32x16(*reinterpret_cast<const u32x4*>(ks + off), qf[kk], s);
+          dp = mfma32x32x16(*reinterpret_cast<const u32x4*>(vs + off), df[kk], dp);
         }
-      }
-      u32x4 dh[2], dlo[2];
+        float ds[16];
 #pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        const float* c = ds + 8 * f;
-        dh[f] = u32x4{pack_bf16x2(c[0], c[1]), pack_bf16x2(c[2], c[3]), pack_bf16x2(c[4], c[5]), pack_bf16x2(c[6], c[7])};
-        if (split) {
-          float rc[8];
+        for (int g4 = 0; g4 < 4; ++g4) {
+          uint32_t vw = 0xffffffffu;
+          if (HAS_MASK) vw = *reinterpret_cast<const uint32_t*>(vb + half * 32 + g4 * 8 + hh * 4);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            rc[2 * e] = c[2 * e] - bf16lo_to_f32(dh[f][e]);
-            rc[2 * e + 1] = c[2 * e + 1] - bf16hi_to_f32(dh[f][e]);
+            const int i = g4 * 4 + e;
+            const int key = key0 + g4 * 8 + hh * 4 + e;
+            const bool ok = key < p.n && !(p.causal && key > t) && (!HAS_MASK || ((vw >> (8 * e)) & 0xffu));
+            const float pv = ok ? __builtin_amdgcn_exp2f(fmaf(s[i], p.c, -lse2)) : 0.f;
+            ds[i] = pv * (dp[i] - dl);
           }
-          dlo[f] = u32x4{pack_bf16x2(rc[0], rc[1]), pack_bf16x2(rc[2], rc[3]), pack_bf16x2(rc[4], rc[5]),
-                         pack_bf16x2(rc[6], rc[7])};
         }
-      }
-      // dQ^T += K^T dS^T
+        u32x4 dh[2], dlo[2];
 #pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        const int chunk = half * 4 + f * 2 + hh;
+        for (int f = 0; f < 2; ++f) {
+          dh[f] = pack8(ds + 8 * f);
+          if (split) dlo[f] = pack8_residual(ds + 8 * f, dh[f]);
+        }
+        // dQ^T += K^T dS^T  (K^T read transposed from the row-major K tile)
 #pragma unroll
-        for (int j = 0; j < DJ; ++j) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(kts + t64_off(j * 32 + l32, chunk));
-          dqa[j] = mfma32x32x16(a, dh[f], dqa[j]);
-          if (split) dqa[j] = mfma32x32x16(a, dlo[f], dqa[j]);
+        for (int f = 0; f < 2; ++f) {
+#pragma unroll
+          for (int j = 0; j < DJ; ++j) {
+            const u32x4 a = tr_operand(ks, L::kRowBytes, half * 32 + 16 * f, 32 * j, lane);
+            dqa[j] = mfma32x32x16(a, dh[f], dqa[j]);
+            if (split) dqa[j] = mfma32x32x16(a, dlo[f], dqa[j]);
+          }
         }
       }
     }
+    if (it + 1 < ntiles) dq_store<D, HAS_MASK>(st, smem + ((it + 1) & 1) * L::kStageAligned, tid);
+    __syncthreads();
   }
 
   if (t < p.n) {

@@ -18,17 +18,18 @@
 //    and the rescale of O stay in-lane (one swap between half-waves for the
 //    max).  O is accumulated transposed too, O^T += V^T P^T, with P^T used
 //    straight from the score registers as the B operand.
-//  * K tiles are stored row-major in LDS (16-byte padded rows); V tiles are
-//    transposed in registers while staging and stored as V^T with the key
-//    slots permuted to match the score registers' key order, in 16-byte
-//    chunks XOR-swizzled per row so that both the staging writes and the
-//    MFMA operand reads are free of bank conflicts.
+//  * K and V tiles are stored row-major in LDS with XOR-swizzled 16-byte
+//    chunks.  K rows feed S^T = K Q^T directly; the V^T operand of the PV
+//    product is read with the gfx950 transposing LDS read (ds_read_b64_tr_b16),
+//    in the key order of the score registers, so nothing is transposed in
+//    registers and both read patterns are free of bank conflicts.
 //  * Global->LDS staging of tile i+1 is issued before the MFMA work on tile i
 //    (double-buffered LDS, one barrier per tile).
-//  * Online softmax in base 2 (log2(e) folded into the scale).  The running
-//    max is only raised when a tile's max exceeds it by more than 8 (log2
-//    units): O and the row sum then carry factors up to 2^8, harmless in
-//    fp32, and the rescale of O is skipped on almost every tile.
+//  * Online softmax in base 2: the row max is taken on raw scores and each
+//    probability is one FMA (score * scale*log2(e) - max) and one v_exp_f32.
+//    The running max is only raised when a tile's max exceeds it by more than
+//    8 (log2 units): O and the row sum then carry factors up to 2^8, harmless
+//    in fp32, and the rescale of O is skipped on almost every tile.
 //  * Rows below kSplitRows use a hi/lo split of P (two bf16 MFMAs) to keep
 //    the error of the few-key rows, whose weights are large, far below 1e-2.
 //  * The grid is launched longest-first (last query blocks first) so the
@@ -50,15 +51,14 @@ constexpr float kRescaleSlack = 8.0f;   // log2 units
 
 template <int D>
 struct FwdLayout {
-  static constexpr int kStrideK = D + 8;                 // bf16 elements per K row in LDS
-  static constexpr int kBytesK = kBN * kStrideK * 2;
-  static constexpr int kBytesV = D * kBN * 2;            // V^T: D rows of 64 key slots (128 B)
+  static constexpr int kRowBytes = 2 * D;                // one K or V row (bf16) in LDS
+  static constexpr int kChunks = D / 8;                  // 16-byte chunks per row
+  static constexpr int kBytesK = kBN * kRowBytes;
+  static constexpr int kBytesV = kBN * kRowBytes;
   static constexpr int kBytesValid = kBN;
   static constexpr int kStage = kBytesK + kBytesV + kBytesValid;
   static constexpr int kStageAligned = (kStage + 127) / 128 * 128;
-  static constexpr int kKChunksPerRow = D / 8;           // 16-byte chunks per K/V row
-  static constexpr int kKChunksPerThread = kBN * kKChunksPerRow / kThreads;
-  static constexpr int kVBlocks = (kBN / 4) * (D / 8);   // 4 keys x 8 dims per staging block
+  static constexpr int kChunksPerThread = kBN * kChunks / kThreads;   // per tensor
 };
 
 struct FwdParams {
@@ -80,40 +80,28 @@ struct FwdParams {
 
 template <int D>
 struct Staging {
-  u32x4 kreg[FwdLayout<D>::kKChunksPerThread];
-  u32x4 vreg[4];
+  u32x4 kreg[FwdLayout<D>::kChunksPerThread];
+  u32x4 vreg[FwdLayout<D>::kChunksPerThread];
   uint32_t vbyte;
 };
 
+// Global -> registers: 16-byte chunks of the K and V rows of one 64-key tile
+// (consecutive threads read consecutive chunks of a row: coalesced).
 template <int D, bool HAS_MASK>
 __device__ __forceinline__ void stage_load(Staging<D>& st, const FwdParams& p, int b, int kvh, int tile, int tid) {
   using L = FwdLayout<D>;
   const int key_base = tile * kBN;
 #pragma unroll
-  for (int u = 0; u < L::kKChunksPerThread; ++u) {
+  for (int u = 0; u < L::kChunksPerThread; ++u) {
     const int c = tid + u * kThreads;
-    const int row = c / L::kKChunksPerRow;
-    const int col = c % L::kKChunksPerRow;
-    const int key = key_base + row;
+    const int key = key_base + c / L::kChunks;
     if (key < p.n) {
-      const int64_t off = ((int64_t(b) * p.n + key) * p.Hkv + kvh) * D + col * 8;
+      const int64_t off = ((int64_t(b) * p.n + key) * p.Hkv + kvh) * D + (c % L::kChunks) * 8;
       st.kreg[u] = *reinterpret_cast<const u32x4*>(p.k + off);
+      st.vreg[u] = *reinterpret_cast<const u32x4*>(p.v + off);
     } else {
       st.kreg[u] = u32x4{0, 0, 0, 0};
-    }
-  }
-  if (tid < L::kVBlocks) {
-    const int dg = tid % (D / 8);
-    const int kg = tid / (D / 8);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int key = key_base + kg * 4 + e;
-      if (key < p.n) {
-        const int64_t off = ((int64_t(b) * p.n + key) * p.Hkv + kvh) * D + dg * 8;
-        st.vreg[e] = *reinterpret_cast<const u32x4*>(p.v + off);
-      } else {
-        st.vreg[e] = u32x4{0, 0, 0, 0};
-      }
+      st.vreg[u] = u32x4{0, 0, 0, 0};
     }
   }
   if (HAS_MASK && tid < kBN) {
@@ -122,30 +110,16 @@ __device__ __forceinline__ void stage_load(Staging<D>& st, const FwdParams& p, i
   }
 }
 
+// Registers -> LDS: row-major tiles with swizzled chunks.
 template <int D, bool HAS_MASK>
 __device__ __forceinline__ void stage_store(const Staging<D>& st, uint8_t* stage, int tid) {
   using L = FwdLayout<D>;
-  uint16_t* ks = reinterpret_cast<uint16_t*>(stage);
-  uint8_t* vt = stage + L::kBytesK;
 #pragma unroll
-  for (int u = 0; u < L::kKChunksPerThread; ++u) {
+  for (int u = 0; u < L::kChunksPerThread; ++u) {
     const int c = tid + u * kThreads;
-    const int row = c / L::kKChunksPerRow;
-    const int col = c % L::kKChunksPerRow;
-    *reinterpret_cast<u32x4*>(ks + row * L::kStrideK + col * 8) = st.kreg[u];
-  }
-  if (tid < L::kVBlocks) {
-    const int dg = tid % (D / 8);
-    const int kg = tid / (D / 8);
-    const int kt = kg * 4;                       // first key of the group within the tile
-    const int slot = (kt & 32) | tslot(kt & 31);
-    const int chunk = slot >> 3;
-    const int half = (slot >> 2) & 1;
-#pragma unroll
-    for (int e2 = 0; e2 < 8; ++e2) {
-      const int d = dg * 8 + e2;
-      *reinterpret_cast<u32x2*>(vt + t64_off(d, chunk) + half * 8) = transpose_col(st.vreg, e2);
-    }
+    const int off = rm_off(c / L::kChunks, c % L::kChunks, L::kRowBytes);
+    *reinterpret_cast<u32x4*>(stage + off) = st.kreg[u];
+    *reinterpret_cast<u32x4*>(stage + L::kBytesK + off) = st.vreg[u];
   }
   if (HAS_MASK && tid < kBN) stage[L::kBytesK + L::kBytesV + tid] = uint8_t(st.vbyte);
 }
@@ -212,28 +186,28 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const FwdPar
 
     const int tile0 = it * kBN;
     if (wave_live && !(p.causal && tile0 > wave_last)) {
-      const uint16_t* ks = reinterpret_cast<const uint16_t*>(cur);
-      const uint8_t* vt = cur + L::kBytesK;
+      const uint8_t* ks = cur;
+      const uint8_t* vs = cur + L::kBytesK;
       const bool act1 = !(p.causal && tile0 + 32 > wave_last);   // second half-tile has a visible key
 
       // ---- S^T for the two 32-key halves
       f32x16 s0 = f32x16{}, s1 = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        const u32x4 a0 = *reinterpret_cast<const u32x4*>(ks + l32 * L::kStrideK + kk * 16 + hh * 8);
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(ks + rm_off(l32, 2 * kk + hh, L::kRowBytes));
         s0 = mfma32x32x16(a0, qf[kk], s0);
         if (act1) {
-          const u32x4 a1 = *reinterpret_cast<const u32x4*>(ks + (32 + l32) * L::kStrideK + kk * 16 + hh * 8);
+          const u32x4 a1 = *reinterpret_cast<const u32x4*>(ks + rm_off(32 + l32, 2 * kk + hh, L::kRowBytes));
           s1 = mfma32x32x16(a1, qf[kk], s1);
         }
       }
 
-      // ---- scale to log2 units and mask
+      // ---- raw scores and masks (masked keys -> -inf)
       float x[32];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        x[i] = s0[i] * p.c;
-        x[16 + i] = act1 ? s1[i] * p.c : -INFINITY;
+        x[i] = s0[i];
+        x[16 + i] = act1 ? s1[i] : -INFINITY;
       }
       const bool diag = p.causal && (tile0 + kBN - 1 > p0);
       const bool tail = !HAS_MASK && (tile0 + kBN > p.n);
@@ -256,11 +230,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const FwdPar
         }
       }
 
-      // ---- online softmax (lazy rescale)
-      float mx = x[0];
+      // ---- online softmax (lazy rescale); scale > 0, so max(s * c) = max(s) * c
+      float mr = x[0];
 #pragma unroll
-      for (int i = 1; i < 32; ++i) mx = fmaxf(mx, x[i]);
-      mx = fmaxf(mx, swap_halves(mx));
+      for (int i = 1; i < 32; ++i) mr = fmaxf(mr, x[i]);
+      mr = fmaxf(mr, swap_halves(mr));
+      const float mx = mr * p.c;
       const bool raise = mx > m_ref + kRescaleSlack;
       if (__any(raise)) {
         const float alpha = raise ? __builtin_amdgcn_exp2f(m_ref - mx) : 1.0f;
@@ -271,11 +246,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const FwdPar
 #pragma unroll
           for (int i = 0; i < 16; ++i) oacc[j][i] *= alpha;
       }
-      const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+      const float neg_m = (m_ref == -INFINITY) ? 0.f : -m_ref;
       float pr[32];
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
-        pr[i] = __builtin_amdgcn_exp2f(x[i] - m_use);
+        pr[i] = __builtin_amdgcn_exp2f(fmaf(x[i], p.c, neg_m));
         lsum += pr[i];
       }
 
@@ -306,11 +281,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const FwdPar
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
         if (f >= 2 && !act1) break;
-        const int chunk = f * 2 + hh;            // slot f*16 + 8*hh within the tile
 #pragma unroll
         for (int j = 0; j < DJ; ++j) {
-          const int d = j * 32 + l32;
-          const u32x4 a = *reinterpret_cast<const u32x4*>(vt + t64_off(d, chunk));
+          // V^T rows d = 32j + l%32, keys in the order of phi[f] (tile rows 16f + ...)
+          const u32x4 a = tr_operand(vs, L::kRowBytes, 16 * f, 32 * j, lane);
           oacc[j] = mfma32x32x16(a, phi[f], oacc[j]);
           if (split) oacc[j] = mfma32x32x16(a, plo[f], oacc[j]);
         }

@@ -105,4 +105,48 @@ __device__ __forceinline__ u32x2 transpose_col(const u32x4* rows, int c) {
   return u32x2{x0 | (x1 << 16), x2 | (x3 << 16)};
 }
 
+// ---- row-major tiles with XOR-swizzled 16-byte chunks
+//
+// A tile row holds D bf16 (D/8 chunks of 16 bytes).  Chunk c of row r is
+// stored at physical chunk c ^ rm_swz(r) (low three bits only), where
+// rm_swz takes all 8 values on any 8 consecutive rows and the 4 values of one
+// parity on any 4 aligned rows.  Then
+//  * 16-byte row reads by 8 lanes on 8 consecutive rows (an MFMA operand whose
+//    rows are on the lanes) hit 8 distinct bank groups, and
+//  * transposing reads (ds_read_b64_tr_b16), where 16 lanes cover 4 aligned
+//    rows x 32 bytes, hit 8 distinct bank groups too.
+__device__ __forceinline__ int rm_swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
+__device__ __forceinline__ int rm_off(int r, int chunk, int row_bytes) {
+  return r * row_bytes + ((chunk ^ rm_swz(r)) << 4);
+}
+
+// gfx950 transposing LDS read.  Within each group of 16 lanes, lane i returns
+// element (i % 4) of the 8-byte chunks supplied by lanes 4e + i/4, e = 0..3:
+// the 16 lanes together read 4 rows x 16 columns and each lane receives one
+// column (4 rows).
+__device__ __forceinline__ u32x2 ds_read_tr16_b64(const uint8_t* lds) {
+  typedef short i16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(const_cast<uint8_t*>(lds)));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+// MFMA A operand (row m = l%32 of a 32-row block, 8 contraction slots) taken
+// transposed from a row-major swizzled tile T[rows][D]: lane l gets
+// T[r][col] for col = col0 + l%32 and the 8 rows
+//   r0 + 4*(l/32) + {0,1,2,3}  and  r0 + 8 + 4*(l/32) + {0,1,2,3},
+// i.e. exactly the row order in which a lane holds its share of an MFMA
+// accumulator column (rows (i/4)*8 + 4*(l/32) + i%4, i = 8k .. 8k+7).
+// r0 must be a multiple of 16 and col0 a multiple of 32.
+__device__ __forceinline__ u32x4 tr_operand(const uint8_t* tile, int row_bytes, int r0, int col0, int lane) {
+  const int hh = lane >> 5;
+  const int r = r0 + 4 * hh + ((lane & 15) >> 2);
+  const int col = col0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int sub = (col & 7) * 2;                    // byte offset inside the 16-byte chunk (0 or 8)
+  const u32x2 a = ds_read_tr16_b64(tile + rm_off(r, col >> 3, row_bytes) + sub);
+  const u32x2 b = ds_read_tr16_b64(tile + rm_off(r + 8, col >> 3, row_bytes) + sub);
+  return u32x4{a[0], a[1], b[0], b[1]};
+}
+
 }  // namespace ulysses
