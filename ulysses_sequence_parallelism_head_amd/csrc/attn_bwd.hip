@@ -111,60 +111,23 @@ struct DkdvLayout {
   static constexpr int kOffDL = kOffLSE + kRows * 4;
   static constexpr int kStage = kOffDL + kRows * 4;
   static constexpr int kStageAligned = (kStage + 127) / 128 * 128;
-  static constexpr int kChunksPerThread = kRows * kChunks / kThreads;   // per tensor
 };
 
+// DMA the query tile t0 .. t0+63 of query head `head`: Q and dO rows into the
+// swizzled row-major tiles, the raw logsumexp and Dl values into two float
+// arrays (rows past n read as zero).
 template <int D>
-struct DkdvStaging {
-  u32x4 q[DkdvLayout<D>::kChunksPerThread];
-  u32x4 d[DkdvLayout<D>::kChunksPerThread];
-  float lse2, dl;
-};
-
-template <int D>
-__device__ __forceinline__ void dkdv_load(DkdvStaging<D>& st, const BwdParams& p, int b, int head, int t0, int tid) {
+__device__ __forceinline__ void dkdv_issue(uint8_t* stage, const BwdParams& p, int b, int head, int t0, int wave,
+                                           int lane) {
   using L = DkdvLayout<D>;
-  const int64_t base = (int64_t(b) * p.n * p.Hq + head) * D;
-#pragma unroll
-  for (int u = 0; u < L::kChunksPerThread; ++u) {
-    const int c = tid + u * kThreads;
-    const int t = t0 + c / L::kChunks;
-    if (t < p.n) {
-      const int64_t off = base + int64_t(t) * p.Hq * D + (c % L::kChunks) * 8;
-      st.q[u] = *reinterpret_cast<const u32x4*>(p.q + off);
-      st.d[u] = *reinterpret_cast<const u32x4*>(p.dout + off);
-    } else {
-      st.q[u] = u32x4{0, 0, 0, 0};
-      st.d[u] = u32x4{0, 0, 0, 0};
-    }
-  }
-  if (tid < L::kRows) {
-    const int t = t0 + tid;
-    if (t < p.n) {
-      const float l = p.lse[(int64_t(b) * p.Hq + head) * p.n + t];
-      st.lse2 = (l == -INFINITY) ? INFINITY : l * kLog2e;   // a row with no key contributes nothing
-      st.dl = p.rowdot[(int64_t(b) * p.Hq + head) * p.n + t];
-    } else {
-      st.lse2 = INFINITY;
-      st.dl = 0.f;
-    }
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void dkdv_store(const DkdvStaging<D>& st, uint8_t* stage, int tid) {
-  using L = DkdvLayout<D>;
-#pragma unroll
-  for (int u = 0; u < L::kChunksPerThread; ++u) {
-    const int c = tid + u * kThreads;
-    const int off = rm_off(c / L::kChunks, c % L::kChunks, L::kRowBytes);
-    *reinterpret_cast<u32x4*>(stage + L::kOffQ + off) = st.q[u];
-    *reinterpret_cast<u32x4*>(stage + L::kOffDO + off) = st.d[u];
-  }
-  if (tid < L::kRows) {
-    reinterpret_cast<float*>(stage + L::kOffLSE)[tid] = st.lse2;
-    reinterpret_cast<float*>(stage + L::kOffDL)[tid] = st.dl;
-  }
+  const int rows_ok = min(L::kRows, p.n - t0);
+  const int64_t off = ((int64_t(b) * p.n + t0) * p.Hq + head) * D;
+  const int stride = p.Hq * D * 2;
+  dma_tile<D, L::kRows, kWaves>(stage + L::kOffQ, p.q + off, stride, rows_ok, wave, lane);
+  dma_tile<D, L::kRows, kWaves>(stage + L::kOffDO, p.dout + off, stride, rows_ok, wave, lane);
+  const int64_t roff = (int64_t(b) * p.Hq + head) * p.n + t0;
+  if (wave == 0) dma4(buffer_rsrc(p.lse + roff, uint32_t(rows_ok) * 4u), stage + L::kOffLSE, lane * 4);
+  if (wave == 1) dma4(buffer_rsrc(p.rowdot + roff, uint32_t(rows_ok) * 4u), stage + L::kOffDL, lane * 4);
 }
 
 // Pack 8 floats (x[0..7]) as the bf16 B operand of one MFMA, and optionally
@@ -183,7 +146,7 @@ __device__ __forceinline__ u32x4 pack8_residual(const float* x, const u32x4 hi) 
   return pack8(r);
 }
 
-template <int D, bool HAS_MASK>
+template <int D, bool HAS_MASK, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdParams p) {
   using L = DkdvLayout<D>;
   constexpr int KK = D / 16;
@@ -228,35 +191,33 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdParams p) {
     dva[j] = f32x16{};
   }
 
-  const int q_first = p.causal ? kb * 128 : 0;
+  const int q_first = CAUSAL ? kb * 128 : 0;
   const int ntq = (p.n - q_first + L::kRows - 1) / L::kRows;   // query tiles per head
   const int niter = p.g * ntq;
 
-  DkdvStaging<D> st;
-  if (niter > 0) {
-    dkdv_load<D>(st, p, b, kvh * p.g, q_first, tid);
-    dkdv_store<D>(st, smem, tid);
-  }
+  if (niter > 0) dkdv_issue<D>(smem, p, b, kvh * p.g, q_first, wave, lane);
+  wait_vmem();
   __syncthreads();
 
   for (int it = 0; it < niter; ++it) {
     uint8_t* cur = smem + (it & 1) * L::kStageAligned;
     if (it + 1 < niter) {
       const int nh = (it + 1) / ntq, nt = (it + 1) % ntq;
-      dkdv_load<D>(st, p, b, kvh * p.g + nh, q_first + nt * L::kRows, tid);
+      dkdv_issue<D>(smem + ((it + 1) & 1) * L::kStageAligned, p, b, kvh * p.g + nh, q_first + nt * L::kRows,
+                    wave, lane);
     }
     const int t0 = q_first + (it % ntq) * L::kRows;
     if (wave_live) {
       const uint8_t* qs = cur + L::kOffQ;
       const uint8_t* dos = cur + L::kOffDO;
-      const float* lse2s = reinterpret_cast<const float*>(cur + L::kOffLSE);
+      const float* lses = reinterpret_cast<const float*>(cur + L::kOffLSE);
       const float* dls = reinterpret_cast<const float*>(cur + L::kOffDL);
       // 32-row block rb sees this wave's keys only if its last row >= k0w
       bool act[2];
       f32x16 s[2], dp[2];
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
-        act[rb] = !(p.causal && t0 + rb * 32 + 31 < k0w);
+        act[rb] = !(CAUSAL && t0 + rb * 32 + 31 < k0w);
         s[rb] = f32x16{};
         dp[rb] = f32x16{};
       }
@@ -266,7 +227,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdParams p) {
         if (!act[rb]) continue;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-          const int off = rm_off(rb * 32 + l32, 2 * kk + hh, L::kRowBytes);
+          const int off = rm_off<L::kRowBytes>(rb * 32 + l32, 2 * kk + hh);
           s[rb] = mfma32x32x16(*reinterpret_cast<const u32x4*>(qs + off), kf[kk], s[rb]);
           dp[rb] = mfma32x32x16(*reinterpret_cast<const u32x4*>(dos + off), vf[kk], dp[rb]);
         }
@@ -277,17 +238,22 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdParams p) {
         const int r0 = t0 + rb * 32;
         const bool split = r0 < kSplitRows;
         float pr[16], ds[16];
+        // element i is query row t0 + 4hh + C_i (C_i = rb*32 + (i/4)*8 + i%4, a
+        // compile-time constant); the key is visible iff u <= row, i.e. C_i >= lim
+        const int lim = CAUSAL ? u - t0 - 4 * hh : -0x7fffffff;
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int rr = rb * 32 + g4 * 8 + hh * 4;
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + rr);
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lses + rr);
           const f32x4 d4 = *reinterpret_cast<const f32x4*>(dls + rr);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = g4 * 4 + e;
-            const int t = t0 + rr + e;
-            const bool ok = key_ok && !(p.causal && u > t);
-            const float pv = ok ? __builtin_amdgcn_exp2f(fmaf(s[rb][i], p.c, -l4[e])) : 0.f;
+            const int ci = rb * 32 + g4 * 8 + e;
+            const bool ok = key_ok && ci >= lim;
+            // natural-log LSE -> base 2; a row with no visible key (LSE = -inf) contributes nothing
+            const float l2 = (l4[e] == -INFINITY) ? INFINITY : l4[e] * kLog2e;
+            const float pv = ok ? __builtin_amdgcn_exp2f(fmaf(s[rb][i], p.c, -l2)) : 0.f;
             pr[i] = pv;
             ds[i] = pv * (dp[rb][i] - d4[e]);
           }
@@ -307,17 +273,17 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdParams p) {
         for (int f = 0; f < 2; ++f) {
 #pragma unroll
           for (int j = 0; j < DJ; ++j) {
-            const u32x4 adt = tr_operand(dos, L::kRowBytes, rb * 32 + 16 * f, 32 * j, lane);
+            const u32x4 adt = tr_operand<L::kRowBytes>(dos, rb * 32 + 16 * f, 32 * j, lane);
             dva[j] = mfma32x32x16(adt, ph[f], dva[j]);
             if (split) dva[j] = mfma32x32x16(adt, pl[f], dva[j]);
-            const u32x4 aqt = tr_operand(qs, L::kRowBytes, rb * 32 + 16 * f, 32 * j, lane);
+            const u32x4 aqt = tr_operand<L::kRowBytes>(qs, rb * 32 + 16 * f, 32 * j, lane);
             dka[j] = mfma32x32x16(aqt, dh[f], dka[j]);
             if (split) dka[j] = mfma32x32x16(aqt, dl[f], dka[j]);
           }
         }
       }
     }
-    if (it + 1 < niter) dkdv_store<D>(st, smem + ((it + 1) & 1) * L::kStageAligned, tid);
+    wait_vmem();
     __syncthreads();
   }
 
@@ -350,52 +316,25 @@ struct DqLayout {
   static constexpr int kOffValid = kOffV + kBytesRM;
   static constexpr int kStage = kOffValid + kBN;
   static constexpr int kStageAligned = (kStage + 127) / 128 * 128;
-  static constexpr int kChunksPerThread = kBN * kChunks / kThreads;     // per tensor
-};
-
-template <int D>
-struct DqStaging {
-  u32x4 kr[DqLayout<D>::kChunksPerThread], vr[DqLayout<D>::kChunksPerThread];
-  uint32_t vbyte;
 };
 
 template <int D, bool HAS_MASK>
-__device__ __forceinline__ void dq_load(DqStaging<D>& st, const BwdParams& p, int b, int kvh, int tile, int tid) {
+__device__ __forceinline__ void dq_issue(uint8_t* stage, uint32_t& vbyte, const BwdParams& p, int b, int kvh,
+                                         int tile, int wave, int lane, int tid) {
   using L = DqLayout<D>;
   const int key0 = tile * L::kBN;
-#pragma unroll
-  for (int u = 0; u < L::kChunksPerThread; ++u) {
-    const int c = tid + u * kThreads;
-    const int key = key0 + c / L::kChunks;
-    if (key < p.n) {
-      const int64_t off = ((int64_t(b) * p.n + key) * p.Hkv + kvh) * D + (c % L::kChunks) * 8;
-      st.kr[u] = *reinterpret_cast<const u32x4*>(p.k + off);
-      st.vr[u] = *reinterpret_cast<const u32x4*>(p.v + off);
-    } else {
-      st.kr[u] = u32x4{0, 0, 0, 0};
-      st.vr[u] = u32x4{0, 0, 0, 0};
-    }
-  }
+  const int rows_ok = min(L::kBN, p.n - key0);
+  const int64_t off = ((int64_t(b) * p.n + key0) * p.Hkv + kvh) * D;
+  const int stride = p.Hkv * D * 2;
+  dma_tile<D, L::kBN, kWaves>(stage + L::kOffK, p.k + off, stride, rows_ok, wave, lane);
+  dma_tile<D, L::kBN, kWaves>(stage + L::kOffV, p.v + off, stride, rows_ok, wave, lane);
   if (HAS_MASK && tid < L::kBN) {
     const int key = key0 + tid;
-    st.vbyte = (key < p.n) ? (p.valid[int64_t(b) * p.n + key] != 0 ? 1u : 0u) : 0u;
+    vbyte = (key < p.n) ? (p.valid[int64_t(b) * p.n + key] != 0 ? 1u : 0u) : 0u;
   }
 }
 
-template <int D, bool HAS_MASK>
-__device__ __forceinline__ void dq_store(const DqStaging<D>& st, uint8_t* stage, int tid) {
-  using L = DqLayout<D>;
-#pragma unroll
-  for (int u = 0; u < L::kChunksPerThread; ++u) {
-    const int c = tid + u * kThreads;
-    const int off = rm_off(c / L::kChunks, c % L::kChunks, L::kRowBytes);
-    *reinterpret_cast<u32x4*>(stage + L::kOffK + off) = st.kr[u];
-    *reinterpret_cast<u32x4*>(stage + L::kOffV + off) = st.vr[u];
-  }
-  if (HAS_MASK && tid < L::kBN) stage[L::kOffValid + tid] = uint8_t(st.vbyte);
-}
-
-template <int D, bool HAS_MASK>
+template <int D, bool HAS_MASK, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const BwdParams p) {
   using L = DqLayout<D>;
   constexpr int KK = D / 16;
@@ -422,7 +361,7 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const BwdParams p) {
   const int t = p0 + l32;
   const int wave_last = min(p0 + 31, p.n - 1);
   const int wg_last = min(pb * p.pw + p.pw, p.n) - 1;
-  const int kend = p.causal ? wg_last + 1 : p.n;
+  const int kend = CAUSAL ? wg_last + 1 : p.n;
   const int ntiles = (kend + L::kBN - 1) / L::kBN;
   const bool wave_live = p0 < p.n;
   const bool split = p0 < kSplitRows;
@@ -448,33 +387,39 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const BwdParams p) {
 #pragma unroll
   for (int j = 0; j < DJ; ++j) dqa[j] = f32x16{};
 
-  DqStaging<D> st;
-  dq_load<D, HAS_MASK>(st, p, b, kvh, 0, tid);
-  dq_store<D, HAS_MASK>(st, smem, tid);
+  uint32_t vbyte = 0;
+  dq_issue<D, HAS_MASK>(smem, vbyte, p, b, kvh, 0, wave, lane, tid);
+  if (HAS_MASK && tid < L::kBN) smem[L::kOffValid + tid] = uint8_t(vbyte);
+  wait_vmem();
   __syncthreads();
 
   for (int it = 0; it < ntiles; ++it) {
     uint8_t* cur = smem + (it & 1) * L::kStageAligned;
-    if (it + 1 < ntiles) dq_load<D, HAS_MASK>(st, p, b, kvh, it + 1, tid);   // in flight during the math
+    uint8_t* nxt = smem + ((it + 1) & 1) * L::kStageAligned;
+    if (it + 1 < ntiles) dq_issue<D, HAS_MASK>(nxt, vbyte, p, b, kvh, it + 1, wave, lane, tid);   // in flight during the math
 
     const int tile0 = it * L::kBN;
-    if (wave_live && !(p.causal && tile0 > wave_last)) {
+    if (wave_live && !(CAUSAL && tile0 > wave_last)) {
       const uint8_t* ks = cur + L::kOffK;
       const uint8_t* vs = cur + L::kOffV;
       const uint8_t* vb = cur + L::kOffValid;
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int key0 = tile0 + half * 32;
-        if (p.causal && key0 > wave_last) break;
+        if (CAUSAL && key0 > wave_last) break;
         // S^T[key][q] and dP^T[key][q]: lane = query row t, rows key = (i/4)*8 + 4hh + i%4
         f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-          const int off = rm_off(half * 32 + l32, 2 * kk + hh, L::kRowBytes);
+          const int off = rm_off<L::kRowBytes>(half * 32 + l32, 2 * kk + hh);
           s = mfma32x32x16(*reinterpret_cast<const u32x4*>(ks + off), qf[kk], s);
           dp = mfma32x32x16(*reinterpret_cast<const u32x4*>(vs + off), df[kk], dp);
         }
         float ds[16];
+        // element i is key key0 + 4hh + C_i (C_i = (i/4)*8 + i%4, a compile-time
+        // constant); visible iff C_i <= lim (key < n, and key <= t if causal)
+        int lim = p.n - 1 - key0 - 4 * hh;
+        if (CAUSAL) lim = min(lim, t - key0 - 4 * hh);
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           uint32_t vw = 0xffffffffu;
@@ -482,8 +427,8 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const BwdParams p) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = g4 * 4 + e;
-            const int key = key0 + g4 * 8 + hh * 4 + e;
-            const bool ok = key < p.n && !(p.causal && key > t) && (!HAS_MASK || ((vw >> (8 * e)) & 0xffu));
+            const int ci = g4 * 8 + e;
+            const bool ok = ci <= lim && (!HAS_MASK || ((vw >> (8 * e)) & 0xffu));
             const float pv = ok ? __builtin_amdgcn_exp2f(fmaf(s[i], p.c, -lse2)) : 0.f;
             ds[i] = pv * (dp[i] - dl);
           }
@@ -499,14 +444,15 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const BwdParams p) {
         for (int f = 0; f < 2; ++f) {
 #pragma unroll
           for (int j = 0; j < DJ; ++j) {
-            const u32x4 a = tr_operand(ks, L::kRowBytes, half * 32 + 16 * f, 32 * j, lane);
+            const u32x4 a = tr_operand<L::kRowBytes>(ks, half * 32 + 16 * f, 32 * j, lane);
             dqa[j] = mfma32x32x16(a, dh[f], dqa[j]);
             if (split) dqa[j] = mfma32x32x16(a, dlo[f], dqa[j]);
           }
         }
       }
     }
-    if (it + 1 < ntiles) dq_store<D, HAS_MASK>(st, smem + ((it + 1) & 1) * L::kStageAligned, tid);
+    if (HAS_MASK && it + 1 < ntiles && tid < L::kBN) nxt[L::kOffValid + tid] = uint8_t(vbyte);
+    wait_vmem();
     __syncthreads();
   }
 
@@ -538,15 +484,29 @@ hipError_t launch_bwd_d(const BwdParams& p, bool has_mask, bool o_f32, hipStream
   const int64_t q_blocks = int64_t(p.n_pblocks) * p.n_hsub * p.Hkv * p.B;
   if (kv_blocks > 0x7fffffff || q_blocks > 0x7fffffff) return hipErrorInvalidValue;
   if (has_mask) {
-    hipLaunchKernelGGL((dkdv_kernel<D, true>), dim3(kv_blocks), dim3(kThreads), 0, stream, p);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((dq_kernel<D, true>), dim3(q_blocks), dim3(kThreads), 0, stream, p);
+    if (p.causal) {
+      hipLaunchKernelGGL((dkdv_kernel<D, true, true>), dim3(kv_blocks), dim3(kThreads), 0, stream, p);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((dq_kernel<D, true, true>), dim3(q_blocks), dim3(kThreads), 0, stream, p);
+    } else {
+      hipLaunchKernelGGL((dkdv_kernel<D, true, false>), dim3(kv_blocks), dim3(kThreads), 0, stream, p);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((dq_kernel<D, true, false>), dim3(q_blocks), dim3(kThreads), 0, stream, p);
+    }
   } else {
-    hipLaunchKernelGGL((dkdv_kernel<D, false>), dim3(kv_blocks), dim3(kThreads), 0, stream, p);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((dq_kernel<D, false>), dim3(q_blocks), dim3(kThreads), 0, stream, p);
+    if (p.causal) {
+      hipLaunchKernelGGL((dkdv_kernel<D, false, true>), dim3(kv_blocks), dim3(kThreads), 0, stream, p);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((dq_kernel<D, false, true>), dim3(q_blocks), dim3(kThreads), 0, stream, p);
+    } else {
+      hipLaunchKernelGGL((dkdv_kernel<D, false, false>), dim3(kv_blocks), dim3(kThreads), 0, stream, p);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((dq_kernel<D, false, false>), dim3(q_blocks), dim3(kThreads), 0, stream, p);
+    }
   }
   return hipGetLastError();
 }

@@ -15,7 +15,7 @@
 //    feeds 128 query rows with identical causal extents.
 //  * Scores are computed transposed, S^T = K Q^T (32 keys x 32 queries per
 //    32x32x16 bf16 MFMA), so each lane owns one query row: row max, row sum
-//    and the rescale of O stay in-lane (one swap between half-waves for the
+//    and the rescale of O stay in-lane (one half-wave exchange for the
 //    max).  O is accumulated transposed too, O^T += V^T P^T, with P^T used
 //    straight from the score registers as the B operand.
 //  * K and V tiles are stored row-major in LDS with XOR-swizzled 16-byte
@@ -117,14 +117,14 @@ __device__ __forceinline__ void stage_store(const Staging<D>& st, uint8_t* stage
 #pragma unroll
   for (int u = 0; u < L::kChunksPerThread; ++u) {
     const int c = tid + u * kThreads;
-    const int off = rm_off(c / L::kChunks, c % L::kChunks, L::kRowBytes);
+    const int off = rm_off<L::kRowBytes>(c / L::kChunks, c % L::kChunks);
     *reinterpret_cast<u32x4*>(stage + off) = st.kreg[u];
     *reinterpret_cast<u32x4*>(stage + L::kBytesK + off) = st.vreg[u];
   }
   if (HAS_MASK && tid < kBN) stage[L::kBytesK + L::kBytesV + tid] = uint8_t(st.vbyte);
 }
 
-template <int D, bool HAS_MASK, bool O_F32>
+template <int D, bool HAS_MASK, bool O_F32, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const FwdParams p) {
   using L = FwdLayout<D>;
   constexpr int KK = D / 16;     // contraction slices of the score product
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const FwdPar
   const int t = p0 + l32;                               // this lane's query row
   const int wave_last = min(p0 + 31, p.n - 1);
   const int wg_last = min(pb * p.pw + p.pw, p.n) - 1;
-  const int kend = p.causal ? wg_last + 1 : p.n;
+  const int kend = CAUSAL ? wg_last + 1 : p.n;
   const int ntiles = (kend + kBN - 1) / kBN;
   const bool wave_live = p0 < p.n;
 
@@ -185,19 +185,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const FwdPar
     if (it + 1 < ntiles) stage_load<D, HAS_MASK>(st, p, b, kvh, it + 1, tid);
 
     const int tile0 = it * kBN;
-    if (wave_live && !(p.causal && tile0 > wave_last)) {
+    if (wave_live && !(CAUSAL && tile0 > wave_last)) {
       const uint8_t* ks = cur;
       const uint8_t* vs = cur + L::kBytesK;
-      const bool act1 = !(p.causal && tile0 + 32 > wave_last);   // second half-tile has a visible key
+      const bool act1 = !(CAUSAL && tile0 + 32 > wave_last);   // second half-tile has a visible key
 
       // ---- S^T for the two 32-key halves
       f32x16 s0 = f32x16{}, s1 = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        const u32x4 a0 = *reinterpret_cast<const u32x4*>(ks + rm_off(l32, 2 * kk + hh, L::kRowBytes));
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(ks + rm_off<L::kRowBytes>(l32, 2 * kk + hh));
         s0 = mfma32x32x16(a0, qf[kk], s0);
         if (act1) {
-          const u32x4 a1 = *reinterpret_cast<const u32x4*>(ks + rm_off(32 + l32, 2 * kk + hh, L::kRowBytes));
+          const u32x4 a1 = *reinterpret_cast<const u32x4*>(ks + rm_off<L::kRowBytes>(32 + l32, 2 * kk + hh));
           s1 = mfma32x32x16(a1, qf[kk], s1);
         }
       }
@@ -209,14 +209,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const FwdPar
         x[i] = s0[i];
         x[16 + i] = act1 ? s1[i] : -INFINITY;
       }
-      const bool diag = p.causal && (tile0 + kBN - 1 > p0);
-      const bool tail = !HAS_MASK && (tile0 + kBN > p.n);
+      const bool diag = CAUSAL && (tile0 + kBN - 1 > p0);
+      const bool tail = !CAUSAL && (tile0 + kBN > p.n);
       if (diag || tail) {
+        // element i holds key tile0 + 4hh + C_i with C_i a compile-time constant;
+        // it is visible iff C_i <= lim.  Causal: key <= t (this also hides keys
+        // >= n, since t < n); otherwise only the tail limit key < n applies.
+        const int lim = (CAUSAL ? t : p.n - 1) - tile0 - 4 * hh;
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
-          const int key = tile0 + (i >> 4) * 32 + ((i & 15) >> 2) * 8 + hh * 4 + (i & 3);
-          const bool bad = (p.causal && key > t) || key >= p.n;
-          x[i] = bad ? -INFINITY : x[i];
+          const int ci = (i >> 4) * 32 + ((i & 15) >> 2) * 8 + (i & 3);
+          x[i] = (ci > lim) ? -INFINITY : x[i];
         }
       }
       if (HAS_MASK) {
@@ -234,7 +237,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const FwdPar
       float mr = x[0];
 #pragma unroll
       for (int i = 1; i < 32; ++i) mr = fmaxf(mr, x[i]);
-      mr = fmaxf(mr, swap_halves(mr));
+      mr = halves_max(mr);
       const float mx = mr * p.c;
       const bool raise = mx > m_ref + kRescaleSlack;
       if (__any(raise)) {
@@ -284,7 +287,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const FwdPar
 #pragma unroll
         for (int j = 0; j < DJ; ++j) {
           // V^T rows d = 32j + l%32, keys in the order of phi[f] (tile rows 16f + ...)
-          const u32x4 a = tr_operand(vs, L::kRowBytes, 16 * f, 32 * j, lane);
+          const u32x4 a = tr_operand<L::kRowBytes>(vs, 16 * f, 32 * j, lane);
           oacc[j] = mfma32x32x16(a, phi[f], oacc[j]);
           if (split) oacc[j] = mfma32x32x16(a, plo[f], oacc[j]);
         }
@@ -297,7 +300,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const FwdPar
 
   // ---- epilogue: normalise, write O (row t, dims 32j + 8*(i/4) + 4hh + i%4) and LSE
   if (t < p.n) {
-    const float ltot = lsum + swap_halves(lsum);
+    const float ltot = halves_sum(lsum);
     const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
     const int64_t obase = ((int64_t(b) * p.n + t) * p.Hq + head) * D;
 #pragma unroll
@@ -322,16 +325,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const FwdPar
   }
 }
 
-template <int D, bool HAS_MASK, bool O_F32>
+template <int D, bool HAS_MASK, bool O_F32, bool CAUSAL>
 hipError_t launch_fwd_t(const FwdParams& p, int blocks, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, HAS_MASK, O_F32>), dim3(blocks), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, HAS_MASK, O_F32, CAUSAL>), dim3(blocks), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
+}
+
+template <int D, bool HAS_MASK, bool O_F32>
+hipError_t dispatch_causal(const FwdParams& p, int blocks, hipStream_t stream) {
+  return p.causal ? launch_fwd_t<D, HAS_MASK, O_F32, true>(p, blocks, stream)
+                  : launch_fwd_t<D, HAS_MASK, O_F32, false>(p, blocks, stream);
 }
 
 template <int D>
 hipError_t dispatch_fwd(const FwdParams& p, int blocks, bool has_mask, bool o_f32, hipStream_t stream) {
-  if (has_mask) return o_f32 ? launch_fwd_t<D, true, true>(p, blocks, stream) : launch_fwd_t<D, true, false>(p, blocks, stream);
-  return o_f32 ? launch_fwd_t<D, false, true>(p, blocks, stream) : launch_fwd_t<D, false, false>(p, blocks, stream);
+  if (has_mask) return o_f32 ? dispatch_causal<D, true, true>(p, blocks, stream) : dispatch_causal<D, true, false>(p, blocks, stream);
+  return o_f32 ? dispatch_causal<D, false, true>(p, blocks, stream) : dispatch_causal<D, false, false>(p, blocks, stream);
 }
 
 }  // namespace

@@ -95,7 +95,7 @@ __global__ __launch_bounds__(kF32Threads) void attn_fwd_f32_kernel(const F32Para
       float part = 0.f;
 #pragma unroll
       for (int c = 0; c < DH; ++c) part = fmaf(qv[c], ks[j][hh * DH + c], part);
-      s[j] = part + swap_halves(part);
+      s[j] = halves_sum(part);
     }
     float mt = -INFINITY;
 #pragma unroll

@@ -37,9 +37,17 @@ __device__ __forceinline__ f32x16 mfma32x32x16(const u32x4 a, const u32x4 b, con
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// Exchange a value with the lane 32 positions away (the other half-wave).
-__device__ __forceinline__ float swap_halves(float x) {
-  return __shfl_xor(x, 32, 64);
+// Combine a value with the one held by the lane 32 positions away (the other
+// half-wave), without going through LDS: v_permlane32_swap returns the two
+// halves exchanged, so each lane sees {x[l], x[l ^ 32]} in its two results.
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Round-up division by an invariant 32-bit divisor (Granlund & Montgomery,
@@ -64,61 +72,29 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
   return uint32_t((t + n) >> f.s);
 }
 
-// ---- transposed operand tiles in LDS
-//
-// A lane holds its 32-slot share of scores (or probabilities / dS) for keys
-// (or query rows) (i/4)*8 + 4*(l/32) + i%4, i = 0..15 (the MFMA accumulator
-// row order).  To use them directly as an MFMA operand, the matching
-// transposed tile (V^T, K^T, Q^T or dO^T) stores element x of a 32-slice at
-// slot tslot(x): bits 2 and 3 swapped, so a lane's 8 values for a 16-wide
-// contraction slice sit in 8 consecutive slots.
-__device__ __forceinline__ int tslot(int x32) {
-  return (x32 & ~12) | ((x32 & 4) << 1) | ((x32 & 8) >> 1);
-}
-
-// Byte offset of 16-byte chunk `chunk` (0..7) of row r in a transposed tile
-// with 64 slots (128 B) per row.  Chunks are XOR-swizzled by row so that the
-// MFMA operand reads (8 consecutive rows, same chunk) and the transposing
-// staging writes (rows 8 apart) both spread over all banks.
-__device__ __forceinline__ int t64_off(int r, int chunk) {
-  const int swz = (r & 7) ^ ((r >> 3) & 7);
-  return r * 128 + ((chunk ^ swz) << 4);
-}
-
-// Same for a tile with 32 slots (64 B) per row, chunks 0..3.
-__device__ __forceinline__ int t32_off(int r, int chunk) {
-  const int swz = ((r >> 1) ^ (r >> 3)) & 3;
-  return r * 64 + ((chunk ^ swz) << 4);
-}
-
-// Transpose a 4-row x 8-column block of bf16 (rows[e] = 8 columns of row e)
-// into 8 column words of 4 rows each: out[c] = {row0[c] | row1[c] << 16,
-// row2[c] | row3[c] << 16}.
-__device__ __forceinline__ u32x2 transpose_col(const u32x4* rows, int c) {
-  const int w = c >> 1;
-  uint32_t x0, x1, x2, x3;
-  if (c & 1) {
-    x0 = rows[0][w] >> 16; x1 = rows[1][w] >> 16; x2 = rows[2][w] >> 16; x3 = rows[3][w] >> 16;
-  } else {
-    x0 = rows[0][w] & 0xffffu; x1 = rows[1][w] & 0xffffu; x2 = rows[2][w] & 0xffffu; x3 = rows[3][w] & 0xffffu;
-  }
-  return u32x2{x0 | (x1 << 16), x2 | (x3 << 16)};
-}
-
 // ---- row-major tiles with XOR-swizzled 16-byte chunks
 //
 // A tile row holds D bf16 (D/8 chunks of 16 bytes).  Chunk c of row r is
-// stored at physical chunk c ^ rm_swz(r) (low three bits only), where
-// rm_swz takes all 8 values on any 8 consecutive rows and the 4 values of one
-// parity on any 4 aligned rows.  Then
-//  * 16-byte row reads by 8 lanes on 8 consecutive rows (an MFMA operand whose
-//    rows are on the lanes) hit 8 distinct bank groups, and
-//  * transposing reads (ds_read_b64_tr_b16), where 16 lanes cover 4 aligned
-//    rows x 32 bytes, hit 8 distinct bank groups too.
-__device__ __forceinline__ int rm_swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+// stored at physical chunk c ^ rm_swz(r).  gfx950's LDS has 64 banks (256
+// bytes per pass); a 16-byte read is serviced 16 lanes per pass and an
+// 8-byte read 32 lanes per pass.  The swizzle makes every access pattern of
+// the kernels hit 64 distinct banks per pass:
+//  * 16-byte row reads, 16 lanes on 16 consecutive rows, same logical chunk
+//    (an MFMA operand whose rows are on the lanes);
+//  * transposing reads (ds_read_b64_tr_b16), 32 lanes on 4 aligned rows x 64
+//    bytes;
+//  * the staging writes, 16 lanes on consecutive chunks.
+// D = 128: rows are 256 bytes (one pass), all 4 chunk-index bits are
+// swizzled; D = 64: two 128-byte rows share a pass.
+template <int ROW_BYTES>
+__device__ __forceinline__ int rm_swz(int r) {
+  if (ROW_BYTES >= 256) return ((r & 3) << 2) | ((r >> 2) & 3);
+  return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
 
-__device__ __forceinline__ int rm_off(int r, int chunk, int row_bytes) {
-  return r * row_bytes + ((chunk ^ rm_swz(r)) << 4);
+template <int ROW_BYTES>
+__device__ __forceinline__ int rm_off(int r, int chunk) {
+  return r * ROW_BYTES + ((chunk ^ rm_swz<ROW_BYTES>(r)) << 4);
 }
 
 // gfx950 transposing LDS read.  Within each group of 16 lanes, lane i returns
@@ -139,14 +115,74 @@ __device__ __forceinline__ u32x2 ds_read_tr16_b64(const uint8_t* lds) {
 // i.e. exactly the row order in which a lane holds its share of an MFMA
 // accumulator column (rows (i/4)*8 + 4*(l/32) + i%4, i = 8k .. 8k+7).
 // r0 must be a multiple of 16 and col0 a multiple of 32.
-__device__ __forceinline__ u32x4 tr_operand(const uint8_t* tile, int row_bytes, int r0, int col0, int lane) {
+template <int ROW_BYTES>
+__device__ __forceinline__ u32x4 tr_operand(const uint8_t* tile, int r0, int col0, int lane) {
   const int hh = lane >> 5;
   const int r = r0 + 4 * hh + ((lane & 15) >> 2);
   const int col = col0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   const int sub = (col & 7) * 2;                    // byte offset inside the 16-byte chunk (0 or 8)
-  const u32x2 a = ds_read_tr16_b64(tile + rm_off(r, col >> 3, row_bytes) + sub);
-  const u32x2 b = ds_read_tr16_b64(tile + rm_off(r + 8, col >> 3, row_bytes) + sub);
+  const u32x2 a = ds_read_tr16_b64(tile + rm_off<ROW_BYTES>(r, col >> 3) + sub);
+  const u32x2 b = ds_read_tr16_b64(tile + rm_off<ROW_BYTES>(r + 8, col >> 3) + sub);
   return u32x4{a[0], a[1], b[0], b[1]};
+}
+
+// ---- direct global -> LDS staging (buffer loads with the LDS destination)
+//
+// One buffer_load ... lds instruction moves 16 bytes per lane from global
+// memory straight into LDS, lane l landing at (wave-uniform LDS base) + 16*l,
+// without passing through registers.  Offsets at or beyond the buffer
+// resource's byte size read as zero, which pads sequence tails for free.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint32_t* lds_u32_ptr;
+
+extern "C" __device__ void llvm_amdgcn_raw_buffer_load_lds(i32x4 rsrc, lds_u32_ptr lds, int size, int voffset,
+                                                          int soffset, int offset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+// Buffer resource for a raw byte range [base, base + bytes) (gfx9 layout:
+// 48-bit base, stride 0, byte size, default format word).
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = int(uint32_t(a));
+  r[1] = int(uint32_t(a >> 32) & 0xffffu);
+  r[2] = int(bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+__device__ __forceinline__ void dma16(const i32x4 rsrc, uint8_t* lds, int voffset) {
+  llvm_amdgcn_raw_buffer_load_lds(rsrc, (lds_u32_ptr)(lds), 16, voffset, 0, 0, 0);
+}
+
+__device__ __forceinline__ void dma4(const i32x4 rsrc, uint8_t* lds, int voffset) {
+  llvm_amdgcn_raw_buffer_load_lds(rsrc, (lds_u32_ptr)(lds), 4, voffset, 0, 0, 0);
+}
+
+// Wait until this wave's outstanding global loads (including the LDS DMA)
+// have landed.
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// DMA a ROWS x D bf16 tile, rows row0.. of a row-major tensor whose rows are
+// row_stride_bytes apart, into the swizzled LDS layout of rm_off.  `rows_ok`
+// rows hold data; the rest of the tile is zero-filled.  Every wave of the
+// workgroup calls this with its wave index; together they cover the tile.
+template <int D, int ROWS, int NWAVES>
+__device__ __forceinline__ void dma_tile(uint8_t* lds_tile, const uint16_t* row0, int row_stride_bytes, int rows_ok,
+                                         int wave, int lane) {
+  constexpr int NC = D / 8;                      // 16-byte chunks per row
+  constexpr int ROW_BYTES = 2 * D;
+  constexpr int PER_WAVE = ROWS * NC / (64 * NWAVES);
+  static_assert(ROWS * NC % (64 * NWAVES) == 0, "tile must split evenly across the waves");
+  const i32x4 rsrc = buffer_rsrc(row0, uint32_t(rows_ok > 0 ? rows_ok : 0) * uint32_t(row_stride_bytes));
+#pragma unroll
+  for (int u = 0; u < PER_WAVE; ++u) {
+    const int blk = u * NWAVES + wave;           // 1 KB block of the tile written by this instruction
+    const int pos = blk * 64 + lane;             // physical chunk position
+    const int r = pos / NC;
+    const int c = (pos % NC) ^ rm_swz<ROW_BYTES>(r);
+    dma16(rsrc, lds_tile + blk * 1024, r * row_stride_bytes + c * 16);
+  }
 }
 
 }  // namespace ulysses
