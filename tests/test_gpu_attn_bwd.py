@@ -25,16 +25,15 @@ from tests.gpu_helpers import say, bits_to_device, to_f64, to_host_f64, assert_c
 pytestmark = pytest.mark.gpu
 
 
-def _inputs(seed, n, Hq, Hkv, D, masked):
+def _inputs(seed, n, Hq, Hkv, D, masked, B=1):
     g = synth.streams(seed)
-    q = synth.normal_bf16(g[0], (1, n, Hq, D))
-    k = synth.normal_bf16(g[1], (1, n, Hkv, D))
-    v = synth.normal_bf16(g[2], (1, n, Hkv, D))
-    do = synth.normal_bf16(g[3], (1, n, Hq, D))
+    q = synth.normal_bf16(g[0], (B, n, Hq, D))
+    k = synth.normal_bf16(g[1], (B, n, Hkv, D))
+    v = synth.normal_bf16(g[2], (B, n, Hkv, D))
+    do = synth.normal_bf16(g[3], (B, n, Hq, D))
     valid = None
     if masked:
-        valid, _ = synth.document_valid(g[4], n, 4, max(1, n // 3))
-        valid = valid.reshape(1, n)
+        valid = np.stack([synth.document_valid(g[4], n, 4, max(1, n // 3))[0].reshape(n) for _ in range(B)])
     return q, k, v, do, valid
 
 
@@ -99,6 +98,20 @@ def test_bwd_small(n, Hq, Hkv, D, causal, masked, o_dtype):
         bq, bk = o_rounding_bound(to_f64(q), to_f64(k), to_f64(do), O, L, scale, causal, valid)
         assert_close("dQ", dq, dQ, 1e-2 + bq)
         assert_close("dK", dk, dK, 1e-2 + bk)
+    assert_close("dV", dv, dV, 1e-2)
+
+
+@pytest.mark.parametrize("n,causal,masked", [(300, True, True), (520, True, False), (200, False, False)])
+def test_bwd_batch2(n, causal, masked):
+    """Two sequences in one call (an odd and an even number of 128-key
+    blocks): each batch entry matches the oracle."""
+    say(f"bwd B=2 n={n} causal={causal} masked={masked}")
+    q, k, v, do, valid = _inputs(7 * n + 1, n, 8, 2, 128, masked, B=2)
+    scale = 128 ** -0.5
+    dQ, dK, dV, _, _ = oracle.attn_bwd(to_f64(q), to_f64(k), to_f64(v), to_f64(do), scale, causal, valid)
+    dq, dk, dv = _gpu_fwd_bwd(q, k, v, do, valid, scale, causal, torch.float32)
+    assert_close("dQ", dq, dQ, 1e-2)
+    assert_close("dK", dk, dK, 1e-2)
     assert_close("dV", dv, dV, 1e-2)
 
 

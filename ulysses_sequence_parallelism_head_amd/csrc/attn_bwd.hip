@@ -15,7 +15,9 @@
 //  1. rowdot: Dl[b][h][t] = dO . O per query row (float32 workspace).
 //  2. dkdv (KV-stationary): a workgroup of 4 waves owns 128 keys of one KV
 //     head (32 per wave, K and V held in registers) and streams the 64-row
-//     query tiles of every query head of the group that can see them.  It
+//     query tiles of every query head of the group that can see them (for
+//     causal attention, two key blocks in turn, ordered so that resident
+//     workgroups read the same tiles at the same time).  It
 //     computes S = Q K^T and dP = dO V^T with the key on the lane (so P and dS
 //     come out as MFMA B operands) and accumulates dV^T += dO^T P and
 //     dK^T += Q^T dS.  Q and dO are staged once, row-major with swizzled
@@ -30,6 +32,8 @@
 //     makes every gradient deterministic.
 // Rows below kSplitRows use a hi/lo bf16 split of P and dS (two MFMAs) for
 // accuracy where few keys carry large weights.
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -146,12 +150,82 @@ __device__ __forceinline__ u32x4 pack8_residual(const float* x, const u32x4 hi) 
   return pack8(r);
 }
 
+// One 32-row block of a staged query tile against this wave's 32 keys, after
+// S and dP are in registers: P, dS, then dV^T += dO^T P and dK^T += Q^T dS.
+// SPLIT adds the bf16 residuals of P and dS as second MFMAs.
+template <int D, bool CAUSAL, bool SPLIT>
+__device__ __forceinline__ void dkdv_rows(const uint8_t* qs, const uint8_t* dos, const float* lses, const float* dls,
+                                          const f32x16& s, const f32x16& dp, int rb, int t0, int u, bool key_ok,
+                                          int hh, int lane, float c, f32x16 (&dka)[D / 32], f32x16 (&dva)[D / 32]) {
+  using L = DkdvLayout<D>;
+  constexpr int DJ = D / 32;
+  float pr[16], ds[16];
+  // element i is query row t0 + 4hh + C_i (C_i = rb*32 + (i/4)*8 + i%4, a
+  // compile-time constant); the key is visible iff u <= row, i.e. C_i >= lim
+  const int lim = CAUSAL ? u - t0 - 4 * hh : -0x7fffffff;
+#pragma unroll
+  for (int g4 = 0; g4 < 4; ++g4) {
+    const int rr = rb * 32 + g4 * 8 + hh * 4;
+    const f32x4 l4 = *reinterpret_cast<const f32x4*>(lses + rr);
+    const f32x4 d4 = *reinterpret_cast<const f32x4*>(dls + rr);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = g4 * 4 + e;
+      const int ci = rb * 32 + g4 * 8 + e;
+      const bool ok = key_ok && ci >= lim;
+      // natural-log LSE -> base 2; a row with no visible key (LSE = -inf) gets
+      // exponent -inf, as does every invisible key: exp2(-inf) = 0 exactly
+      const float l2 = (l4[e] == -INFINITY) ? INFINITY : l4[e] * kLog2e;
+      const float x = ok ? fmaf(s[i], c, -l2) : -INFINITY;
+      const float pv = __builtin_amdgcn_exp2f(x);
+      pr[i] = pv;
+      ds[i] = pv * (dp[i] - d4[e]);
+    }
+  }
+  u32x4 ph[2], pl[2], dh[2], dl[2];
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    ph[f] = pack8(pr + 8 * f);
+    dh[f] = pack8(ds + 8 * f);
+    if (SPLIT) {
+      pl[f] = pack8_residual(pr + 8 * f, ph[f]);
+      dl[f] = pack8_residual(ds + 8 * f, dh[f]);
+    }
+  }
+  // dV^T += dO^T P,  dK^T += Q^T dS   (A operands read transposed from the row-major tiles)
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+#pragma unroll
+    for (int j = 0; j < DJ; ++j) {
+      const u32x4 adt = tr_operand<L::kRowBytes>(dos, rb * 32 + 16 * f, 32 * j, lane);
+      dva[j] = mfma32x32x16(adt, ph[f], dva[j]);
+      if (SPLIT) dva[j] = mfma32x32x16(adt, pl[f], dva[j]);
+      const u32x4 aqt = tr_operand<L::kRowBytes>(qs, rb * 32 + 16 * f, 32 * j, lane);
+      dka[j] = mfma32x32x16(aqt, dh[f], dka[j]);
+      if (SPLIT) dka[j] = mfma32x32x16(aqt, dl[f], dka[j]);
+    }
+  }
+}
+
+// Work items and tile order.  A work item is one key block (non-causal) or,
+// for causal attention, the pair of key blocks (nkb-1-w, w): the first one
+// sweeps the query tiles from the last down to its diagonal, the second from
+// its diagonal up to the last, so every pair does the same number of tiles.
+// Query heads of the group are the innermost loop.  With this order every
+// resident workgroup reads, at unit U, either tile ntq-1-U/g (first phase) or
+// tile U/g + 2nkb-2-ntq (second phase) of query head U%g: the workgroups of
+// one XCD share two tiles at a time, which the XCD's L2 keeps.
+// The two staging buffers are separate LDS objects and the loop is unrolled
+// by two, so every LDS read names its buffer statically and the compiler can
+// see that it never overlaps the DMA writing the other buffer.
 template <int D, bool HAS_MASK, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdParams p) {
   using L = DkdvLayout<D>;
   constexpr int KK = D / 16;
   constexpr int DJ = D / 32;
-  __shared__ __attribute__((aligned(128))) uint8_t smem[2 * L::kStageAligned];
+  constexpr int kKeys = 128;                      // keys per workgroup (4 waves x 32)
+  __shared__ __attribute__((aligned(128))) uint8_t stage0[L::kStageAligned];
+  __shared__ __attribute__((aligned(128))) uint8_t stage1[L::kStageAligned];
 
   const int tid = threadIdx.x;
   // wave index as a scalar: every branch that guards a matrix-core instruction
@@ -161,146 +235,116 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdParams p) {
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
-  // block -> (key block, kv head, batch); key block 0 (the longest) first
-  const int per_kb = p.Hkv * p.B;
-  const int kb = int(blockIdx.x) / per_kb;
-  const int rem = int(blockIdx.x) % per_kb;
+  // block -> (work item, kv head, batch); kv head varies fastest
+  const int per_w = p.Hkv * p.B;
+  const int w = int(blockIdx.x) / per_w;
+  const int rem = int(blockIdx.x) % per_w;
   const int b = rem / p.Hkv;
   const int kvh = rem % p.Hkv;
-  const int k0w = kb * 128 + wave * 32;          // first key of this wave
-  const int u = k0w + l32;                       // this lane's key
-  const bool wave_live = k0w < p.n;
+  const int ntq = (p.n + L::kRows - 1) / L::kRows;   // query tiles per head
+  const int nph = (CAUSAL && p.n_kblocks - 1 - w != w) ? 2 : 1;
 
-  // K and V rows of this lane's key as the B operands of S = Q K^T, dP = dO V^T
-  u32x4 kf[KK], vf[KK];
-  bool key_ok = u < p.n;
-  {
-    const int64_t off = ((int64_t(b) * p.n + (key_ok ? u : 0)) * p.Hkv + kvh) * D + 8 * hh;
+  for (int ph = 0; ph < nph; ++ph) {
+    const bool down = CAUSAL && ph == 0;
+    const int kb = down ? p.n_kblocks - 1 - w : w;
+    const int k0w = kb * kKeys + wave * 32;        // first key of this wave
+    const int u = k0w + l32;                       // this lane's key
+    const bool wave_live = k0w < p.n;
+
+    // K and V rows of this lane's key as the B operands of S = Q K^T, dP = dO V^T
+    u32x4 kf[KK], vf[KK];
+    bool key_ok = u < p.n;
+    {
+      const int64_t off = ((int64_t(b) * p.n + (key_ok ? u : 0)) * p.Hkv + kvh) * D + 8 * hh;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      kf[kk] = key_ok ? *reinterpret_cast<const u32x4*>(p.k + off + 16 * kk) : u32x4{0, 0, 0, 0};
-      vf[kk] = key_ok ? *reinterpret_cast<const u32x4*>(p.v + off + 16 * kk) : u32x4{0, 0, 0, 0};
-    }
-    if (HAS_MASK && key_ok) key_ok = p.valid[int64_t(b) * p.n + u] != 0;
-  }
-
-  f32x16 dka[DJ], dva[DJ];
-#pragma unroll
-  for (int j = 0; j < DJ; ++j) {
-    dka[j] = f32x16{};
-    dva[j] = f32x16{};
-  }
-
-  const int q_first = CAUSAL ? kb * 128 : 0;
-  const int ntq = (p.n - q_first + L::kRows - 1) / L::kRows;   // query tiles per head
-  const int niter = p.g * ntq;
-
-  if (niter > 0) dkdv_issue<D>(smem, p, b, kvh * p.g, q_first, wave, lane);
-  wait_vmem();
-  __syncthreads();
-
-  for (int it = 0; it < niter; ++it) {
-    uint8_t* cur = smem + (it & 1) * L::kStageAligned;
-    if (it + 1 < niter) {
-      const int nh = (it + 1) / ntq, nt = (it + 1) % ntq;
-      dkdv_issue<D>(smem + ((it + 1) & 1) * L::kStageAligned, p, b, kvh * p.g + nh, q_first + nt * L::kRows,
-                    wave, lane);
-    }
-    const int t0 = q_first + (it % ntq) * L::kRows;
-    if (wave_live) {
-      const uint8_t* qs = cur + L::kOffQ;
-      const uint8_t* dos = cur + L::kOffDO;
-      const float* lses = reinterpret_cast<const float*>(cur + L::kOffLSE);
-      const float* dls = reinterpret_cast<const float*>(cur + L::kOffDL);
-      // 32-row block rb sees this wave's keys only if its last row >= k0w
-      bool act[2];
-      f32x16 s[2], dp[2];
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        act[rb] = !(CAUSAL && t0 + rb * 32 + 31 < k0w);
-        s[rb] = f32x16{};
-        dp[rb] = f32x16{};
+      for (int kk = 0; kk < KK; ++kk) {
+        kf[kk] = key_ok ? *reinterpret_cast<const u32x4*>(p.k + off + 16 * kk) : u32x4{0, 0, 0, 0};
+        vf[kk] = key_ok ? *reinterpret_cast<const u32x4*>(p.v + off + 16 * kk) : u32x4{0, 0, 0, 0};
       }
-      // S[q][key] and dP[q][key] for both row blocks: lane = key, rows q = (i/4)*8 + 4hh + i%4
+      if (HAS_MASK && key_ok) key_ok = p.valid[int64_t(b) * p.n + u] != 0;
+    }
+
+    f32x16 dka[DJ], dva[DJ];
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        if (!act[rb]) continue;
+    for (int j = 0; j < DJ; ++j) {
+      dka[j] = f32x16{};
+      dva[j] = f32x16{};
+    }
+
+    // query tiles tfirst .. ntq-1 hold every row that can see the block's keys
+    const int tfirst = CAUSAL ? (kb * kKeys) / L::kRows : 0;
+    const int niter = (ntq - tfirst) * p.g;
+    // unit it -> (tile, head of the group)
+    auto tile_of = [&](int it) { return down ? ntq - 1 - it / p.g : tfirst + it / p.g; };
+
+    // one unit: prefetch unit it+1 into `nxt`, compute on `cur`, then wait for
+    // the prefetch and synchronise (both buffers are free again afterwards)
+    auto unit = [&](uint8_t* cur, uint8_t* nxt, int it) {
+      if (it + 1 < niter)
+        dkdv_issue<D>(nxt, p, b, kvh * p.g + (it + 1) % p.g, tile_of(it + 1) * L::kRows, wave, lane);
+      const int t0 = tile_of(it) * L::kRows;
+      if (wave_live) {
+        const uint8_t* qs = cur + L::kOffQ;
+        const uint8_t* dos = cur + L::kOffDO;
+        const float* lses = reinterpret_cast<const float*>(cur + L::kOffLSE);
+        const float* dls = reinterpret_cast<const float*>(cur + L::kOffDL);
+        // 32-row block rb sees this wave's keys only if its last row >= k0w
+        bool act[2];
+        f32x16 s[2], dp[2];
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          const int off = rm_off<L::kRowBytes>(rb * 32 + l32, 2 * kk + hh);
-          s[rb] = mfma32x32x16(*reinterpret_cast<const u32x4*>(qs + off), kf[kk], s[rb]);
-          dp[rb] = mfma32x32x16(*reinterpret_cast<const u32x4*>(dos + off), vf[kk], dp[rb]);
+        for (int rb = 0; rb < 2; ++rb) {
+          act[rb] = !(CAUSAL && t0 + rb * 32 + 31 < k0w);
+          s[rb] = f32x16{};
+          dp[rb] = f32x16{};
         }
-      }
+        // S[q][key] and dP[q][key] for both row blocks: lane = key, rows q = (i/4)*8 + 4hh + i%4
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        if (!act[rb]) continue;
-        const int r0 = t0 + rb * 32;
-        const bool split = r0 < kSplitRows;
-        float pr[16], ds[16];
-        // element i is query row t0 + 4hh + C_i (C_i = rb*32 + (i/4)*8 + i%4, a
-        // compile-time constant); the key is visible iff u <= row, i.e. C_i >= lim
-        const int lim = CAUSAL ? u - t0 - 4 * hh : -0x7fffffff;
+        for (int rb = 0; rb < 2; ++rb) {
+          if (!act[rb]) continue;
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int rr = rb * 32 + g4 * 8 + hh * 4;
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lses + rr);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dls + rr);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = g4 * 4 + e;
-            const int ci = rb * 32 + g4 * 8 + e;
-            const bool ok = key_ok && ci >= lim;
-            // natural-log LSE -> base 2; a row with no visible key (LSE = -inf) contributes nothing
-            const float l2 = (l4[e] == -INFINITY) ? INFINITY : l4[e] * kLog2e;
-            const float pv = ok ? __builtin_amdgcn_exp2f(fmaf(s[rb][i], p.c, -l2)) : 0.f;
-            pr[i] = pv;
-            ds[i] = pv * (dp[rb][i] - d4[e]);
+          for (int kk = 0; kk < KK; ++kk) {
+            const int off = rm_off<L::kRowBytes>(rb * 32 + l32, 2 * kk + hh);
+            s[rb] = mfma32x32x16(*reinterpret_cast<const u32x4*>(qs + off), kf[kk], s[rb]);
+            dp[rb] = mfma32x32x16(*reinterpret_cast<const u32x4*>(dos + off), vf[kk], dp[rb]);
           }
         }
-        u32x4 ph[2], pl[2], dh[2], dl[2];
 #pragma unroll
-        for (int f = 0; f < 2; ++f) {
-          ph[f] = pack8(pr + 8 * f);
-          dh[f] = pack8(ds + 8 * f);
-          if (split) {
-            pl[f] = pack8_residual(pr + 8 * f, ph[f]);
-            dl[f] = pack8_residual(ds + 8 * f, dh[f]);
-          }
-        }
-        // dV^T += dO^T P,  dK^T += Q^T dS   (A operands read transposed from the row-major tiles)
-#pragma unroll
-        for (int f = 0; f < 2; ++f) {
-#pragma unroll
-          for (int j = 0; j < DJ; ++j) {
-            const u32x4 adt = tr_operand<L::kRowBytes>(dos, rb * 32 + 16 * f, 32 * j, lane);
-            dva[j] = mfma32x32x16(adt, ph[f], dva[j]);
-            if (split) dva[j] = mfma32x32x16(adt, pl[f], dva[j]);
-            const u32x4 aqt = tr_operand<L::kRowBytes>(qs, rb * 32 + 16 * f, 32 * j, lane);
-            dka[j] = mfma32x32x16(aqt, dh[f], dka[j]);
-            if (split) dka[j] = mfma32x32x16(aqt, dl[f], dka[j]);
-          }
+        for (int rb = 0; rb < 2; ++rb) {
+          if (!act[rb]) continue;
+          if (t0 + rb * 32 < kSplitRows)
+            dkdv_rows<D, CAUSAL, true>(qs, dos, lses, dls, s[rb], dp[rb], rb, t0, u, key_ok, hh, lane, p.c, dka, dva);
+          else
+            dkdv_rows<D, CAUSAL, false>(qs, dos, lses, dls, s[rb], dp[rb], rb, t0, u, key_ok, hh, lane, p.c, dka,
+                                        dva);
         }
       }
-    }
+      wait_vmem();
+      __syncthreads();
+    };
+
+    if (niter > 0) dkdv_issue<D>(stage0, p, b, kvh * p.g, tile_of(0) * L::kRows, wave, lane);
     wait_vmem();
     __syncthreads();
-  }
+    for (int it = 0; it < niter; it += 2) {
+      unit(stage0, stage1, it);
+      if (it + 1 < niter) unit(stage1, stage0, it + 1);
+    }
 
-  // write dK = scale * dK^T^T and dV: lane = key u, dims 32j + 8*(i/4) + 4hh + i%4
-  if (u < p.n) {
-    const int64_t base = ((int64_t(b) * p.n + u) * p.Hkv + kvh) * D;
+    // write dK = scale * dK^T^T and dV: lane = key u, dims 32j + 8*(i/4) + 4hh + i%4
+    if (u < p.n) {
+      const int64_t base = ((int64_t(b) * p.n + u) * p.Hkv + kvh) * D;
 #pragma unroll
-    for (int j = 0; j < DJ; ++j)
+      for (int j = 0; j < DJ; ++j)
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int d0 = j * 32 + i4 * 8 + hh * 4;
-        *reinterpret_cast<f32x4*>(p.dk + base + d0) =
-            f32x4{dka[j][i4 * 4] * p.scale, dka[j][i4 * 4 + 1] * p.scale, dka[j][i4 * 4 + 2] * p.scale,
-                  dka[j][i4 * 4 + 3] * p.scale};
-        *reinterpret_cast<f32x4*>(p.dv + base + d0) =
-            f32x4{dva[j][i4 * 4], dva[j][i4 * 4 + 1], dva[j][i4 * 4 + 2], dva[j][i4 * 4 + 3]};
-      }
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int d0 = j * 32 + i4 * 8 + hh * 4;
+          *reinterpret_cast<f32x4*>(p.dk + base + d0) =
+              f32x4{dka[j][i4 * 4] * p.scale, dka[j][i4 * 4 + 1] * p.scale, dka[j][i4 * 4 + 2] * p.scale,
+                    dka[j][i4 * 4 + 3] * p.scale};
+          *reinterpret_cast<f32x4*>(p.dv + base + d0) =
+              f32x4{dva[j][i4 * 4], dva[j][i4 * 4 + 1], dva[j][i4 * 4 + 2], dva[j][i4 * 4 + 3]};
+        }
+    }
   }
 }
 
@@ -334,12 +378,69 @@ __device__ __forceinline__ void dq_issue(uint8_t* stage, uint32_t& vbyte, const 
   }
 }
 
+// One 32-key half of a staged K/V tile against this wave's 32 query rows:
+// S^T and dP^T, dS^T, then dQ^T += K^T dS^T.  `lim`: key row C of the half is
+// visible iff C <= lim (and its valid byte is set when HAS_MASK).  SPLIT adds
+// the bf16 residual of dS as second MFMAs.
+template <int D, bool HAS_MASK, bool SPLIT>
+__device__ __forceinline__ void dq_half(const uint8_t* ks, const uint8_t* vs, const uint8_t* vb, int half, int lim,
+                                        const u32x4 (&qf)[D / 16], const u32x4 (&df)[D / 16], float lse2, float dl,
+                                        float c, int l32, int hh, int lane, f32x16 (&dqa)[D / 32]) {
+  using L = DqLayout<D>;
+  constexpr int KK = D / 16;
+  constexpr int DJ = D / 32;
+  // S^T[key][q] and dP^T[key][q]: lane = query row, rows key = (i/4)*8 + 4hh + i%4
+  f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    const int off = rm_off<L::kRowBytes>(half * 32 + l32, 2 * kk + hh);
+    s = mfma32x32x16(*reinterpret_cast<const u32x4*>(ks + off), qf[kk], s);
+    dp = mfma32x32x16(*reinterpret_cast<const u32x4*>(vs + off), df[kk], dp);
+  }
+  float ds[16];
+  // element i is key row C_i = (i/4)*8 + i%4 of the half (plus 4hh)
+#pragma unroll
+  for (int g4 = 0; g4 < 4; ++g4) {
+    uint32_t vw = 0xffffffffu;
+    if (HAS_MASK) vw = *reinterpret_cast<const uint32_t*>(vb + half * 32 + g4 * 8 + hh * 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = g4 * 4 + e;
+      const int ci = g4 * 8 + e;
+      const bool ok = ci <= lim && (!HAS_MASK || ((vw >> (8 * e)) & 0xffu));
+      // invisible keys (and rows with no visible key: lse2 = +inf) get exponent -inf
+      const float x = ok ? fmaf(s[i], c, -lse2) : -INFINITY;
+      ds[i] = __builtin_amdgcn_exp2f(x) * (dp[i] - dl);
+    }
+  }
+  u32x4 dh[2], dlo[2];
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    dh[f] = pack8(ds + 8 * f);
+    if (SPLIT) dlo[f] = pack8_residual(ds + 8 * f, dh[f]);
+  }
+  // dQ^T += K^T dS^T  (K^T read transposed from the row-major K tile)
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+#pragma unroll
+    for (int j = 0; j < DJ; ++j) {
+      const u32x4 a = tr_operand<L::kRowBytes>(ks, half * 32 + 16 * f, 32 * j, lane);
+      dqa[j] = mfma32x32x16(a, dh[f], dqa[j]);
+      if (SPLIT) dqa[j] = mfma32x32x16(a, dlo[f], dqa[j]);
+    }
+  }
+}
+
+// The two staging buffers are separate LDS objects and the tile loop is
+// unrolled by two, so the compiler sees that LDS reads of one buffer never
+// overlap the DMA filling the other.
 template <int D, bool HAS_MASK, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const BwdParams p) {
   using L = DqLayout<D>;
   constexpr int KK = D / 16;
   constexpr int DJ = D / 32;
-  __shared__ __attribute__((aligned(128))) uint8_t smem[2 * L::kStageAligned];
+  __shared__ __attribute__((aligned(128))) uint8_t stage0[L::kStageAligned];
+  __shared__ __attribute__((aligned(128))) uint8_t stage1[L::kStageAligned];
 
   const int tid = threadIdx.x;
   // wave index as a scalar: every branch that guards a matrix-core instruction
@@ -364,7 +465,6 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const BwdParams p) {
   const int kend = CAUSAL ? wg_last + 1 : p.n;
   const int ntiles = (kend + L::kBN - 1) / L::kBN;
   const bool wave_live = p0 < p.n;
-  const bool split = p0 < kSplitRows;
 
   u32x4 qf[KK], df[KK];
   float lse2 = INFINITY, dl = 0.f;
@@ -383,91 +483,63 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const BwdParams p) {
     }
   }
 
-  f32x16 dqa[DJ];
+  // rows below kSplitRows take the hi/lo path; the choice is made once per
+  // workgroup (its first row) so the common path carries no residuals
+  auto run = [&](auto split_tag) {
+    constexpr bool SPLIT = decltype(split_tag)::value;
+    f32x16 dqa[DJ];
 #pragma unroll
-  for (int j = 0; j < DJ; ++j) dqa[j] = f32x16{};
+    for (int j = 0; j < DJ; ++j) dqa[j] = f32x16{};
 
-  uint32_t vbyte = 0;
-  dq_issue<D, HAS_MASK>(smem, vbyte, p, b, kvh, 0, wave, lane, tid);
-  if (HAS_MASK && tid < L::kBN) smem[L::kOffValid + tid] = uint8_t(vbyte);
-  wait_vmem();
-  __syncthreads();
-
-  for (int it = 0; it < ntiles; ++it) {
-    uint8_t* cur = smem + (it & 1) * L::kStageAligned;
-    uint8_t* nxt = smem + ((it + 1) & 1) * L::kStageAligned;
-    if (it + 1 < ntiles) dq_issue<D, HAS_MASK>(nxt, vbyte, p, b, kvh, it + 1, wave, lane, tid);   // in flight during the math
-
-    const int tile0 = it * L::kBN;
-    if (wave_live && !(CAUSAL && tile0 > wave_last)) {
-      const uint8_t* ks = cur + L::kOffK;
-      const uint8_t* vs = cur + L::kOffV;
-      const uint8_t* vb = cur + L::kOffValid;
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int key0 = tile0 + half * 32;
-        if (CAUSAL && key0 > wave_last) break;
-        // S^T[key][q] and dP^T[key][q]: lane = query row t, rows key = (i/4)*8 + 4hh + i%4
-        f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          const int off = rm_off<L::kRowBytes>(half * 32 + l32, 2 * kk + hh);
-          s = mfma32x32x16(*reinterpret_cast<const u32x4*>(ks + off), qf[kk], s);
-          dp = mfma32x32x16(*reinterpret_cast<const u32x4*>(vs + off), df[kk], dp);
-        }
-        float ds[16];
-        // element i is key key0 + 4hh + C_i (C_i = (i/4)*8 + i%4, a compile-time
-        // constant); visible iff C_i <= lim (key < n, and key <= t if causal)
-        int lim = p.n - 1 - key0 - 4 * hh;
-        if (CAUSAL) lim = min(lim, t - key0 - 4 * hh);
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          uint32_t vw = 0xffffffffu;
-          if (HAS_MASK) vw = *reinterpret_cast<const uint32_t*>(vb + half * 32 + g4 * 8 + hh * 4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = g4 * 4 + e;
-            const int ci = g4 * 8 + e;
-            const bool ok = ci <= lim && (!HAS_MASK || ((vw >> (8 * e)) & 0xffu));
-            const float pv = ok ? __builtin_amdgcn_exp2f(fmaf(s[i], p.c, -lse2)) : 0.f;
-            ds[i] = pv * (dp[i] - dl);
-          }
-        }
-        u32x4 dh[2], dlo[2];
-#pragma unroll
-        for (int f = 0; f < 2; ++f) {
-          dh[f] = pack8(ds + 8 * f);
-          if (split) dlo[f] = pack8_residual(ds + 8 * f, dh[f]);
-        }
-        // dQ^T += K^T dS^T  (K^T read transposed from the row-major K tile)
-#pragma unroll
-        for (int f = 0; f < 2; ++f) {
-#pragma unroll
-          for (int j = 0; j < DJ; ++j) {
-            const u32x4 a = tr_operand<L::kRowBytes>(ks, half * 32 + 16 * f, 32 * j, lane);
-            dqa[j] = mfma32x32x16(a, dh[f], dqa[j]);
-            if (split) dqa[j] = mfma32x32x16(a, dlo[f], dqa[j]);
-          }
-        }
-      }
-    }
-    if (HAS_MASK && it + 1 < ntiles && tid < L::kBN) nxt[L::kOffValid + tid] = uint8_t(vbyte);
+    uint32_t vbyte = 0;
+    dq_issue<D, HAS_MASK>(stage0, vbyte, p, b, kvh, 0, wave, lane, tid);
+    if (HAS_MASK && tid < L::kBN) stage0[L::kOffValid + tid] = uint8_t(vbyte);
     wait_vmem();
     __syncthreads();
-  }
 
-  if (t < p.n) {
-    const int64_t base = ((int64_t(b) * p.n + t) * p.Hq + head) * D;
+    // one tile: prefetch tile it+1 into `nxt`, compute on `cur`, then wait for
+    // the prefetch and synchronise
+    auto unit = [&](uint8_t* cur, uint8_t* nxt, int it) {
+      if (it + 1 < ntiles) dq_issue<D, HAS_MASK>(nxt, vbyte, p, b, kvh, it + 1, wave, lane, tid);
+      const int tile0 = it * L::kBN;
+      if (wave_live && !(CAUSAL && tile0 > wave_last)) {
+        const uint8_t* ks = cur + L::kOffK;
+        const uint8_t* vs = cur + L::kOffV;
+        const uint8_t* vb = cur + L::kOffValid;
 #pragma unroll
-    for (int j = 0; j < DJ; ++j)
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int d0 = j * 32 + i4 * 8 + hh * 4;
-        *reinterpret_cast<f32x4*>(p.dq + base + d0) =
-            f32x4{dqa[j][i4 * 4] * p.scale, dqa[j][i4 * 4 + 1] * p.scale, dqa[j][i4 * 4 + 2] * p.scale,
-                  dqa[j][i4 * 4 + 3] * p.scale};
+        for (int half = 0; half < 2; ++half) {
+          const int key0 = tile0 + half * 32;
+          if (CAUSAL && key0 > wave_last) break;
+          // visible iff key < n, and key <= t if causal
+          int lim = p.n - 1 - key0 - 4 * hh;
+          if (CAUSAL) lim = min(lim, t - key0 - 4 * hh);
+          dq_half<D, HAS_MASK, SPLIT>(ks, vs, vb, half, lim, qf, df, lse2, dl, p.c, l32, hh, lane, dqa);
+        }
       }
-  }
+      if (HAS_MASK && it + 1 < ntiles && tid < L::kBN) nxt[L::kOffValid + tid] = uint8_t(vbyte);
+      wait_vmem();
+      __syncthreads();
+    };
+    for (int it = 0; it < ntiles; it += 2) {
+      unit(stage0, stage1, it);
+      if (it + 1 < ntiles) unit(stage1, stage0, it + 1);
+    }
+
+    if (t < p.n) {
+      const int64_t base = ((int64_t(b) * p.n + t) * p.Hq + head) * D;
+#pragma unroll
+      for (int j = 0; j < DJ; ++j)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int d0 = j * 32 + i4 * 8 + hh * 4;
+          *reinterpret_cast<f32x4*>(p.dq + base + d0) =
+              f32x4{dqa[j][i4 * 4] * p.scale, dqa[j][i4 * 4 + 1] * p.scale, dqa[j][i4 * 4 + 2] * p.scale,
+                    dqa[j][i4 * 4 + 3] * p.scale};
+        }
+    }
+  };
+  if (pb * p.pw < kSplitRows) run(std::true_type{});
+  else run(std::false_type{});
 }
 
 template <int D>
@@ -480,7 +552,9 @@ hipError_t launch_bwd_d(const BwdParams& p, bool has_mask, bool o_f32, hipStream
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  const int64_t kv_blocks = int64_t(p.n_kblocks) * p.Hkv * p.B;
+  // causal: one workgroup per pair of key blocks (nkb-1-w, w)
+  const int64_t kv_work = p.causal ? (int64_t(p.n_kblocks) + 1) / 2 : p.n_kblocks;
+  const int64_t kv_blocks = kv_work * p.Hkv * p.B;
   const int64_t q_blocks = int64_t(p.n_pblocks) * p.n_hsub * p.Hkv * p.B;
   if (kv_blocks > 0x7fffffff || q_blocks > 0x7fffffff) return hipErrorInvalidValue;
   if (has_mask) {

@@ -10,10 +10,12 @@
 //   seq2head:  dst[j][b][i][s][r] = src[i][b][s][j][r]
 //   head2seq:  dst[i][b][s][j][r] = src[j][b][i][s][r]
 // (i = sequence shard, j = head block, s = token within the shard).
-// The grid walks the destination linearly in vectors of VB bytes (16 when R,
-// and both pointers, allow it): every wave writes whole coalesced lines, and
-// each run is read contiguously too.  Streaming loads/stores are marked
-// non-temporal: nothing is reused.
+// The grid walks the sequence-sharded side linearly (the source of seq2head,
+// the destination of head2seq) in vectors of 16 bytes when the run size and
+// both pointers allow it.  That side is then one contiguous stream and the
+// head-sharded side is P sequential streams (one per head block), each
+// advancing one run at a time: both sides stay DRAM-page friendly.
+// Streaming loads/stores are marked non-temporal: nothing is reused.
 #include "device_common.h"
 #include "internal.h"
 
@@ -28,44 +30,35 @@ template <typename V>
 __global__ __launch_bounds__(kRepackThreads) void repack_kernel(const V* __restrict__ src, V* __restrict__ dst,
                                                                uint32_t total_vecs, FastDiv fd_rv, FastDiv fd_nl,
                                                                FastDiv fd_P, FastDiv fd_B, int seq2head) {
-  // total_vecs < 2^32 and every run index < 2^32 are checked on the host
+  // total_vecs < 2^32 and every run index < 2^32 are checked on the host.
+  // Linear index o walks the sequence-sharded layout [i][b][s][j][r]; its run
+  // ((i*B + b)*nl + s)*P + j maps to the head-sharded run ((j*B + b)*P + i)*nl + s.
   const uint32_t Rv = fd_rv.d, nl = fd_nl.d, P = fd_P.d, B = fd_B.d;
   const uint64_t base = uint64_t(blockIdx.x) * (kRepackThreads * kRepackUnroll) + threadIdx.x;
   V val[kRepackUnroll];
+  uint64_t hidx[kRepackUnroll];
 #pragma unroll
   for (int u = 0; u < kRepackUnroll; ++u) {
     const uint64_t o64 = base + uint64_t(u) * kRepackThreads;
+    hidx[u] = 0;
     if (o64 < total_vecs) {
       const uint32_t o = uint32_t(o64);
       const uint32_t run = fdiv(o, fd_rv);
       const uint32_t e = o - run * Rv;
-      uint32_t src_run;
-      if (seq2head) {
-        // destination run = ((j*B + b)*P + i)*nl + s  ->  source ((i*B + b)*nl + s)*P + j
-        const uint32_t q1 = fdiv(run, fd_nl);
-        const uint32_t s = run - q1 * nl;
-        const uint32_t q2 = fdiv(q1, fd_P);
-        const uint32_t i = q1 - q2 * P;
-        const uint32_t j = fdiv(q2, fd_B);
-        const uint32_t b = q2 - j * B;
-        src_run = ((i * B + b) * nl + s) * P + j;
-      } else {
-        // destination run = ((i*B + b)*nl + s)*P + j  ->  source ((j*B + b)*P + i)*nl + s
-        const uint32_t q1 = fdiv(run, fd_P);
-        const uint32_t j = run - q1 * P;
-        const uint32_t q2 = fdiv(q1, fd_nl);
-        const uint32_t s = q1 - q2 * nl;
-        const uint32_t i = fdiv(q2, fd_B);
-        const uint32_t b = q2 - i * B;
-        src_run = ((j * B + b) * P + i) * nl + s;
-      }
-      val[u] = __builtin_nontemporal_load(src + (uint64_t(src_run) * Rv + e));
+      const uint32_t q1 = fdiv(run, fd_P);
+      const uint32_t j = run - q1 * P;
+      const uint32_t q2 = fdiv(q1, fd_nl);
+      const uint32_t s = q1 - q2 * nl;
+      const uint32_t i = fdiv(q2, fd_B);
+      const uint32_t b = q2 - i * B;
+      hidx[u] = uint64_t(((j * B + b) * P + i) * nl + s) * Rv + e;
+      val[u] = __builtin_nontemporal_load(src + (seq2head ? o64 : hidx[u]));
     }
   }
 #pragma unroll
   for (int u = 0; u < kRepackUnroll; ++u) {
     const uint64_t o64 = base + uint64_t(u) * kRepackThreads;
-    if (o64 < total_vecs) __builtin_nontemporal_store(val[u], dst + o64);
+    if (o64 < total_vecs) __builtin_nontemporal_store(val[u], dst + (seq2head ? hidx[u] : o64));
   }
 }
 
