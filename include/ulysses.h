@@ -164,8 +164,9 @@ ULYSSES_API ulysses_status_t ulysses_attn_fwd(const void* q, const void* k, cons
                                   void* stream);
 
 /*
- * Bytes of device workspace ulysses_attn_bwd needs for this problem
- * (the per-row dot products dO.O, float32 [B][Hq][n], rounded up to 256 B).
+ * Bytes of device workspace ulysses_attn_bwd needs for this problem: two
+ * float32 [B][Hq][n] arrays (the per-row dot products dO.O, and the
+ * logsumexp in base 2), each rounded up to 256 B.
  */
 ULYSSES_API size_t ulysses_attn_bwd_workspace_bytes(int32_t B, int64_t n, int32_t Hq, int32_t Hkv, int32_t D);
 

@@ -114,7 +114,7 @@ def _bwd(lib, ws=ctypes.c_void_p(0x9000000), wsb=1 << 20, dq=ctypes.c_void_p(0x6
 
 def test_bwd_validation(lib):
     need = lib.ulysses_attn_bwd_workspace_bytes(1, 64, 8, 2, 128)
-    assert need == 64 * 8 * 4 and need % 256 == 0
+    assert need == 2 * 64 * 8 * 4 and need % 256 == 0
     assert lib.ulysses_attn_bwd_workspace_bytes(0, 64, 8, 2, 128) == 0
     assert _bwd(lib, wsb=need - 1) == INVALID
     assert _bwd(lib, ws=None) == INVALID

@@ -57,7 +57,8 @@ struct BwdParams {
   float* dq;
   float* dk;
   float* dv;
-  float* rowdot;      // [B][Hq][n]
+  float* rowdot;      // [B][Hq][n] dO . O (workspace)
+  float* lse2;        // [B][Hq][n] lse * log2(e), +inf for empty rows (workspace)
   int32_t B, n, Hq, Hkv, g;
   float scale;
   float c;            // scale * log2(e)
@@ -69,6 +70,7 @@ struct BwdParams {
 };
 
 // ------------------------------------------------------------------ rowdot
+// Dl = dO . O per query row, and the base-2 logsumexp, into the workspace.
 template <int D, bool O_F32>
 __global__ __launch_bounds__(256) void rowdot_kernel(const BwdParams p) {
   // 16 lanes per row, D/16 elements each
@@ -98,7 +100,12 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const BwdParams p) {
     const int64_t bt = row / p.Hq;
     const int64_t t = bt % p.n;
     const int64_t b = bt / p.n;
-    p.rowdot[(b * p.Hq + h) * p.n + t] = acc;
+    const int64_t idx = (b * p.Hq + h) * p.n + t;
+    p.rowdot[idx] = acc;
+    // base-2 logsumexp for the exponentials of the dK/dV pass; a row with no
+    // visible key (lse = -inf) gets +inf so that every exponent is -inf
+    const float l = p.lse[idx];
+    p.lse2[idx] = (l == -INFINITY) ? INFINITY : l * kLog2e;
   }
 }
 
@@ -118,7 +125,7 @@ struct DkdvLayout {
 };
 
 // DMA the query tile t0 .. t0+63 of query head `head`: Q and dO rows into the
-// swizzled row-major tiles, the raw logsumexp and Dl values into two float
+// swizzled row-major tiles, the base-2 logsumexp and Dl values into two float
 // arrays (rows past n read as zero).
 template <int D>
 __device__ __forceinline__ void dkdv_issue(uint8_t* stage, const BwdParams& p, int b, int head, int t0, int wave,
@@ -130,7 +137,7 @@ __device__ __forceinline__ void dkdv_issue(uint8_t* stage, const BwdParams& p, i
   dma_tile<D, L::kRows, kWaves>(stage + L::kOffQ, p.q + off, stride, rows_ok, wave, lane);
   dma_tile<D, L::kRows, kWaves>(stage + L::kOffDO, p.dout + off, stride, rows_ok, wave, lane);
   const int64_t roff = (int64_t(b) * p.Hq + head) * p.n + t0;
-  if (wave == 0) dma4(buffer_rsrc(p.lse + roff, uint32_t(rows_ok) * 4u), stage + L::kOffLSE, lane * 4);
+  if (wave == 0) dma4(buffer_rsrc(p.lse2 + roff, uint32_t(rows_ok) * 4u), stage + L::kOffLSE, lane * 4);
   if (wave == 1) dma4(buffer_rsrc(p.rowdot + roff, uint32_t(rows_ok) * 4u), stage + L::kOffDL, lane * 4);
 }
 
@@ -173,10 +180,9 @@ __device__ __forceinline__ void dkdv_rows(const uint8_t* qs, const uint8_t* dos,
       const int i = g4 * 4 + e;
       const int ci = rb * 32 + g4 * 8 + e;
       const bool ok = key_ok && ci >= lim;
-      // natural-log LSE -> base 2; a row with no visible key (LSE = -inf) gets
-      // exponent -inf, as does every invisible key: exp2(-inf) = 0 exactly
-      const float l2 = (l4[e] == -INFINITY) ? INFINITY : l4[e] * kLog2e;
-      const float x = ok ? fmaf(s[i], c, -l2) : -INFINITY;
+      // invisible keys, and rows with no visible key (base-2 LSE = +inf), get
+      // exponent -inf: exp2(-inf) = 0 exactly
+      const float x = ok ? fmaf(s[i], c, -l4[e]) : -INFINITY;
       const float pv = __builtin_amdgcn_exp2f(x);
       pr[i] = pv;
       ds[i] = pv * (dp[i] - d4[e]);
@@ -215,17 +221,13 @@ __device__ __forceinline__ void dkdv_rows(const uint8_t* qs, const uint8_t* dos,
 // resident workgroup reads, at unit U, either tile ntq-1-U/g (first phase) or
 // tile U/g + 2nkb-2-ntq (second phase) of query head U%g: the workgroups of
 // one XCD share two tiles at a time, which the XCD's L2 keeps.
-// The two staging buffers are separate LDS objects and the loop is unrolled
-// by two, so every LDS read names its buffer statically and the compiler can
-// see that it never overlaps the DMA writing the other buffer.
 template <int D, bool HAS_MASK, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdParams p) {
   using L = DkdvLayout<D>;
   constexpr int KK = D / 16;
   constexpr int DJ = D / 32;
   constexpr int kKeys = 128;                      // keys per workgroup (4 waves x 32)
-  __shared__ __attribute__((aligned(128))) uint8_t stage0[L::kStageAligned];
-  __shared__ __attribute__((aligned(128))) uint8_t stage1[L::kStageAligned];
+  __shared__ __attribute__((aligned(128))) uint8_t smem[2 * L::kStageAligned];
 
   const int tid = threadIdx.x;
   // wave index as a scalar: every branch that guards a matrix-core instruction
@@ -277,11 +279,16 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdParams p) {
     // unit it -> (tile, head of the group)
     auto tile_of = [&](int it) { return down ? ntq - 1 - it / p.g : tfirst + it / p.g; };
 
-    // one unit: prefetch unit it+1 into `nxt`, compute on `cur`, then wait for
-    // the prefetch and synchronise (both buffers are free again afterwards)
-    auto unit = [&](uint8_t* cur, uint8_t* nxt, int it) {
+    if (niter > 0) dkdv_issue<D>(smem, p, b, kvh * p.g, tile_of(0) * L::kRows, wave, lane);
+    wait_vmem();
+    __syncthreads();
+
+    for (int it = 0; it < niter; ++it) {
+      // prefetch unit it+1 into the other buffer while computing on this one
+      uint8_t* cur = smem + (it & 1) * L::kStageAligned;
       if (it + 1 < niter)
-        dkdv_issue<D>(nxt, p, b, kvh * p.g + (it + 1) % p.g, tile_of(it + 1) * L::kRows, wave, lane);
+        dkdv_issue<D>(smem + ((it + 1) & 1) * L::kStageAligned, p, b, kvh * p.g + (it + 1) % p.g,
+                      tile_of(it + 1) * L::kRows, wave, lane);
       const int t0 = tile_of(it) * L::kRows;
       if (wave_live) {
         const uint8_t* qs = cur + L::kOffQ;
@@ -320,14 +327,6 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdParams p) {
       }
       wait_vmem();
       __syncthreads();
-    };
-
-    if (niter > 0) dkdv_issue<D>(stage0, p, b, kvh * p.g, tile_of(0) * L::kRows, wave, lane);
-    wait_vmem();
-    __syncthreads();
-    for (int it = 0; it < niter; it += 2) {
-      unit(stage0, stage1, it);
-      if (it + 1 < niter) unit(stage1, stage0, it + 1);
     }
 
     // write dK = scale * dK^T^T and dV: lane = key u, dims 32j + 8*(i/4) + 4hh + i%4
@@ -431,16 +430,12 @@ __device__ __forceinline__ void dq_half(const uint8_t* ks, const uint8_t* vs, co
   }
 }
 
-// The two staging buffers are separate LDS objects and the tile loop is
-// unrolled by two, so the compiler sees that LDS reads of one buffer never
-// overlap the DMA filling the other.
 template <int D, bool HAS_MASK, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const BwdParams p) {
   using L = DqLayout<D>;
   constexpr int KK = D / 16;
   constexpr int DJ = D / 32;
-  __shared__ __attribute__((aligned(128))) uint8_t stage0[L::kStageAligned];
-  __shared__ __attribute__((aligned(128))) uint8_t stage1[L::kStageAligned];
+  __shared__ __attribute__((aligned(128))) uint8_t smem[2 * L::kStageAligned];
 
   const int tid = threadIdx.x;
   // wave index as a scalar: every branch that guards a matrix-core instruction
@@ -492,14 +487,15 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const BwdParams p) {
     for (int j = 0; j < DJ; ++j) dqa[j] = f32x16{};
 
     uint32_t vbyte = 0;
-    dq_issue<D, HAS_MASK>(stage0, vbyte, p, b, kvh, 0, wave, lane, tid);
-    if (HAS_MASK && tid < L::kBN) stage0[L::kOffValid + tid] = uint8_t(vbyte);
+    dq_issue<D, HAS_MASK>(smem, vbyte, p, b, kvh, 0, wave, lane, tid);
+    if (HAS_MASK && tid < L::kBN) smem[L::kOffValid + tid] = uint8_t(vbyte);
     wait_vmem();
     __syncthreads();
 
-    // one tile: prefetch tile it+1 into `nxt`, compute on `cur`, then wait for
-    // the prefetch and synchronise
-    auto unit = [&](uint8_t* cur, uint8_t* nxt, int it) {
+    for (int it = 0; it < ntiles; ++it) {
+      // prefetch tile it+1 into the other buffer while computing on this one
+      uint8_t* cur = smem + (it & 1) * L::kStageAligned;
+      uint8_t* nxt = smem + ((it + 1) & 1) * L::kStageAligned;
       if (it + 1 < ntiles) dq_issue<D, HAS_MASK>(nxt, vbyte, p, b, kvh, it + 1, wave, lane, tid);
       const int tile0 = it * L::kBN;
       if (wave_live && !(CAUSAL && tile0 > wave_last)) {
@@ -519,10 +515,6 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const BwdParams p) {
       if (HAS_MASK && it + 1 < ntiles && tid < L::kBN) nxt[L::kOffValid + tid] = uint8_t(vbyte);
       wait_vmem();
       __syncthreads();
-    };
-    for (int it = 0; it < ntiles; it += 2) {
-      unit(stage0, stage1, it);
-      if (it + 1 < ntiles) unit(stage1, stage0, it + 1);
     }
 
     if (t < p.n) {
@@ -587,10 +579,16 @@ hipError_t launch_bwd_d(const BwdParams& p, bool has_mask, bool o_f32, hipStream
 
 }  // namespace
 
-size_t attn_bwd_workspace_bytes(int32_t B, int64_t n, int32_t Hq) {
+namespace {
+// one float32 [B][Hq][n] array, rounded up to 256 bytes
+size_t row_array_bytes(int32_t B, int64_t n, int32_t Hq) {
   const size_t bytes = size_t(B) * size_t(n) * size_t(Hq) * sizeof(float);
   return (bytes + 255) / 256 * 256;
 }
+}  // namespace
+
+// Dl = dO . O, then the base-2 logsumexp
+size_t attn_bwd_workspace_bytes(int32_t B, int64_t n, int32_t Hq) { return 2 * row_array_bytes(B, n, Hq); }
 
 hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const uint8_t* valid, const void* o,
                                 const float* lse, const void* dout, float* dq, float* dk, float* dv,
@@ -607,6 +605,7 @@ hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, con
   p.dk = dk;
   p.dv = dv;
   p.rowdot = workspace;
+  p.lse2 = workspace + row_array_bytes(s.B, s.n, s.Hq) / sizeof(float);
   p.B = s.B;
   p.n = int32_t(s.n);
   p.Hq = s.Hq;

@@ -128,16 +128,22 @@ __device__ __forceinline__ u32x4 tr_operand(const uint8_t* tile, int r0, int col
 
 // ---- direct global -> LDS staging (buffer loads with the LDS destination)
 //
-// One buffer_load ... lds instruction moves 16 bytes per lane from global
-// memory straight into LDS, lane l landing at (wave-uniform LDS base) + 16*l,
-// without passing through registers.  Offsets at or beyond the buffer
-// resource's byte size read as zero, which pads sequence tails for free.
+// One buffer_load ... lds instruction moves 16 (or 4) bytes per lane from
+// global memory straight into LDS, lane l landing at (wave-uniform LDS base
+// in M0) + 16*l (4*l), without passing through registers.  Offsets at or
+// beyond the buffer resource's byte size read as zero, which pads sequence
+// tails for free.
+//
+// The instructions are issued from inline assembly, out of the compiler's
+// sight: it would otherwise make every later LDS read it cannot prove
+// disjoint (transposing reads carry no alias information) wait for all
+// outstanding DMA, including the prefetch into the other staging buffer.
+// Callers therefore synchronise by hand: wait_vmem() and a workgroup barrier
+// before the staged data is read, and a barrier before a buffer is refilled.
+// M0 is saved and restored around each instruction, and one wait state
+// separates the M0 write from the load that reads it.
 typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) uint32_t* lds_u32_ptr;
-
-extern "C" __device__ void llvm_amdgcn_raw_buffer_load_lds(i32x4 rsrc, lds_u32_ptr lds, int size, int voffset,
-                                                          int soffset, int offset, int aux)
-    __asm("llvm.amdgcn.raw.buffer.load.lds");
+typedef __attribute__((address_space(3))) uint8_t* lds_u8_ptr;
 
 // Buffer resource for a raw byte range [base, base + bytes) (gfx9 layout:
 // 48-bit base, stride 0, byte size, default format word).
@@ -151,17 +157,57 @@ __device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
   return r;
 }
 
-__device__ __forceinline__ void dma16(const i32x4 rsrc, uint8_t* lds, int voffset) {
-  llvm_amdgcn_raw_buffer_load_lds(rsrc, (lds_u32_ptr)(lds), 16, voffset, 0, 0, 0);
+// The resource and the LDS base are wave-uniform by construction; reading
+// them through the first lane puts them in scalar registers as the
+// instruction requires.
+__device__ __forceinline__ i32x4 uniform_rsrc(const i32x4 r) {
+  i32x4 u;
+  u[0] = __builtin_amdgcn_readfirstlane(r[0]);
+  u[1] = __builtin_amdgcn_readfirstlane(r[1]);
+  u[2] = __builtin_amdgcn_readfirstlane(r[2]);
+  u[3] = __builtin_amdgcn_readfirstlane(r[3]);
+  return u;
 }
 
+__device__ __forceinline__ uint32_t lds_addr(uint8_t* lds) {
+  return __builtin_amdgcn_readfirstlane(uint32_t(uintptr_t((lds_u8_ptr)lds)));
+}
+
+// 16 bytes per lane: global rsrc + voffset -> LDS lds + 16 * lane
+__device__ __forceinline__ void dma16(const i32x4 rsrc, uint8_t* lds, int voffset) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr(lds)), "v"(voffset), "s"(uniform_rsrc(rsrc))
+      : "memory");
+}
+
+// 4 bytes per lane: global rsrc + voffset -> LDS lds + 4 * lane
 __device__ __forceinline__ void dma4(const i32x4 rsrc, uint8_t* lds, int voffset) {
-  llvm_amdgcn_raw_buffer_load_lds(rsrc, (lds_u32_ptr)(lds), 4, voffset, 0, 0, 0);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr(lds)), "v"(voffset), "s"(uniform_rsrc(rsrc))
+      : "memory");
 }
 
 // Wait until this wave's outstanding global loads (including the LDS DMA)
-// have landed.
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// have landed: s_waitcnt vmcnt(0), expcnt and lgkmcnt left at their maxima
+// (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).  The
+// builtin, unlike an asm statement, tells the compiler's wait-count tracking
+// that every earlier load is complete, so it inserts no vmcnt wait of its
+// own in the loop that follows (one that would also stall on the prefetch).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // DMA a ROWS x D bf16 tile, rows row0.. of a row-major tensor whose rows are
 // row_stride_bytes apart, into the swizzled LDS layout of rm_off.  `rows_ok`
