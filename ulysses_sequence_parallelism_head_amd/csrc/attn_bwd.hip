@@ -43,7 +43,7 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kSplitRows = 512;
+constexpr int kSplitRows = 512;   // a multiple of both query tile heights (64)
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct BwdParams {
@@ -283,50 +283,56 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdParams p) {
     wait_vmem();
     __syncthreads();
 
-    for (int it = 0; it < niter; ++it) {
-      // prefetch unit it+1 into the other buffer while computing on this one
-      uint8_t* cur = smem + (it & 1) * L::kStageAligned;
-      if (it + 1 < niter)
-        dkdv_issue<D>(smem + ((it + 1) & 1) * L::kStageAligned, p, b, kvh * p.g + (it + 1) % p.g,
-                      tile_of(it + 1) * L::kRows, wave, lane);
-      const int t0 = tile_of(it) * L::kRows;
-      if (wave_live) {
-        const uint8_t* qs = cur + L::kOffQ;
-        const uint8_t* dos = cur + L::kOffDO;
-        const float* lses = reinterpret_cast<const float*>(cur + L::kOffLSE);
-        const float* dls = reinterpret_cast<const float*>(cur + L::kOffDL);
-        // 32-row block rb sees this wave's keys only if its last row >= k0w
-        bool act[2];
-        f32x16 s[2], dp[2];
+    // units [it0, it1), all on tiles of one kind: rows below kSplitRows (hi/lo
+    // split) or not.  Keeping the choice out of the loop body matters: a
+    // branch inside it makes the two sides allocate the 128 dK/dV accumulator
+    // registers differently and copy all of them at every merge.
+    auto run = [&](int it0, int it1, auto split_tag) {
+      constexpr bool SPLIT = decltype(split_tag)::value;
+      for (int it = it0; it < it1; ++it) {
+        // prefetch unit it+1 into the other buffer while computing on this one
+        uint8_t* cur = smem + (it & 1) * L::kStageAligned;
+        if (it + 1 < niter)
+          dkdv_issue<D>(smem + ((it + 1) & 1) * L::kStageAligned, p, b, kvh * p.g + (it + 1) % p.g,
+                        tile_of(it + 1) * L::kRows, wave, lane);
+        const int t0 = tile_of(it) * L::kRows;
+        if (wave_live) {
+          const uint8_t* qs = cur + L::kOffQ;
+          const uint8_t* dos = cur + L::kOffDO;
+          const float* lses = reinterpret_cast<const float*>(cur + L::kOffLSE);
+          const float* dls = reinterpret_cast<const float*>(cur + L::kOffDL);
+          // 32-row blocks one after the other (only one block's S and dP live);
+          // block rb sees this wave's keys only if its last row >= k0w
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          act[rb] = !(CAUSAL && t0 + rb * 32 + 31 < k0w);
-          s[rb] = f32x16{};
-          dp[rb] = f32x16{};
-        }
-        // S[q][key] and dP[q][key] for both row blocks: lane = key, rows q = (i/4)*8 + 4hh + i%4
+          for (int rb = 0; rb < 2; ++rb) {
+            if (CAUSAL && t0 + rb * 32 + 31 < k0w) continue;
+            // S[q][key] and dP[q][key]: lane = key, rows q = (i/4)*8 + 4hh + i%4
+            f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          if (!act[rb]) continue;
-#pragma unroll
-          for (int kk = 0; kk < KK; ++kk) {
-            const int off = rm_off<L::kRowBytes>(rb * 32 + l32, 2 * kk + hh);
-            s[rb] = mfma32x32x16(*reinterpret_cast<const u32x4*>(qs + off), kf[kk], s[rb]);
-            dp[rb] = mfma32x32x16(*reinterpret_cast<const u32x4*>(dos + off), vf[kk], dp[rb]);
+            for (int kk = 0; kk < KK; ++kk) {
+              const int off = rm_off<L::kRowBytes>(rb * 32 + l32, 2 * kk + hh);
+              s = mfma32x32x16(*reinterpret_cast<const u32x4*>(qs + off), kf[kk], s);
+              dp = mfma32x32x16(*reinterpret_cast<const u32x4*>(dos + off), vf[kk], dp);
+            }
+            // keep three k-steps of operands in flight: LDS latency is several
+            // times one MFMA pair, and this wave is alone on its SIMD
+            pipeline_reads_mfma<6, 2 * KK>();
+            dkdv_rows<D, CAUSAL, SPLIT>(qs, dos, lses, dls, s, dp, rb, t0, u, key_ok, hh, lane, p.c, dka, dva);
           }
         }
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          if (!act[rb]) continue;
-          if (t0 + rb * 32 < kSplitRows)
-            dkdv_rows<D, CAUSAL, true>(qs, dos, lses, dls, s[rb], dp[rb], rb, t0, u, key_ok, hh, lane, p.c, dka, dva);
-          else
-            dkdv_rows<D, CAUSAL, false>(qs, dos, lses, dls, s[rb], dp[rb], rb, t0, u, key_ok, hh, lane, p.c, dka,
-                                        dva);
-        }
+        wait_vmem();
+        __syncthreads();
       }
-      wait_vmem();
-      __syncthreads();
+    };
+    // tiles below kSplitRows / kRows need the split: tfirst .. min(that, ntq) - 1
+    constexpr int kSplitTiles = kSplitRows / L::kRows;
+    const int nsplit = max(0, min(kSplitTiles, ntq) - tfirst) * p.g;
+    if (down) {                       // split tiles come last
+      run(0, niter - nsplit, std::false_type{});
+      run(niter - nsplit, niter, std::true_type{});
+    } else {                          // split tiles come first
+      run(0, nsplit, std::true_type{});
+      run(nsplit, niter, std::false_type{});
     }
 
     // write dK = scale * dK^T^T and dV: lane = key u, dims 32j + 8*(i/4) + 4hh + i%4

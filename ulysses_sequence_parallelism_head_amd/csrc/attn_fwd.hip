@@ -23,8 +23,12 @@
 //    product is read with the gfx950 transposing LDS read (ds_read_b64_tr_b16),
 //    in the key order of the score registers, so nothing is transposed in
 //    registers and both read patterns are free of bank conflicts.
-//  * Global->LDS staging of tile i+1 is issued before the MFMA work on tile i
-//    (double-buffered LDS, one barrier per tile).
+//  * Tile i+1 is copied global->LDS by buffer-load DMA (no registers, keys
+//    past n read as zero) while the MFMA work runs on tile i (double-buffered
+//    LDS, one barrier per tile).
+//  * The loop body has no branch between matrix instructions: the hi/lo split
+//    is chosen per workgroup outside the loop, and on a causal diagonal tile
+//    both 32-key halves are computed (a half with no visible key adds zeros).
 //  * Online softmax in base 2: the row max is taken on raw scores and each
 //    probability is one FMA (score * scale*log2(e) - max) and one v_exp_f32.
 //    The running max is only raised when a tile's max exceeds it by more than
@@ -34,6 +38,8 @@
 //    the error of the few-key rows, whose weights are large, far below 1e-2.
 //  * The grid is launched longest-first (last query blocks first) so the
 //    causal triangle's long blocks do not trail at the end.
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -58,7 +64,6 @@ struct FwdLayout {
   static constexpr int kBytesValid = kBN;
   static constexpr int kStage = kBytesK + kBytesV + kBytesValid;
   static constexpr int kStageAligned = (kStage + 127) / 128 * 128;
-  static constexpr int kChunksPerThread = kBN * kChunks / kThreads;   // per tensor
 };
 
 struct FwdParams {
@@ -78,50 +83,24 @@ struct FwdParams {
   int32_t causal;
 };
 
-template <int D>
-struct Staging {
-  u32x4 kreg[FwdLayout<D>::kChunksPerThread];
-  u32x4 vreg[FwdLayout<D>::kChunksPerThread];
-  uint32_t vbyte;
-};
-
-// Global -> registers: 16-byte chunks of the K and V rows of one 64-key tile
-// (consecutive threads read consecutive chunks of a row: coalesced).
+// DMA the K and V rows of 64-key tile `tile` into the swizzled row-major
+// tiles of `stage` (keys past n read as zero), and load the tile's key-valid
+// bytes into a register of the first 64 threads (stored by the caller once
+// the buffer is free).
 template <int D, bool HAS_MASK>
-__device__ __forceinline__ void stage_load(Staging<D>& st, const FwdParams& p, int b, int kvh, int tile, int tid) {
+__device__ __forceinline__ void fwd_issue(uint8_t* stage, uint32_t& vbyte, const FwdParams& p, int b, int kvh,
+                                          int tile, int wave, int lane, int tid) {
   using L = FwdLayout<D>;
-  const int key_base = tile * kBN;
-#pragma unroll
-  for (int u = 0; u < L::kChunksPerThread; ++u) {
-    const int c = tid + u * kThreads;
-    const int key = key_base + c / L::kChunks;
-    if (key < p.n) {
-      const int64_t off = ((int64_t(b) * p.n + key) * p.Hkv + kvh) * D + (c % L::kChunks) * 8;
-      st.kreg[u] = *reinterpret_cast<const u32x4*>(p.k + off);
-      st.vreg[u] = *reinterpret_cast<const u32x4*>(p.v + off);
-    } else {
-      st.kreg[u] = u32x4{0, 0, 0, 0};
-      st.vreg[u] = u32x4{0, 0, 0, 0};
-    }
-  }
+  const int key0 = tile * kBN;
+  const int rows_ok = min(kBN, p.n - key0);
+  const int64_t off = ((int64_t(b) * p.n + key0) * p.Hkv + kvh) * D;
+  const int stride = p.Hkv * D * 2;
+  dma_tile<D, kBN, kWaves>(stage, p.k + off, stride, rows_ok, wave, lane);
+  dma_tile<D, kBN, kWaves>(stage + L::kBytesK, p.v + off, stride, rows_ok, wave, lane);
   if (HAS_MASK && tid < kBN) {
-    const int key = key_base + tid;
-    st.vbyte = (key < p.n) ? (p.valid[int64_t(b) * p.n + key] != 0 ? 1u : 0u) : 0u;
+    const int key = key0 + tid;
+    vbyte = (key < p.n) ? (p.valid[int64_t(b) * p.n + key] != 0 ? 1u : 0u) : 0u;
   }
-}
-
-// Registers -> LDS: row-major tiles with swizzled chunks.
-template <int D, bool HAS_MASK>
-__device__ __forceinline__ void stage_store(const Staging<D>& st, uint8_t* stage, int tid) {
-  using L = FwdLayout<D>;
-#pragma unroll
-  for (int u = 0; u < L::kChunksPerThread; ++u) {
-    const int c = tid + u * kThreads;
-    const int off = rm_off<L::kRowBytes>(c / L::kChunks, c % L::kChunks);
-    *reinterpret_cast<u32x4*>(stage + off) = st.kreg[u];
-    *reinterpret_cast<u32x4*>(stage + L::kBytesK + off) = st.vreg[u];
-  }
-  if (HAS_MASK && tid < kBN) stage[L::kBytesK + L::kBytesV + tid] = uint8_t(st.vbyte);
 }
 
 template <int D, bool HAS_MASK, bool O_F32, bool CAUSAL>
@@ -168,161 +147,167 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const FwdPar
       qf[kk] = ok ? *reinterpret_cast<const u32x4*>(p.q + off + 16 * kk) : u32x4{0, 0, 0, 0};
   }
 
-  f32x16 oacc[DJ];
+  // Rows below kSplitRows take the hi/lo path; the choice is made once per
+  // workgroup (its first row), outside the tile loop, so the loop body has
+  // no branch between its matrix instructions.
+  auto run = [&](auto split_tag) {
+    constexpr bool SPLIT = decltype(split_tag)::value;
+    f32x16 oacc[DJ];
 #pragma unroll
-  for (int j = 0; j < DJ; ++j) oacc[j] = f32x16{};
-  float m_ref = -INFINITY;   // running reference max (log2 units), identical in both half-waves
-  float lsum = 0.f;          // this half-wave's share of the row sum
-  const bool split = p0 < kSplitRows;
+    for (int j = 0; j < DJ; ++j) oacc[j] = f32x16{};
+    float m_ref = -INFINITY;   // running reference max (log2 units), identical in both half-waves
+    float lsum = 0.f;          // this half-wave's share of the row sum
 
-  Staging<D> st;
-  stage_load<D, HAS_MASK>(st, p, b, kvh, 0, tid);
-  stage_store<D, HAS_MASK>(st, smem, tid);
-  __syncthreads();
+    uint32_t vbyte = 0;
+    fwd_issue<D, HAS_MASK>(smem, vbyte, p, b, kvh, 0, wave, lane, tid);
+    if (HAS_MASK && tid < kBN) smem[L::kBytesK + L::kBytesV + tid] = uint8_t(vbyte);
+    wait_vmem();
+    __syncthreads();
 
-  for (int it = 0; it < ntiles; ++it) {
-    uint8_t* cur = smem + (it & 1) * L::kStageAligned;
-    if (it + 1 < ntiles) stage_load<D, HAS_MASK>(st, p, b, kvh, it + 1, tid);
+    for (int it = 0; it < ntiles; ++it) {
+      // prefetch tile it+1 into the other buffer while computing on this one
+      uint8_t* cur = smem + (it & 1) * L::kStageAligned;
+      uint8_t* nxt = smem + ((it + 1) & 1) * L::kStageAligned;
+      if (it + 1 < ntiles) fwd_issue<D, HAS_MASK>(nxt, vbyte, p, b, kvh, it + 1, wave, lane, tid);
 
-    const int tile0 = it * kBN;
-    if (wave_live && !(CAUSAL && tile0 > wave_last)) {
-      const uint8_t* ks = cur;
-      const uint8_t* vs = cur + L::kBytesK;
-      const bool act1 = !(CAUSAL && tile0 + 32 > wave_last);   // second half-tile has a visible key
+      const int tile0 = it * kBN;
+      if (wave_live && !(CAUSAL && tile0 > wave_last)) {
+        const uint8_t* ks = cur;
+        const uint8_t* vs = cur + L::kBytesK;
 
-      // ---- S^T for the two 32-key halves
-      f32x16 s0 = f32x16{}, s1 = f32x16{};
+        // ---- S^T for the two 32-key halves.  On a causal diagonal tile the
+        // second half may hold no visible key; it is computed anyway (its
+        // scores are masked to -inf below, so it adds exact zeros to O).
+        f32x16 s0 = f32x16{}, s1 = f32x16{};
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const u32x4 a0 = *reinterpret_cast<const u32x4*>(ks + rm_off<L::kRowBytes>(l32, 2 * kk + hh));
-        s0 = mfma32x32x16(a0, qf[kk], s0);
-        if (act1) {
+        for (int kk = 0; kk < KK; ++kk) {
+          const u32x4 a0 = *reinterpret_cast<const u32x4*>(ks + rm_off<L::kRowBytes>(l32, 2 * kk + hh));
           const u32x4 a1 = *reinterpret_cast<const u32x4*>(ks + rm_off<L::kRowBytes>(32 + l32, 2 * kk + hh));
+          s0 = mfma32x32x16(a0, qf[kk], s0);
           s1 = mfma32x32x16(a1, qf[kk], s1);
         }
-      }
+        pipeline_reads_mfma<6, 2 * KK>();   // three k-steps of K rows in flight
 
-      // ---- raw scores and masks (masked keys -> -inf)
-      float x[32];
+        // ---- raw scores and masks (masked keys -> -inf)
+        float x[32];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        x[i] = s0[i];
-        x[16 + i] = act1 ? s1[i] : -INFINITY;
-      }
-      const bool diag = CAUSAL && (tile0 + kBN - 1 > p0);
-      const bool tail = !CAUSAL && (tile0 + kBN > p.n);
-      if (diag || tail) {
-        // element i holds key tile0 + 4hh + C_i with C_i a compile-time constant;
-        // it is visible iff C_i <= lim.  Causal: key <= t (this also hides keys
-        // >= n, since t < n); otherwise only the tail limit key < n applies.
-        const int lim = (CAUSAL ? t : p.n - 1) - tile0 - 4 * hh;
+        for (int i = 0; i < 16; ++i) {
+          x[i] = s0[i];
+          x[16 + i] = s1[i];
+        }
+        const bool diag = CAUSAL && (tile0 + kBN - 1 > p0);
+        const bool tail = !CAUSAL && (tile0 + kBN > p.n);
+        if (diag || tail) {
+          // element i holds key tile0 + 4hh + C_i with C_i a compile-time constant;
+          // it is visible iff C_i <= lim.  Causal: key <= t (this also hides keys
+          // >= n, since t < n); otherwise only the tail limit key < n applies.
+          const int lim = (CAUSAL ? t : p.n - 1) - tile0 - 4 * hh;
+#pragma unroll
+          for (int i = 0; i < 32; ++i) {
+            const int ci = (i >> 4) * 32 + ((i & 15) >> 2) * 8 + (i & 3);
+            x[i] = (ci > lim) ? -INFINITY : x[i];
+          }
+        }
+        if (HAS_MASK) {
+          const uint8_t* vb = cur + L::kBytesK + L::kBytesV;
+#pragma unroll
+          for (int grp = 0; grp < 8; ++grp) {
+            const int kt = (grp >> 2) * 32 + (grp & 3) * 8 + hh * 4;
+            const uint32_t w = *reinterpret_cast<const uint32_t*>(vb + kt);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[grp * 4 + e] = ((w >> (8 * e)) & 0xffu) ? x[grp * 4 + e] : -INFINITY;
+          }
+        }
+
+        // ---- online softmax (lazy rescale); scale > 0, so max(s * c) = max(s) * c
+        float mr = x[0];
+#pragma unroll
+        for (int i = 1; i < 32; ++i) mr = fmaxf(mr, x[i]);
+        mr = halves_max(mr);
+        const float mx = mr * p.c;
+        const bool raise = mx > m_ref + kRescaleSlack;
+        if (__any(raise)) {
+          const float alpha = raise ? __builtin_amdgcn_exp2f(m_ref - mx) : 1.0f;
+          if (raise) m_ref = mx;
+          lsum *= alpha;
+#pragma unroll
+          for (int j = 0; j < DJ; ++j)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[j][i] *= alpha;
+        }
+        const float neg_m = (m_ref == -INFINITY) ? 0.f : -m_ref;
+        float pr[32];
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
-          const int ci = (i >> 4) * 32 + ((i & 15) >> 2) * 8 + (i & 3);
-          x[i] = (ci > lim) ? -INFINITY : x[i];
+          pr[i] = __builtin_amdgcn_exp2f(fmaf(x[i], p.c, neg_m));
+          lsum += pr[i];
         }
-      }
-      if (HAS_MASK) {
-        const uint8_t* vb = cur + L::kBytesK + L::kBytesV;
-#pragma unroll
-        for (int grp = 0; grp < 8; ++grp) {
-          const int kt = (grp >> 2) * 32 + (grp & 3) * 8 + hh * 4;
-          const uint32_t w = *reinterpret_cast<const uint32_t*>(vb + kt);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) x[grp * 4 + e] = ((w >> (8 * e)) & 0xffu) ? x[grp * 4 + e] : -INFINITY;
-        }
-      }
 
-      // ---- online softmax (lazy rescale); scale > 0, so max(s * c) = max(s) * c
-      float mr = x[0];
-#pragma unroll
-      for (int i = 1; i < 32; ++i) mr = fmaxf(mr, x[i]);
-      mr = halves_max(mr);
-      const float mx = mr * p.c;
-      const bool raise = mx > m_ref + kRescaleSlack;
-      if (__any(raise)) {
-        const float alpha = raise ? __builtin_amdgcn_exp2f(m_ref - mx) : 1.0f;
-        if (raise) m_ref = mx;
-        lsum *= alpha;
-#pragma unroll
-        for (int j = 0; j < DJ; ++j)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[j][i] *= alpha;
-      }
-      const float neg_m = (m_ref == -INFINITY) ? 0.f : -m_ref;
-      float pr[32];
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        pr[i] = __builtin_amdgcn_exp2f(fmaf(x[i], p.c, neg_m));
-        lsum += pr[i];
-      }
-
-      // ---- P^T as B operand: per half-tile kb and 16-key slice kk2, the lane's 8 scores
-      u32x4 phi[4], plo[4];
-#pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        const float* pp = pr + f * 8;
-        phi[f] = u32x4{pack_bf16x2(pp[0], pp[1]), pack_bf16x2(pp[2], pp[3]), pack_bf16x2(pp[4], pp[5]),
-                       pack_bf16x2(pp[6], pp[7])};
-      }
-      if (split) {
+        // ---- P^T as B operand: per half-tile and 16-key slice f, the lane's 8 scores
+        u32x4 phi[4], plo[4];
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
           const float* pp = pr + f * 8;
-          float r[8];
+          phi[f] = u32x4{pack_bf16x2(pp[0], pp[1]), pack_bf16x2(pp[2], pp[3]), pack_bf16x2(pp[4], pp[5]),
+                         pack_bf16x2(pp[6], pp[7])};
+          if (SPLIT) {
+            float r[8];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            r[2 * e] = pp[2 * e] - bf16lo_to_f32(phi[f][e]);
-            r[2 * e + 1] = pp[2 * e + 1] - bf16hi_to_f32(phi[f][e]);
+            for (int e = 0; e < 4; ++e) {
+              r[2 * e] = pp[2 * e] - bf16lo_to_f32(phi[f][e]);
+              r[2 * e + 1] = pp[2 * e + 1] - bf16hi_to_f32(phi[f][e]);
+            }
+            plo[f] = u32x4{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]), pack_bf16x2(r[4], r[5]),
+                           pack_bf16x2(r[6], r[7])};
           }
-          plo[f] = u32x4{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]), pack_bf16x2(r[4], r[5]),
-                         pack_bf16x2(r[6], r[7])};
+        }
+
+        // ---- O^T += V^T P^T
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+#pragma unroll
+          for (int j = 0; j < DJ; ++j) {
+            // V^T rows d = 32j + l%32, keys in the order of phi[f] (tile rows 16f + ...)
+            const u32x4 a = tr_operand<L::kRowBytes>(vs, 16 * f, 32 * j, lane);
+            oacc[j] = mfma32x32x16(a, phi[f], oacc[j]);
+            if (SPLIT) oacc[j] = mfma32x32x16(a, plo[f], oacc[j]);
+          }
         }
       }
 
-      // ---- O^T += V^T P^T
-#pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        if (f >= 2 && !act1) break;
-#pragma unroll
-        for (int j = 0; j < DJ; ++j) {
-          // V^T rows d = 32j + l%32, keys in the order of phi[f] (tile rows 16f + ...)
-          const u32x4 a = tr_operand<L::kRowBytes>(vs, 16 * f, 32 * j, lane);
-          oacc[j] = mfma32x32x16(a, phi[f], oacc[j]);
-          if (split) oacc[j] = mfma32x32x16(a, plo[f], oacc[j]);
-        }
-      }
+      if (HAS_MASK && it + 1 < ntiles && tid < kBN) nxt[L::kBytesK + L::kBytesV + tid] = uint8_t(vbyte);
+      wait_vmem();
+      __syncthreads();
     }
 
-    if (it + 1 < ntiles) stage_store<D, HAS_MASK>(st, smem + ((it + 1) & 1) * L::kStageAligned, tid);
-    __syncthreads();
-  }
-
-  // ---- epilogue: normalise, write O (row t, dims 32j + 8*(i/4) + 4hh + i%4) and LSE
-  if (t < p.n) {
-    const float ltot = halves_sum(lsum);
-    const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
-    const int64_t obase = ((int64_t(b) * p.n + t) * p.Hq + head) * D;
+    // ---- epilogue: normalise, write O (row t, dims 32j + 8*(i/4) + 4hh + i%4) and LSE
+    if (t < p.n) {
+      const float ltot = halves_sum(lsum);
+      const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
+      const int64_t obase = ((int64_t(b) * p.n + t) * p.Hq + head) * D;
 #pragma unroll
-    for (int j = 0; j < DJ; ++j) {
+      for (int j = 0; j < DJ; ++j) {
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int d0 = j * 32 + i4 * 8 + hh * 4;
-        const float v0 = oacc[j][i4 * 4 + 0] * inv, v1 = oacc[j][i4 * 4 + 1] * inv;
-        const float v2 = oacc[j][i4 * 4 + 2] * inv, v3 = oacc[j][i4 * 4 + 3] * inv;
-        if (O_F32) {
-          *reinterpret_cast<f32x4*>(static_cast<float*>(p.o) + obase + d0) = f32x4{v0, v1, v2, v3};
-        } else {
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.o) + obase + d0) =
-              u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int d0 = j * 32 + i4 * 8 + hh * 4;
+          const float v0 = oacc[j][i4 * 4 + 0] * inv, v1 = oacc[j][i4 * 4 + 1] * inv;
+          const float v2 = oacc[j][i4 * 4 + 2] * inv, v3 = oacc[j][i4 * 4 + 3] * inv;
+          if (O_F32) {
+            *reinterpret_cast<f32x4*>(static_cast<float*>(p.o) + obase + d0) = f32x4{v0, v1, v2, v3};
+          } else {
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.o) + obase + d0) =
+                u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+          }
         }
       }
+      if (hh == 0) {
+        p.lse[(int64_t(b) * p.Hq + head) * p.n + t] =
+            ltot > 0.f ? (m_ref + __log2f(ltot)) * kLn2 : -INFINITY;
+      }
     }
-    if (hh == 0) {
-      p.lse[(int64_t(b) * p.Hq + head) * p.n + t] =
-          ltot > 0.f ? (m_ref + __log2f(ltot)) * kLn2 : -INFINITY;
-    }
-  }
+  };
+  if (pb * p.pw < kSplitRows) run(std::true_type{});
+  else run(std::false_type{});
 }
 
 template <int D, bool HAS_MASK, bool O_F32, bool CAUSAL>

@@ -126,6 +126,25 @@ __device__ __forceinline__ u32x4 tr_operand(const uint8_t* tile, int r0, int col
   return u32x4{a[0], a[1], b[0], b[1]};
 }
 
+// ---- instruction scheduling hints
+//
+// Order the LDS reads and MFMAs of the enclosing basic block as a software
+// pipeline: AHEAD reads first, then alternating pairs of MFMAs and pairs of
+// reads, then the remaining MFMAs (N reads feeding N MFMAs in total).  The
+// compiler's latency model treats LDS reads as short and otherwise issues
+// them only two ahead of their use.
+template <int AHEAD, int N>
+__device__ __forceinline__ void pipeline_reads_mfma() {
+  constexpr int kMaskMfma = 0x008, kMaskDsRead = 0x100;
+  __builtin_amdgcn_sched_group_barrier(kMaskDsRead, AHEAD, 0);
+#pragma unroll
+  for (int i = 0; i < (N - AHEAD) / 2; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kMaskMfma, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(kMaskDsRead, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kMaskMfma, AHEAD, 0);
+}
+
 // ---- direct global -> LDS staging (buffer loads with the LDS destination)
 //
 // One buffer_load ... lds instruction moves 16 (or 4) bytes per lane from
