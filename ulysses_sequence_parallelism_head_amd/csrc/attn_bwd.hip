@@ -301,24 +301,34 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdParams p) {
           const uint8_t* dos = cur + L::kOffDO;
           const float* lses = reinterpret_cast<const float*>(cur + L::kOffLSE);
           const float* dls = reinterpret_cast<const float*>(cur + L::kOffDL);
-          // 32-row blocks one after the other (only one block's S and dP live);
-          // block rb sees this wave's keys only if its last row >= k0w
+          // S[q][key] and dP[q][key] for both 32-row blocks (lane = key, rows
+          // q = rb*32 + (i/4)*8 + 4hh + i%4), then P, dS and the dV/dK products
+          // block by block, all in one basic block so that one block's
+          // exponentials overlap the other block's matrix work.  On a causal
+          // diagonal tile a block may hold no row that sees these keys; it is
+          // computed anyway and masked to exact zeros.
+          f32x16 s[2], dp[2];
 #pragma unroll
           for (int rb = 0; rb < 2; ++rb) {
-            if (CAUSAL && t0 + rb * 32 + 31 < k0w) continue;
-            // S[q][key] and dP[q][key]: lane = key, rows q = (i/4)*8 + 4hh + i%4
-            f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-              const int off = rm_off<L::kRowBytes>(rb * 32 + l32, 2 * kk + hh);
-              s = mfma32x32x16(*reinterpret_cast<const u32x4*>(qs + off), kf[kk], s);
-              dp = mfma32x32x16(*reinterpret_cast<const u32x4*>(dos + off), vf[kk], dp);
-            }
-            // keep three k-steps of operands in flight: LDS latency is several
-            // times one MFMA pair, and this wave is alone on its SIMD
-            pipeline_reads_mfma<6, 2 * KK>();
-            dkdv_rows<D, CAUSAL, SPLIT>(qs, dos, lses, dls, s, dp, rb, t0, u, key_ok, hh, lane, p.c, dka, dva);
+            s[rb] = f32x16{};
+            dp[rb] = f32x16{};
           }
+#pragma unroll
+          for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+              const int off = rm_off<L::kRowBytes>(rb * 32 + l32, 2 * kk + hh);
+              s[rb] = mfma32x32x16(*reinterpret_cast<const u32x4*>(qs + off), kf[kk], s[rb]);
+              dp[rb] = mfma32x32x16(*reinterpret_cast<const u32x4*>(dos + off), vf[kk], dp[rb]);
+            }
+          }
+          // keep three k-steps of operands in flight: LDS latency is several
+          // times one MFMA pair, and this wave is alone on its SIMD
+          pipeline_reads_mfma<6, 4 * KK>();
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+            dkdv_rows<D, CAUSAL, SPLIT>(qs, dos, lses, dls, s[rb], dp[rb], rb, t0, u, key_ok, hh, lane, p.c, dka,
+                                        dva);
         }
         wait_vmem();
         __syncthreads();
@@ -402,6 +412,7 @@ __device__ __forceinline__ void dq_half(const uint8_t* ks, const uint8_t* vs, co
     s = mfma32x32x16(*reinterpret_cast<const u32x4*>(ks + off), qf[kk], s);
     dp = mfma32x32x16(*reinterpret_cast<const u32x4*>(vs + off), df[kk], dp);
   }
+  pipeline_reads_mfma<6, 2 * KK>();   // three k-steps of K/V rows in flight
   float ds[16];
   // element i is key row C_i = (i/4)*8 + i%4 of the half (plus 4hh)
 #pragma unroll
@@ -434,6 +445,7 @@ __device__ __forceinline__ void dq_half(const uint8_t* ks, const uint8_t* vs, co
       if (SPLIT) dqa[j] = mfma32x32x16(a, dlo[f], dqa[j]);
     }
   }
+  if (!SPLIT) pipeline_tr_reads_mfma<3, 2 * DJ>();
 }
 
 template <int D, bool HAS_MASK, bool CAUSAL>

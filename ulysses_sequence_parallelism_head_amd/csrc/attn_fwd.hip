@@ -273,6 +273,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const FwdPar
             if (SPLIT) oacc[j] = mfma32x32x16(a, plo[f], oacc[j]);
           }
         }
+        if (!SPLIT) pipeline_tr_reads_mfma<4, 4 * DJ>();
       }
 
       if (HAS_MASK && it + 1 < ntiles && tid < kBN) nxt[L::kBytesK + L::kBytesV + tid] = uint8_t(vbyte);

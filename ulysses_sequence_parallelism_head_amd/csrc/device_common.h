@@ -145,6 +145,21 @@ __device__ __forceinline__ void pipeline_reads_mfma() {
   __builtin_amdgcn_sched_group_barrier(kMaskMfma, AHEAD, 0);
 }
 
+// The same for MFMAs whose A operand takes two LDS reads (the transposing
+// reads): reads for AHEAD MFMAs first, then one MFMA and its two reads at a
+// time, then the last AHEAD MFMAs (2N reads, N MFMAs).
+template <int AHEAD, int N>
+__device__ __forceinline__ void pipeline_tr_reads_mfma() {
+  constexpr int kMaskMfma = 0x008, kMaskDsRead = 0x100;
+  __builtin_amdgcn_sched_group_barrier(kMaskDsRead, 2 * AHEAD, 0);
+#pragma unroll
+  for (int i = 0; i < N - AHEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kMaskMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kMaskDsRead, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kMaskMfma, AHEAD, 0);
+}
+
 // ---- direct global -> LDS staging (buffer loads with the LDS destination)
 //
 // One buffer_load ... lds instruction moves 16 (or 4) bytes per lane from
