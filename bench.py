@@ -23,6 +23,7 @@ Prints ONE JSON line on stdout.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -36,6 +37,33 @@ if ROOT not in sys.path:
 
 MFMA_BF16_PEAK_TFLOPS = 2516.6     # 256 CU x 4096 flop/clk x 2.4 GHz (dense)
 HBM_PEAK_GBS = 8000.0
+
+# HBM bytes per launch of each attention call at this workload, from rocprofv3
+# FETCH_SIZE and WRITE_SIZE passes (scaled by a 512 MiB copy calibration; the
+# summary is under profiles/), valid only for the kernel sources they were
+# measured on: the roofline reports null traffic once those sources change.
+CSRC = os.path.join(ROOT, "ulysses_sequence_parallelism_head_amd", "csrc")
+MEASURED_TRAFFIC = {
+    "attn_bwd": {"bytes": 6.457e9, "sources": ("attn_bwd.hip", "device_common.h", "internal.h"),
+                 "sha256": "b7dd1b646b688d6f6aa791bc3ac4d7249a4b083928a33aa5d964fe7eef4ad6ca"},
+    "attn_fwd": {"bytes": 2.937e9, "sources": ("attn_fwd.hip", "device_common.h", "internal.h"),
+                 "sha256": "4de5746b63c68cc95f396649114ae85c42aa04127b15a9778c6a75a9a4164091"},
+}
+
+
+def sources_sha256(names) -> str:
+    h = hashlib.sha256()
+    for name in names:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(call: str):
+    m = MEASURED_TRAFFIC.get(call)
+    if m is None or sources_sha256(m["sources"]) != m["sha256"]:
+        return None
+    return m["bytes"]
 
 
 def log(*a):
@@ -215,7 +243,8 @@ def main():
     dom_flops = fwd_flops if dom == "attn_fwd" else bwd_flops
     achieved = dom_flops / (avg[dom] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": measured_traffic(dom)}
 
     result = {
         "metric": "causal attn TFLOP/s @64K, 8q/2kv heads d128 bf16; % MFMA peak; repack GB/s",
