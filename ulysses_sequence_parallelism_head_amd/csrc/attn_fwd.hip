@@ -164,10 +164,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const FwdPar
     wait_vmem();
     __syncthreads();
 
-    for (int it = 0; it < ntiles; ++it) {
-      // prefetch tile it+1 into the other buffer while computing on this one
-      uint8_t* cur = smem + (it & 1) * L::kStageAligned;
-      uint8_t* nxt = smem + ((it + 1) & 1) * L::kStageAligned;
+    // one tile: prefetch tile it+1 into `nxt` while computing on `cur`.  The
+    // loop below is unrolled by two so each copy names its buffers
+    // statically and every LDS address folds the buffer into the
+    // instruction's immediate offset.
+    auto tile = [&](int it, uint8_t* cur, uint8_t* nxt) {
       if (it + 1 < ntiles) fwd_issue<D, HAS_MASK>(nxt, vbyte, p, b, kvh, it + 1, wave, lane, tid);
 
       const int tile0 = it * kBN;
@@ -279,7 +280,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const FwdPar
       if (HAS_MASK && it + 1 < ntiles && tid < kBN) nxt[L::kBytesK + L::kBytesV + tid] = uint8_t(vbyte);
       wait_vmem();
       __syncthreads();
+    };
+    int it = 0;
+    for (; it + 1 < ntiles; it += 2) {
+      tile(it, smem, smem + L::kStageAligned);
+      tile(it + 1, smem + L::kStageAligned, smem);
     }
+    if (it < ntiles) tile(it, smem, smem + L::kStageAligned);
 
     // ---- epilogue: normalise, write O (row t, dims 32j + 8*(i/4) + 4hh + i%4) and LSE
     if (t < p.n) {
