@@ -204,21 +204,9 @@ __device__ __forceinline__ i32x4 uniform_rsrc(const i32x4 r) {
 }
 
 __device__ __forceinline__ uint32_t lds_addr(uint8_t* lds) {
-  return __builtin_amdgcn_readfirstlane(uint32_t(uintptr_t((lds_u8_ptr)lds)));
-}
-
-// 16 bytes per lane: global rsrc + voffset -> LDS lds + 16 * lane
-__device__ __forceinline__ void dma16(const i32x4 rsrc, uint8_t* lds, int voffset) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds_addr(lds)), "v"(voffset), "s"(uniform_rsrc(rsrc))
-      : "memory");
+  // the low 32 bits of a flat address in the LDS aperture are the LDS offset
+  // (an address-space cast would add a null check to every call)
+  return __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>(lds)));
 }
 
 // 4 bytes per lane: global rsrc + voffset -> LDS lds + 4 * lane
@@ -243,10 +231,53 @@ __device__ __forceinline__ void dma4(const i32x4 rsrc, uint8_t* lds, int voffset
 // own in the loop that follows (one that would also stall on the prefetch).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Two or four 16-byte-per-lane loads in one asm statement (one M0 save and
+// restore): load u reads rsrc + vo[u] into LDS m0[u] + 16 * lane.
+__device__ __forceinline__ void dma16x2(const i32x4 rsrc, const uint32_t (&m0)[2], const int (&vo)[2]) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %3, %5, 0 offen lds\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %4, %5, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(m0[0]), "s"(m0[1]), "v"(vo[0]), "v"(vo[1]), "s"(uniform_rsrc(rsrc))
+      : "memory");
+}
+
+__device__ __forceinline__ void dma16x4(const i32x4 rsrc, const uint32_t (&m0)[4], const int (&vo)[4]) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %5, %9, 0 offen lds\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %6, %9, 0 offen lds\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %7, %9, 0 offen lds\n\t"
+      "s_mov_b32 m0, %4\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %8, %9, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(m0[0]), "s"(m0[1]), "s"(m0[2]), "s"(m0[3]), "v"(vo[0]), "v"(vo[1]), "v"(vo[2]), "v"(vo[3]),
+        "s"(uniform_rsrc(rsrc))
+      : "memory");
+}
+
 // DMA a ROWS x D bf16 tile, rows row0.. of a row-major tensor whose rows are
 // row_stride_bytes apart, into the swizzled LDS layout of rm_off.  `rows_ok`
 // rows hold data; the rest of the tile is zero-filled.  Every wave of the
 // workgroup calls this with its wave index; together they cover the tile.
+// Load u of this wave writes the tile's 1 KB block u * NWAVES + wave, 16
+// bytes per lane, at the row and (swizzled) chunk that block position holds.
 template <int D, int ROWS, int NWAVES>
 __device__ __forceinline__ void dma_tile(uint8_t* lds_tile, const uint16_t* row0, int row_stride_bytes, int rows_ok,
                                          int wave, int lane) {
@@ -254,15 +285,22 @@ __device__ __forceinline__ void dma_tile(uint8_t* lds_tile, const uint16_t* row0
   constexpr int ROW_BYTES = 2 * D;
   constexpr int PER_WAVE = ROWS * NC / (64 * NWAVES);
   static_assert(ROWS * NC % (64 * NWAVES) == 0, "tile must split evenly across the waves");
+  static_assert(PER_WAVE == 2 || PER_WAVE == 4, "two or four loads per wave");
   const i32x4 rsrc = buffer_rsrc(row0, uint32_t(rows_ok > 0 ? rows_ok : 0) * uint32_t(row_stride_bytes));
+  const uint32_t base = lds_addr(lds_tile);
+  uint32_t m0[PER_WAVE];
+  int vo[PER_WAVE];
 #pragma unroll
   for (int u = 0; u < PER_WAVE; ++u) {
-    const int blk = u * NWAVES + wave;           // 1 KB block of the tile written by this instruction
+    const int blk = u * NWAVES + wave;
     const int pos = blk * 64 + lane;             // physical chunk position
     const int r = pos / NC;
     const int c = (pos % NC) ^ rm_swz<ROW_BYTES>(r);
-    dma16(rsrc, lds_tile + blk * 1024, r * row_stride_bytes + c * 16);
+    m0[u] = base + uint32_t(blk) * 1024u;
+    vo[u] = r * row_stride_bytes + c * 16;
   }
+  if constexpr (PER_WAVE == 4) dma16x4(rsrc, m0, vo);
+  else dma16x2(rsrc, m0, vo);
 }
 
 }  // namespace ulysses
