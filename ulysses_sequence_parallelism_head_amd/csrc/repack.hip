@@ -23,7 +23,7 @@ namespace ulysses {
 
 namespace {
 
-constexpr int kRepackThreads = 256;
+constexpr int kRepackThreads = 64;     // measured best for both directions at 512 MiB
 constexpr int kRepackUnroll = 4;     // vectors in flight per thread
 
 template <typename V>
