@@ -239,10 +239,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const FwdPar
         const float neg_m = (m_ref == -INFINITY) ? 0.f : -m_ref;
         float pr[32];
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          pr[i] = __builtin_amdgcn_exp2f(fmaf(x[i], p.c, neg_m));
-          lsum += pr[i];
-        }
+        for (int i = 0; i < 32; ++i) pr[i] = __builtin_amdgcn_exp2f(fmaf(x[i], p.c, neg_m));
 
         // ---- P^T as B operand: per half-tile and 16-key slice f, the lane's 8 scores
         u32x4 phi[4], plo[4];
@@ -260,6 +257,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const FwdPar
             }
             plo[f] = u32x4{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]), pack_bf16x2(r[4], r[5]),
                            pack_bf16x2(r[6], r[7])};
+          }
+          // row sum of exactly the rounded weights the PV product uses (so O is
+          // a normalised combination of V rows): two bf16 per dot2 instruction
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            lsum = sum_bf16x2(phi[f][e], lsum);
+            if (SPLIT) lsum = sum_bf16x2(plo[f][e], lsum);
           }
         }
 
