@@ -41,8 +41,22 @@ floor(h / (Hq/Hkv)); the causal mask is on global positions with the
 diagonal included; padding keys are excluded from every softmax, padding
 query rows are computed like any other row.
 
+Packed documents ([ALST] section "Integrarea cu Transformers Trainer și TRL
+SFTTrainer" names the trainer's switch for variable sequence lengths, not
+the mask it implies).  The reading taken: a packed sequence holds several
+documents back to back and a token attends only to earlier tokens of its
+own document.  The documents are given per token by ``doc_start[b][t]``,
+the position of the first token of t's document (pad tokens after a
+document belong to it), and the allowed set above gains one condition:
+
+  K_t = { u : doc_start[b][t] <= u, (u <= t if causal) and valid[b][u] }
+
+Every formula above is unchanged.  Nothing here assumes the documents are
+contiguous or the array monotone: the condition is applied as written.
+
 Layouts: q, o ``[B][n][Hq][D]``; k, v ``[B][n][Hkv][D]``; lse ``[B][Hq][n]``;
-key_valid ``[B][n]`` (nonzero = valid) or None.  All arithmetic is float64.
+key_valid ``[B][n]`` (nonzero = valid) or None; doc_start ``[B][n]`` integer
+or None.  All arithmetic is float64.
 """
 from __future__ import annotations
 
@@ -66,7 +80,7 @@ def kv_head_of(h: int, Hq: int, Hkv: int) -> int:
     return h // (Hq // Hkv)
 
 
-def allowed_mask(rows: np.ndarray, n_keys: int, causal: bool, valid_b) -> np.ndarray:
+def allowed_mask(rows: np.ndarray, n_keys: int, causal: bool, valid_b, doc_b=None) -> np.ndarray:
     """Boolean [len(rows)][n_keys]: key u is allowed for query row t."""
     keys = np.arange(n_keys)
     if causal:
@@ -75,7 +89,13 @@ def allowed_mask(rows: np.ndarray, n_keys: int, causal: bool, valid_b) -> np.nda
         m = np.ones((rows.size, n_keys), dtype=bool)
     if valid_b is not None:
         m = m & (np.asarray(valid_b[:n_keys]) != 0)[None, :]
+    if doc_b is not None:
+        m = m & (keys[None, :] >= np.asarray(doc_b, dtype=np.int64)[rows][:, None])
     return m
+
+
+def _doc(doc_start, b):
+    return None if doc_start is None else doc_start[b]
 
 
 def _workers(workers):
@@ -132,7 +152,7 @@ def _softmax_rows(S: np.ndarray, allow: np.ndarray):
 
 
 def attn_fwd(q, k, v, scale: float, causal: bool = True, key_valid=None, rows=None,
-             block: int = DEFAULT_BLOCK, workers=None):
+             block: int = DEFAULT_BLOCK, workers=None, doc_start=None):
     """Forward attention.  Returns ``(O, LSE)`` in float64.
 
     ``rows``: optional sorted query-row indices; then ``O`` is
@@ -164,7 +184,7 @@ def attn_fwd(q, k, v, scale: float, causal: bool = True, key_valid=None, rows=No
         qh, kh, vh = head_arrays(b, h)
         t = rows[r0:r0 + block]
         n_keys = int(t.max()) + 1 if causal else n
-        allow = allowed_mask(t, n_keys, causal, None if key_valid is None else key_valid[b])
+        allow = allowed_mask(t, n_keys, causal, None if key_valid is None else key_valid[b], _doc(doc_start, b))
         S = scale * (qh[t] @ kh[:n_keys].T)
         w, m, L = _softmax_rows(S, allow)
         with np.errstate(divide="ignore", invalid="ignore"):
@@ -179,12 +199,12 @@ def attn_fwd(q, k, v, scale: float, causal: bool = True, key_valid=None, rows=No
 
 
 def attn_bwd(q, k, v, dout, scale: float, causal: bool = True, key_valid=None,
-             block: int = DEFAULT_BLOCK, workers=None):
+             block: int = DEFAULT_BLOCK, workers=None, doc_start=None):
     """Full backward.  Returns ``(dQ, dK, dV, O, LSE)`` in float64."""
     B, n, Hq, Hkv, D = _check(q, k, v)
     if dout.shape != q.shape:
         raise ValueError("dout must have q's shape")
-    O, LSE = attn_fwd(q, k, v, scale, causal, key_valid, block=block, workers=workers)
+    O, LSE = attn_fwd(q, k, v, scale, causal, key_valid, block=block, workers=workers, doc_start=doc_start)
     dQ = np.zeros((B, n, Hq, D), dtype=np.float64)
     dK = np.zeros((B, n, Hkv, D), dtype=np.float64)
     dV = np.zeros((B, n, Hkv, D), dtype=np.float64)
@@ -200,7 +220,7 @@ def attn_bwd(q, k, v, dout, scale: float, causal: bool = True, key_valid=None,
         kb = np.ascontiguousarray(k[b, :n_keys, g, :], dtype=np.float64)
         vb = np.ascontiguousarray(v[b, :n_keys, g, :], dtype=np.float64)
         dob = np.ascontiguousarray(dout[b, t, h, :], dtype=np.float64)
-        allow = allowed_mask(t, n_keys, causal, None if key_valid is None else key_valid[b])
+        allow = allowed_mask(t, n_keys, causal, None if key_valid is None else key_valid[b], _doc(doc_start, b))
         S = scale * (qb @ kb.T)
         lse = LSE[b, h, t]
         lse_safe = np.where(np.isfinite(lse), lse, 0.0)
@@ -223,7 +243,7 @@ def attn_bwd(q, k, v, dout, scale: float, causal: bool = True, key_valid=None,
 
 
 def attn_bwd_sampled(q, k, v, dout, scale: float, causal: bool = True, key_valid=None,
-                     q_rows=None, k_rows=None, block: int = DEFAULT_BLOCK, workers=None):
+                     q_rows=None, k_rows=None, block: int = DEFAULT_BLOCK, workers=None, doc_start=None):
     """Backward at selected rows only.
 
     ``dQ`` at query rows ``q_rows`` (``[B][len(q_rows)][Hq][D]``) and ``dK``/``dV``
@@ -240,7 +260,8 @@ def attn_bwd_sampled(q, k, v, dout, scale: float, causal: bool = True, key_valid
     dV = np.zeros((B, k_rows.size, Hkv, D))
 
     if q_rows.size:
-        Oq, Lq = attn_fwd(q, k, v, scale, causal, key_valid, rows=q_rows, block=block, workers=workers)
+        Oq, Lq = attn_fwd(q, k, v, scale, causal, key_valid, rows=q_rows, block=block, workers=workers,
+                          doc_start=doc_start)
         tasks = [(b, h) for b in range(B) for h in range(Hq)]
 
         def work_q(task):
@@ -252,7 +273,7 @@ def attn_bwd_sampled(q, k, v, dout, scale: float, causal: bool = True, key_valid
             vb = np.ascontiguousarray(v[b, :n_keys, g, :], dtype=np.float64)
             qb = np.ascontiguousarray(q[b, t, h, :], dtype=np.float64)
             dob = np.ascontiguousarray(dout[b, t, h, :], dtype=np.float64)
-            allow = allowed_mask(t, n_keys, causal, None if key_valid is None else key_valid[b])
+            allow = allowed_mask(t, n_keys, causal, None if key_valid is None else key_valid[b], _doc(doc_start, b))
             S = scale * (qb @ kb.T)
             lse = Lq[b, h]
             lse_safe = np.where(np.isfinite(lse), lse, 0.0)
@@ -268,7 +289,8 @@ def attn_bwd_sampled(q, k, v, dout, scale: float, causal: bool = True, key_valid
     if k_rows.size:
         r0 = int(k_rows.min()) if causal else 0
         t_all = np.arange(r0, n, dtype=np.int64)
-        Ot, Lt = attn_fwd(q, k, v, scale, causal, key_valid, rows=t_all, block=block, workers=workers)
+        Ot, Lt = attn_fwd(q, k, v, scale, causal, key_valid, rows=t_all, block=block, workers=workers,
+                          doc_start=doc_start)
         tasks = [(b, h) for b in range(B) for h in range(Hq)]
 
         def work_k(task):
@@ -284,6 +306,8 @@ def attn_bwd_sampled(q, k, v, dout, scale: float, causal: bool = True, key_valid
                 allow &= k_rows[None, :] <= t_all[:, None]
             if key_valid is not None:
                 allow &= (np.asarray(key_valid[b])[k_rows] != 0)[None, :]
+            if doc_start is not None:
+                allow &= k_rows[None, :] >= np.asarray(doc_start[b], dtype=np.int64)[t_all][:, None]
             S = scale * (qb @ ku.T)                       # [t][u]
             lse = Lt[b, h]
             lse_safe = np.where(np.isfinite(lse), lse, 0.0)

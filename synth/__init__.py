@@ -1,8 +1,9 @@
 """Seeded synthetic inputs shared by the tests, the bench and the smoke check.
 
 This module holds none of the method's arithmetic: it draws random numbers,
-rounds them to bfloat16 storage, and builds the key-validity vector of a
-packed sequence of variable-length documents.  Both the HIP path and the
+rounds them to bfloat16 storage, and builds the key-validity vector and the
+per-token document starts of a packed sequence of variable-length
+documents.  Both the HIP path and the
 CPU oracle receive exactly these arrays, so the two sides never share any
 step of the computation itself.
 
@@ -67,17 +68,20 @@ def random_bits(gen: np.random.Generator, shape) -> np.ndarray:
     return gen.integers(0, 1 << 16, size=shape, dtype=np.uint16)
 
 
-def document_valid(gen: np.random.Generator, n: int, pad_multiple: int, max_len: int) -> tuple[np.ndarray, list[int]]:
-    """Key-validity vector of a packed sequence of variable-length documents.
+def documents(gen: np.random.Generator, n: int, pad_multiple: int, max_len: int):
+    """A packed sequence of variable-length documents.
 
     Document lengths L ~ U{1..max_len}; each document is followed by
     ``(-L) mod pad_multiple`` pad tokens (padding to a multiple of the
     number of shards).  Packing stops at the first document that no longer
     fits; it is truncated to fill the sequence exactly, with no pad after it.
-    Returns ``valid`` (uint8, 1 = real token) and the list of document
-    lengths as packed.
+    Returns ``(valid, doc_start, lengths)``: ``valid`` (uint8, 1 = real
+    token), ``doc_start`` (int32, the position of the first token of each
+    token's document; a document's pad tokens belong to it) and the list of
+    document lengths as packed.
     """
     valid = np.zeros(n, dtype=np.uint8)
+    doc_start = np.zeros(n, dtype=np.int32)
     pos = 0
     lengths: list[int] = []
     while pos < n:
@@ -87,8 +91,15 @@ def document_valid(gen: np.random.Generator, n: int, pad_multiple: int, max_len:
             L = n - pos
             pad = 0
         valid[pos:pos + L] = 1
+        doc_start[pos:pos + L + pad] = pos
         lengths.append(L)
         pos += L + pad
+    return valid, doc_start, lengths
+
+
+def document_valid(gen: np.random.Generator, n: int, pad_multiple: int, max_len: int) -> tuple[np.ndarray, list[int]]:
+    """Key-validity vector and document lengths of :func:`documents` (same draws)."""
+    valid, _, lengths = documents(gen, n, pad_multiple, max_len)
     return valid, lengths
 
 
@@ -194,8 +205,9 @@ def local_attention_inputs(c: int, n: int | None = None, with_grad: bool = False
     if with_grad or w.backward:
         out["do"] = draw(g[STREAM_DO], shp_q)
     if w.docs:
-        valid, lengths = document_valid(g[STREAM_DOCS], n, w.P, min(DOC_MAX_LEN, n))
+        valid, doc_start, lengths = documents(g[STREAM_DOCS], n, w.P, min(DOC_MAX_LEN, n))
         out["valid"] = valid.reshape(1, n)
+        out["doc_start"] = doc_start.reshape(1, n)
         out["doc_lengths"] = lengths
     out["row_gen"] = g[STREAM_ROWS]
     return out

@@ -2,7 +2,8 @@
 
 Each mutation replaces one helper of ``oracle.attention`` with a plausible
 wrong version (an off-by-one mask, a wrong head mapping, a dropped mask in
-the normaliser, a logsumexp without the row max, a wrong padding rule) and checks that
+the normaliser, a logsumexp without the row max, a wrong padding rule, a
+document mask dropped, off by one or indexed by the key) and checks that
 the independent references -- brute force, the worked example, torch SDPA --
 then disagree with it.
 """
@@ -13,6 +14,7 @@ import pytest
 
 import oracle.attention as oa
 from tests.test_oracle_attention import brute_fwd, torch_ref, make_valid, rnd
+from tests.test_oracle_docs import brute_docs_fwd, doc_ids_from_lengths, starts_from_lengths, torch_docs_ref
 
 
 def _pins_fail(golden):
@@ -34,32 +36,77 @@ def _pins_fail(golden):
             return True
         ref = torch_ref(q, k, v, do, 0.5, True, valid)
         dq, dk, dv, _, _ = oa.attn_bwd(q, k, v, do, 0.5, True, valid)
+        if not (np.allclose(dq, ref["dq"], atol=1e-10) and np.allclose(dk, ref["dk"], atol=1e-10)
+                and np.allclose(dv, ref["dv"], atol=1e-10)):
+            return True
+        # packed documents: brute force and torch SDPA with the block-diagonal causal mask
+        lengths = [4, 1, 6, 3]
+        n = sum(lengths)
+        q, k, v, do = rnd(6, 1, n, Hq, D), rnd(7, 1, n, Hkv, D), rnd(8, 1, n, Hkv, D), rnd(9, 1, n, Hq, D)
+        valid = make_valid(10, 1, n)
+        ds = starts_from_lengths(lengths).reshape(1, n)
+        ids = doc_ids_from_lengths(lengths).reshape(1, n)
+        O, L = oa.attn_fwd(q, k, v, 0.5, True, valid, doc_start=ds)
+        Ob, Lb = brute_docs_fwd(q, k, v, 0.5, ids, valid)
+        if not (np.allclose(O, Ob, atol=1e-12) and np.array_equal(np.isneginf(L), np.isneginf(Lb))
+                and np.allclose(L[np.isfinite(Lb)], Lb[np.isfinite(Lb)], atol=1e-12)):
+            return True
+        ref = torch_docs_ref(q, k, v, do, 0.5, ids, valid)
+        dq, dk, dv, _, _ = oa.attn_bwd(q, k, v, do, 0.5, True, valid, doc_start=ds)
         return not (np.allclose(dq, ref["dq"], atol=1e-10) and np.allclose(dk, ref["dk"], atol=1e-10)
                     and np.allclose(dv, ref["dv"], atol=1e-10))
     except Exception:
         return True
 
 
-def _mask_including_next(rows, n_keys, causal, valid_b):
+def _docs(m, rows, n_keys, doc_b):
+    """The correct document condition, for mutations that change something else."""
+    if doc_b is None:
+        return m
+    return m & (np.arange(n_keys)[None, :] >= np.asarray(doc_b, dtype=np.int64)[rows][:, None])
+
+
+def _mask_including_next(rows, n_keys, causal, valid_b, doc_b=None):
     keys = np.arange(n_keys)
     m = keys[None, :] <= rows[:, None] + 1 if causal else np.ones((rows.size, n_keys), bool)
     if valid_b is not None:
         m = m & (np.asarray(valid_b[:n_keys]) != 0)[None, :]
-    return m
+    return _docs(m, rows, n_keys, doc_b)
 
 
-def _mask_ignoring_valid(rows, n_keys, causal, valid_b):
+def _mask_ignoring_valid(rows, n_keys, causal, valid_b, doc_b=None):
     keys = np.arange(n_keys)
-    return keys[None, :] <= rows[:, None] if causal else np.ones((rows.size, n_keys), bool)
+    m = keys[None, :] <= rows[:, None] if causal else np.ones((rows.size, n_keys), bool)
+    return _docs(m, rows, n_keys, doc_b)
 
 
-def _mask_query_padding(rows, n_keys, causal, valid_b):
+def _mask_query_padding(rows, n_keys, causal, valid_b, doc_b=None):
     """Wrong padding rule: masks the query's own validity instead of the key's."""
     keys = np.arange(n_keys)
     m = keys[None, :] <= rows[:, None] if causal else np.ones((rows.size, n_keys), bool)
     if valid_b is not None:
         m = m & (np.asarray(valid_b)[rows] != 0)[:, None]
-    return m
+    return _docs(m, rows, n_keys, doc_b)
+
+
+def _mask_ignoring_documents(rows, n_keys, causal, valid_b, doc_b=None):
+    return _orig_mask(rows, n_keys, causal, valid_b, None)
+
+
+def _mask_document_start_excluded(rows, n_keys, causal, valid_b, doc_b=None):
+    """Off by one at the document boundary: the document's first token is dropped."""
+    m = _orig_mask(rows, n_keys, causal, valid_b, None)
+    if doc_b is None:
+        return m
+    return m & (np.arange(n_keys)[None, :] > np.asarray(doc_b, dtype=np.int64)[rows][:, None])
+
+
+def _mask_document_of_key(rows, n_keys, causal, valid_b, doc_b=None):
+    """Transposed index: compares the row with the key's document start."""
+    m = _orig_mask(rows, n_keys, causal, valid_b, None)
+    if doc_b is None:
+        return m
+    return m & (rows[:, None] >= np.asarray(doc_b, dtype=np.int64)[:n_keys][None, :])
 
 
 def _softmax_unmasked_sum(S, allow):
@@ -76,6 +123,7 @@ def _softmax_lse_drops_max(S, allow):
 
 
 _orig_softmax = oa._softmax_rows
+_orig_mask = oa.allowed_mask
 
 
 MUTATIONS = {
@@ -83,6 +131,9 @@ MUTATIONS = {
     "mask_off_by_one": ("allowed_mask", _mask_including_next),
     "mask_ignores_padding": ("allowed_mask", _mask_ignoring_valid),
     "mask_query_padding": ("allowed_mask", _mask_query_padding),
+    "mask_ignores_documents": ("allowed_mask", _mask_ignoring_documents),
+    "mask_drops_document_start": ("allowed_mask", _mask_document_start_excluded),
+    "mask_document_of_key": ("allowed_mask", _mask_document_of_key),
     "normaliser_unmasked": ("_softmax_rows", _softmax_unmasked_sum),
     "lse_drops_max": ("_softmax_rows", _softmax_lse_drops_max),
 }

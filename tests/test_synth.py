@@ -46,3 +46,20 @@ def test_local_inputs_shapes():
     assert d4["valid"].shape == (1, 1024) and "do" in d4
     d1 = synth.local_attention_inputs(1)
     assert d1["q"].dtype == np.float32 and d1["q"].shape == (1, 256, 2, 64)
+
+
+def test_document_starts_follow_the_packing():
+    n, P = 98304, 4
+    valid, doc_start, lengths = synth.documents(synth.streams(4)[synth.STREAM_DOCS], n, P, synth.DOC_MAX_LEN)
+    v2, l2 = synth.document_valid(synth.streams(4)[synth.STREAM_DOCS], n, P, synth.DOC_MAX_LEN)
+    assert np.array_equal(valid, v2) and lengths == l2
+    assert doc_start.dtype == np.int32 and doc_start.shape == (n,)
+    t = np.arange(n)
+    assert np.all(doc_start <= t) and np.all(np.diff(doc_start) >= 0)
+    # each document (with its pad) is one run whose start is its first position
+    pos = 0
+    for L in lengths:
+        span = L + ((-L) % P if pos + L < n else 0)
+        assert np.all(doc_start[pos:pos + span] == pos)
+        pos += span
+    assert pos == n
