@@ -17,7 +17,13 @@ head for the forward, 10*D for the backward) divided by the measured step
 time.  Per-call durations come from HIP events recorded on the stream the
 library launches on (torch's current stream).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+With ``--workload 4`` the step runs the 96K documents workload (n = 98304,
+padding keys masked); adding ``--docs`` also applies the document mask (a
+token sees only earlier tokens of its own document, the ``*_docs`` calls),
+so the work is the tokens' own documents' pairs.  The flop count is always
+that of the visible (query, key) pairs, counted exactly from the masks.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C] [--docs] [--no-cpu-baseline]
 Prints ONE JSON line on stdout.
 """
 from __future__ import annotations
@@ -43,10 +49,10 @@ HBM_PEAK_GBS = 8000.0
 # summary is under profiles/), valid only for the kernel sources they were
 # measured on: the roofline reports null traffic once those sources change.
 CSRC = os.path.join(ROOT, "ulysses_sequence_parallelism_head_amd", "csrc")
-MEASURED_TRAFFIC = {
-    "attn_bwd": {"bytes": 6.515e9, "sources": ("attn_bwd.hip", "device_common.h", "internal.h"),
+MEASURED_TRAFFIC = {      # keyed by (call, workload name)
+    ("attn_bwd", "gqa-n65536-8q2kv-d128-bf16-fwd+repack"): {"bytes": 6.515e9, "sources": ("attn_bwd.hip", "device_common.h", "internal.h"),
                  "sha256": "e74095a5acdfd659993bbdcca95552639bbbb1c0884df0801237ea93ff1fe7cf"},
-    "attn_fwd": {"bytes": 4.426e9, "sources": ("attn_fwd.hip", "device_common.h", "internal.h"),
+    ("attn_fwd", "gqa-n65536-8q2kv-d128-bf16-fwd+repack"): {"bytes": 4.426e9, "sources": ("attn_fwd.hip", "device_common.h", "internal.h"),
                  "sha256": "e8eb0fdda703015bea134c5e2744855f1b22a3469b90c4f616a11355c553965a"},
 }
 
@@ -59,8 +65,8 @@ def sources_sha256(names) -> str:
     return h.hexdigest()
 
 
-def measured_traffic(call: str):
-    m = MEASURED_TRAFFIC.get(call)
+def measured_traffic(call: str, workload: str):
+    m = MEASURED_TRAFFIC.get((call, workload))
     if m is None or sources_sha256(m["sources"]) != m["sha256"]:
         return None
     return m["bytes"]
@@ -70,11 +76,16 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def causal_pairs(n: int) -> int:
-    return n * (n + 1) // 2
+def visible_keys(n: int, valid=None, doc_start=None) -> np.ndarray:
+    """Per query row, the number of keys it sees: u <= t, valid[u], and
+    u >= doc_start[t] when documents are given."""
+    cv = np.zeros(n + 1, dtype=np.int64)
+    cv[1:] = np.cumsum(np.ones(n, np.int64) if valid is None else (np.asarray(valid).reshape(n) != 0))
+    lo = np.zeros(n, np.int64) if doc_start is None else np.asarray(doc_start, np.int64).reshape(n)
+    return cv[1:] - cv[lo]
 
 
-def cpu_baseline(workload, budget_s: float = 12.0):
+def cpu_baseline(workload, docs: bool, budget_s: float = 12.0):
     """The oracle (as it stands) on a bounded sample of the same workload:
     full causal forward rows at seeded positions, timed on the host cores."""
     import oracle
@@ -84,6 +95,9 @@ def cpu_baseline(workload, budget_s: float = 12.0):
     q = synth.bf16_bits_to_f64(d["q"])
     k = synth.bf16_bits_to_f64(d["k"])
     v = synth.bf16_bits_to_f64(d["v"])
+    valid = d["valid"]
+    ds = d.get("doc_start") if docs else None
+    seen = visible_keys(w.n, None if valid is None else valid[0], None if ds is None else ds[0])
     gen = np.random.Generator(np.random.PCG64(12345))
     workers = oracle.attention._workers(None)
     done_rows, flops, spent = 0, 0.0, 0.0
@@ -91,12 +105,13 @@ def cpu_baseline(workload, budget_s: float = 12.0):
     while spent < budget_s:
         rows = np.sort(gen.choice(w.n, size=batch, replace=False))
         t0 = time.perf_counter()
-        oracle.attn_fwd(q, k, v, w.scale, True, rows=rows, block=16, workers=workers)
+        oracle.attn_fwd(q, k, v, w.scale, True, valid, rows=rows, block=16, workers=workers, doc_start=ds)
         spent += time.perf_counter() - t0
-        flops += float(4 * w.D * w.hq * np.sum(rows + 1))
+        flops += float(4 * w.D * w.hq * np.sum(seen[rows]))
         done_rows += batch
+    kind = "document-masked causal" if docs else "causal"
     return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
-            "sample": f"{done_rows} seeded query rows x {w.hq} heads of the n={w.n} causal forward "
+            "sample": f"{done_rows} seeded query rows x {w.hq} heads of the n={w.n} {kind} forward "
                       f"(fp64 NumPy, {spent:.1f} s)"}
 
 
@@ -106,6 +121,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--docs", action="store_true",
+                    help="document-masked attention (workloads with packed documents only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time only a plain 512 MiB device-to-device copy (torch copy_), the reference kernel "
@@ -142,6 +159,9 @@ def main():
     w = synth.WORKLOADS[args.workload]
     P, nl, n, D = w.P, w.n_local, w.n, w.D
     hq, hkv = w.hq, w.hkv
+    if args.docs and not w.docs:
+        print(f"--docs needs a workload with packed documents (workload {w.number} has none)", file=sys.stderr)
+        sys.exit(2)
 
     log(f"[bench] generating workload {w.name}")
     g = synth.streams(w.number)
@@ -153,6 +173,13 @@ def main():
     k_seq = dev_bits(synth.normal_bf16(g[synth.STREAM_K], (P, 1, nl, w.Hkv_global, D)))
     v_seq = dev_bits(synth.normal_bf16(g[synth.STREAM_V], (P, 1, nl, w.Hkv_global, D)))
     do_seq = dev_bits(synth.normal_bf16(g[synth.STREAM_DO], (P, 1, nl, w.Hq_global, D)))
+    # packed documents (global positions, the same on every rank after the exchange)
+    valid_np = ds_np = valid_t = ds_t = None
+    if w.docs:
+        valid_np, ds_np, _ = synth.documents(g[synth.STREAM_DOCS], n, P, min(synth.DOC_MAX_LEN, n))
+        valid_t = torch.from_numpy(valid_np.reshape(1, n)).to(dev)
+        if args.docs:
+            ds_t = torch.from_numpy(ds_np.reshape(1, n)).to(dev)
 
     # buffers (allocated once; the library allocates nothing)
     bf, f32 = torch.bfloat16, torch.float32
@@ -183,12 +210,19 @@ def main():
         U.ulysses_repack_seq2head(k_seq, k_h)
         U.ulysses_repack_seq2head(v_seq, v_h)
         mark(1)
-        U.ulysses_attn_fwd(q_h[0], k_h[0], v_h[0], None, w.scale, True, out=o_h[0], lse=lse)
+        if ds_t is None:
+            U.ulysses_attn_fwd(q_h[0], k_h[0], v_h[0], valid_t, w.scale, True, out=o_h[0], lse=lse)
+        else:
+            U.ulysses_attn_fwd_docs(q_h[0], k_h[0], v_h[0], ds_t, valid_t, w.scale, out=o_h[0], lse=lse)
         mark(2)
         U.ulysses_repack_seq2head(do_seq, do_h)
         mark(3)
-        U.ulysses_attn_bwd(q_h[0], k_h[0], v_h[0], o_h[0], lse, do_h[0], None, w.scale, True,
-                           dq=dq_h[0], dk=dk_h[0], dv=dv_h[0], workspace=ws)
+        if ds_t is None:
+            U.ulysses_attn_bwd(q_h[0], k_h[0], v_h[0], o_h[0], lse, do_h[0], valid_t, w.scale, True,
+                               dq=dq_h[0], dk=dk_h[0], dv=dv_h[0], workspace=ws)
+        else:
+            U.ulysses_attn_bwd_docs(q_h[0], k_h[0], v_h[0], o_h[0], lse, do_h[0], ds_t, valid_t, w.scale,
+                                    dq=dq_h[0], dk=dk_h[0], dv=dv_h[0], workspace=ws)
         mark(4)
         U.ulysses_repack_head2seq(o_h, o_seq)
         mark(5)
@@ -220,7 +254,7 @@ def main():
     ms_step = wall * 1e3 / args.steps
     avg = {k: float(np.mean(v)) for k, v in per.items()}
 
-    pairs = causal_pairs(n)
+    pairs = int(visible_keys(n, valid_np, ds_np if args.docs else None).sum())
     fwd_flops = 4.0 * D * hq * pairs
     bwd_flops = 10.0 * D * hq * pairs
     bf2, f4 = 2, 4
@@ -244,10 +278,15 @@ def main():
     achieved = dom_flops / (avg[dom] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                "traffic": measured_traffic(dom)}
+                "traffic": measured_traffic(dom, w.name)}
 
+    metric = "causal attn TFLOP/s @64K, 8q/2kv heads d128 bf16; % MFMA peak; repack GB/s"
+    if args.docs:
+        metric = f"document-masked causal attn TFLOP/s @{n // 1024}K, {hq}q/{hkv}kv heads d{D} bf16"
+    elif w.number != 3:
+        metric = f"causal attn TFLOP/s @{n // 1024}K, {hq}q/{hkv}kv heads d{D} bf16"
     result = {
-        "metric": "causal attn TFLOP/s @64K, 8q/2kv heads d128 bf16; % MFMA peak; repack GB/s",
+        "metric": metric,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -259,8 +298,10 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name, "n": n, "P": P, "q_heads": hq, "kv_heads": hkv, "head_dim": D,
-                   "global_q_shape": [P, 1, nl, w.Hq_global, D], "causal": True},
+        "config": {"workload": w.name + ("+document-mask" if args.docs else ""), "n": n, "P": P, "q_heads": hq,
+                   "kv_heads": hkv, "head_dim": D, "global_q_shape": [P, 1, nl, w.Hq_global, D], "causal": True,
+                   "padding_mask": valid_np is not None, "document_mask": bool(args.docs),
+                   "visible_pairs_per_head": pairs},
         "breakdown_ms": {k: round(v, 4) for k, v in avg.items()},
         "attn_fwd_tflops": round(fwd_tf, 2),
         "attn_fwd_frac_mfma_peak": round(fwd_tf / MFMA_BF16_PEAK_TFLOPS, 4),
@@ -272,7 +313,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle sample)")
-        result["cpu_baseline"] = cpu_baseline(args.workload)
+        result["cpu_baseline"] = cpu_baseline(args.workload, args.docs)
     print(json.dumps(result), flush=True)
 
 

@@ -11,6 +11,8 @@
  *      and backward for dQ, dK, dV              (ulysses_attn_bwd)
  *   3. the second all-to-all, head shard -> sequence shard
  *                                               (ulysses_repack_head2seq)
+ * and, for packed sequences of variable-length documents, the attention
+ * calls with a document mask (ulysses_attn_fwd_docs, ulysses_attn_bwd_docs).
  *
  * Sources (web pages, cited by title and section):
  *   [ALST]  "Paralelismul de Secvență Ulysses: Antrenarea modelelor AI cu
@@ -205,6 +207,69 @@ ULYSSES_API ulysses_status_t ulysses_attn_bwd(const void* q, const void* k, cons
                                   float softmax_scale, int32_t causal,
                                   ulysses_dtype_t in_dtype, ulysses_dtype_t o_dtype,
                                   void* stream);
+
+/*
+ * ulysses_attn_fwd_docs -- ulysses_attn_fwd over a packed sequence of
+ * documents: causal attention in which a token sees only the tokens of its
+ * own document.
+ *
+ * Source: the trainers' switch for variable sequence lengths ([ALST]
+ * section "Integrarea cu Transformers Trainer și TRL SFTTrainer") packs
+ * several documents into one sequence; the page names the switch, and the
+ * mask here is its plain reading: no token attends across a document
+ * boundary.  Padding keys are excluded as in ulysses_attn_fwd ([ALST]
+ * section "Integrarea cu Accelerate").
+ *
+ * For batch b, query head h, query row t, the allowed keys are
+ *   doc_start[b][t] <= u <= t  and  (key_valid == NULL or key_valid[b][u] != 0)
+ * and everything else is as in ulysses_attn_fwd (o, natural-log lse, a row
+ * with no allowed key gets o = 0 and lse = -inf).  Whole tiles of keys
+ * outside every row's document are never read.
+ *
+ *   doc_start  [B][n] int32, device: the position of the first token of
+ *              token t's document (pad tokens belong to the document they
+ *              follow).  Required: 0 <= doc_start[b][t] <= t and
+ *              doc_start[b][t] non-decreasing in t (documents are
+ *              contiguous).  Any array meeting these two conditions is
+ *              computed exactly (a sliding window, max(0, t - W + 1), is
+ *              one).  An array that violates them is not checked (it lives
+ *              on the device): no access then leaves the buffers, but the
+ *              results are unspecified.
+ *   other arguments as for ulysses_attn_fwd; the mask is always causal.
+ *
+ * Built combinations and errors: as ulysses_attn_fwd, plus INVALID_ARG for
+ * a null or not 4-byte aligned doc_start (non-empty problem) and for an
+ * output overlapping doc_start.
+ */
+ULYSSES_API ulysses_status_t ulysses_attn_fwd_docs(const void* q, const void* k, const void* v,
+                                       const uint8_t* key_valid, const int32_t* doc_start,
+                                       void* o, float* lse,
+                                       int32_t B, int64_t n, int32_t Hq, int32_t Hkv, int32_t D,
+                                       float softmax_scale,
+                                       ulysses_dtype_t in_dtype, ulysses_dtype_t o_dtype,
+                                       void* stream);
+
+/*
+ * ulysses_attn_bwd_docs -- gradients of ulysses_attn_fwd_docs: the
+ * backward of ulysses_attn_bwd restricted to the same document mask
+ * (doc_start as for ulysses_attn_fwd_docs; o and lse from that call).
+ * The workspace size is ulysses_attn_bwd_workspace_bytes(...).  Each key's
+ * dK/dV gather only the query rows of its own document, and the tiles of
+ * rows past the end of that document are never read.
+ *
+ * Built combinations and errors: as ulysses_attn_bwd, plus INVALID_ARG for
+ * a null or not 4-byte aligned doc_start (non-empty problem) and for an
+ * output overlapping doc_start.
+ */
+ULYSSES_API ulysses_status_t ulysses_attn_bwd_docs(const void* q, const void* k, const void* v,
+                                       const uint8_t* key_valid, const int32_t* doc_start,
+                                       const void* o, const float* lse, const void* dout,
+                                       float* dq, float* dk, float* dv,
+                                       void* workspace, size_t workspace_bytes,
+                                       int32_t B, int64_t n, int32_t Hq, int32_t Hkv, int32_t D,
+                                       float softmax_scale,
+                                       ulysses_dtype_t in_dtype, ulysses_dtype_t o_dtype,
+                                       void* stream);
 
 #ifdef __cplusplus
 }

@@ -122,3 +122,30 @@ def test_bwd_validation(lib):
     assert _bwd(lib, dq=ctypes.c_void_p(0x5000000 + 64)) == INVALID        # dq overlaps dout
     assert _bwd(lib, it=F32) == UNSUPPORTED
     assert _bwd(lib, D=80) == UNSUPPORTED
+
+
+DOCS = ctypes.c_void_p(0xA000000)
+
+
+def _fwd_docs(lib, docs=DOCS, o=ctypes.c_void_p(0x3000000), B=1, n=64, it=BF16, ot=BF16):
+    return lib.ulysses_attn_fwd_docs(FAKE, ctypes.c_void_p(0x1000000), ctypes.c_void_p(0x2000000), None, docs, o,
+                                     ctypes.c_void_p(0x4000000), B, n, 8, 2, 128, 0.1, it, ot, None)
+
+
+def _bwd_docs(lib, docs=DOCS, dq=ctypes.c_void_p(0x6000000), n=64):
+    return lib.ulysses_attn_bwd_docs(FAKE, ctypes.c_void_p(0x1000000), ctypes.c_void_p(0x2000000), None, docs,
+                                     ctypes.c_void_p(0x3000000), ctypes.c_void_p(0x4000000),
+                                     ctypes.c_void_p(0x5000000), dq, ctypes.c_void_p(0x7000000),
+                                     ctypes.c_void_p(0x8000000), ctypes.c_void_p(0x9000000), 1 << 20,
+                                     1, n, 8, 2, 128, 0.1, BF16, BF16, None)
+
+
+def test_docs_validation(lib):
+    assert _fwd_docs(lib, docs=None) == INVALID                              # the documents are required
+    assert _fwd_docs(lib, docs=ctypes.c_void_p(0xA000002)) == INVALID        # not 4-byte aligned
+    assert _fwd_docs(lib, o=ctypes.c_void_p(0xA000000 - 1024)) == INVALID    # o overlaps doc_start
+    assert _fwd_docs(lib, it=F32, ot=BF16) == UNSUPPORTED
+    assert _fwd_docs(lib, B=0, docs=None) == OK                              # empty
+    assert _bwd_docs(lib, docs=None) == INVALID
+    assert _bwd_docs(lib, dq=ctypes.c_void_p(0xA000000 - 4096)) == INVALID   # dq overlaps doc_start
+    assert _bwd_docs(lib, n=0, docs=None) == OK

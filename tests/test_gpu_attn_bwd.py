@@ -37,7 +37,7 @@ def _inputs(seed, n, Hq, Hkv, D, masked, B=1):
     return q, k, v, do, valid
 
 
-def o_rounding_bound(q, k, do, O, LSE, scale, causal, valid, block=256):
+def o_rounding_bound(q, k, do, O, LSE, scale, causal, valid, block=256, doc_start=None):
     """Elementwise bound on the dQ / dK error caused by storing O in bfloat16."""
     B, n, Hq, D = q.shape
     Hkv = k.shape[2]
@@ -51,7 +51,8 @@ def o_rounding_bound(q, k, do, O, LSE, scale, causal, valid, block=256):
             dD = np.sum(np.abs(do[b, :, h, :]) * (2.0 ** -8) * np.abs(O[b, :, h, :]), axis=1)   # [n]
             for r0 in range(0, n, block):
                 t = np.arange(r0, min(n, r0 + block))
-                allow = oracle.attention.allowed_mask(t, n, causal, None if valid is None else valid[b])
+                allow = oracle.attention.allowed_mask(t, n, causal, None if valid is None else valid[b],
+                                                      None if doc_start is None else doc_start[b])
                 S = scale * (q[b, t, h, :] @ kh.T)
                 lse = LSE[b, h, t]
                 P = np.where(allow, np.exp(np.where(allow, S, 0.0) - np.where(np.isfinite(lse), lse, 0.0)[:, None]), 0.0)

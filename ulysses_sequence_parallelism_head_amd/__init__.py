@@ -42,6 +42,10 @@ _SIGS = {
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
                                         ctypes.c_int32, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
+    "ulysses_attn_fwd_docs": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                             ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
     "ulysses_attn_bwd_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
                                                            ctypes.c_int32, ctypes.c_int32]),
     "ulysses_attn_bwd": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -51,6 +55,13 @@ _SIGS = {
                                         ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                         ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_int, ctypes.c_int,
                                         ctypes.c_void_p]),
+    "ulysses_attn_bwd_docs": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_size_t,
+                                             ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.c_int32, ctypes.c_float, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_void_p]),
 }
 
 EXPORTED = tuple(_SIGS)
@@ -142,29 +153,54 @@ def ulysses_repack_head2seq(src: torch.Tensor, out: torch.Tensor | None = None) 
     return out
 
 
+def _check_docs(doc_start, B, n):
+    if doc_start is not None and (doc_start.dtype != torch.int32 or tuple(doc_start.shape) != (B, n)):
+        raise ValueError("doc_start must be int32 [B][n]")
+
+
 def ulysses_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, key_valid: torch.Tensor | None = None,
                      softmax_scale: float | None = None, causal: bool = True, o_dtype: torch.dtype | None = None,
                      out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
     """Attention forward.  q ``[B][n][Hq][D]``, k/v ``[B][n][Hkv][D]``,
     key_valid ``[B][n]`` uint8 or None.  Returns ``(o, lse)``; lse is
     float32 ``[B][Hq][n]`` in natural log."""
+    return _attn_fwd(q, k, v, key_valid, None, softmax_scale, causal, o_dtype, out, lse)
+
+
+def ulysses_attn_fwd_docs(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, doc_start: torch.Tensor,
+                          key_valid: torch.Tensor | None = None, softmax_scale: float | None = None,
+                          o_dtype: torch.dtype | None = None, out: torch.Tensor | None = None,
+                          lse: torch.Tensor | None = None):
+    """Document-masked causal forward: ``doc_start`` int32 ``[B][n]`` is the
+    first position of each token's document.  Returns ``(o, lse)``."""
+    return _attn_fwd(q, k, v, key_valid, doc_start, softmax_scale, True, o_dtype, out, lse)
+
+
+def _attn_fwd(q, k, v, key_valid, doc_start, softmax_scale, causal, o_dtype, out, lse):
     lib = load_library()
-    _need_contig_cuda(q, k, v, key_valid, out, lse)
+    _need_contig_cuda(q, k, v, key_valid, doc_start, out, lse)
     B, n, Hq, D = q.shape
     Hkv = k.shape[2]
     if k.shape != v.shape or k.dtype != q.dtype or v.dtype != q.dtype or k.shape[0] != B or k.shape[1] != n:
         raise ValueError("k, v must be [B][n][Hkv][D] with q's dtype")
     if key_valid is not None and (key_valid.dtype != torch.uint8 or tuple(key_valid.shape) != (B, n)):
         raise ValueError("key_valid must be uint8 [B][n]")
+    _check_docs(doc_start, B, n)
     scale = D ** -0.5 if softmax_scale is None else float(softmax_scale)
     o_dtype = q.dtype if o_dtype is None else o_dtype
     if out is None:
         out = torch.empty((B, n, Hq, D), dtype=o_dtype, device=q.device)
     if lse is None:
         lse = torch.empty((B, Hq, n), dtype=torch.float32, device=q.device)
-    _check(lib.ulysses_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(key_valid), _ptr(out), _ptr(lse), B, n, Hq, Hkv, D,
-                                scale, int(bool(causal)), _dtype_code(q), _dtype_code(out), _stream(q.device)),
-           "ulysses_attn_fwd")
+    if doc_start is None:
+        _check(lib.ulysses_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(key_valid), _ptr(out), _ptr(lse), B, n, Hq, Hkv,
+                                    D, scale, int(bool(causal)), _dtype_code(q), _dtype_code(out), _stream(q.device)),
+               "ulysses_attn_fwd")
+    else:
+        _check(lib.ulysses_attn_fwd_docs(_ptr(q), _ptr(k), _ptr(v), _ptr(key_valid), _ptr(doc_start), _ptr(out),
+                                         _ptr(lse), B, n, Hq, Hkv, D, scale, _dtype_code(q), _dtype_code(out),
+                                         _stream(q.device)),
+               "ulysses_attn_fwd_docs")
     return out, lse
 
 
@@ -175,9 +211,20 @@ def ulysses_attn_bwd_workspace_bytes(B: int, n: int, Hq: int, Hkv: int, D: int) 
 def ulysses_attn_bwd(q, k, v, o, lse, dout, key_valid=None, softmax_scale=None, causal=True,
                      dq=None, dk=None, dv=None, workspace=None):
     """Attention backward.  Returns float32 ``(dq, dk, dv)``."""
+    return _attn_bwd(q, k, v, o, lse, dout, key_valid, None, softmax_scale, causal, dq, dk, dv, workspace)
+
+
+def ulysses_attn_bwd_docs(q, k, v, o, lse, dout, doc_start, key_valid=None, softmax_scale=None,
+                          dq=None, dk=None, dv=None, workspace=None):
+    """Backward of :func:`ulysses_attn_fwd_docs`.  Returns float32 ``(dq, dk, dv)``."""
+    return _attn_bwd(q, k, v, o, lse, dout, key_valid, doc_start, softmax_scale, True, dq, dk, dv, workspace)
+
+
+def _attn_bwd(q, k, v, o, lse, dout, key_valid, doc_start, softmax_scale, causal, dq, dk, dv, workspace):
     lib = load_library()
-    _need_contig_cuda(q, k, v, o, lse, dout, key_valid, dq, dk, dv, workspace)
+    _need_contig_cuda(q, k, v, o, lse, dout, key_valid, doc_start, dq, dk, dv, workspace)
     B, n, Hq, D = q.shape
+    _check_docs(doc_start, B, n)
     Hkv = k.shape[2]
     scale = D ** -0.5 if softmax_scale is None else float(softmax_scale)
     dev = q.device
@@ -187,15 +234,23 @@ def ulysses_attn_bwd(q, k, v, o, lse, dout, key_valid=None, softmax_scale=None, 
     wsb = ulysses_attn_bwd_workspace_bytes(B, n, Hq, Hkv, D)
     if workspace is None:
         workspace = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
-    _check(lib.ulysses_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(key_valid), _ptr(o), _ptr(lse), _ptr(dout),
-                                _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                B, n, Hq, Hkv, D, scale, int(bool(causal)), _dtype_code(q), _dtype_code(o),
-                                _stream(dev)),
-           "ulysses_attn_bwd")
+    wbytes = workspace.numel() * workspace.element_size()
+    if doc_start is None:
+        _check(lib.ulysses_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(key_valid), _ptr(o), _ptr(lse), _ptr(dout),
+                                    _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), wbytes,
+                                    B, n, Hq, Hkv, D, scale, int(bool(causal)), _dtype_code(q), _dtype_code(o),
+                                    _stream(dev)),
+               "ulysses_attn_bwd")
+    else:
+        _check(lib.ulysses_attn_bwd_docs(_ptr(q), _ptr(k), _ptr(v), _ptr(key_valid), _ptr(doc_start), _ptr(o),
+                                         _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), wbytes,
+                                         B, n, Hq, Hkv, D, scale, _dtype_code(q), _dtype_code(o), _stream(dev)),
+               "ulysses_attn_bwd_docs")
     return dq, dk, dv
 
 
 __all__ = [
     "load_library", "EXPORTED", "LIB_PATH", "ulysses_abi_version", "ulysses_repack_seq2head",
     "ulysses_repack_head2seq", "ulysses_attn_fwd", "ulysses_attn_bwd", "ulysses_attn_bwd_workspace_bytes",
+    "ulysses_attn_fwd_docs", "ulysses_attn_bwd_docs",
 ]

@@ -65,6 +65,77 @@ ulysses_status_t check_attn_shape(int32_t B, int64_t n, int32_t Hq, int32_t Hkv,
   return ULYSSES_OK;
 }
 
+// Forward with an optional per-row document bound (doc_start, causal only).
+ulysses_status_t attn_fwd(const void* q, const void* k, const void* v, const uint8_t* key_valid,
+                          const int32_t* doc_start, void* o, float* lse, int32_t B, int64_t n, int32_t Hq,
+                          int32_t Hkv, int32_t D, float softmax_scale, int32_t causal, ulysses_dtype_t in_dtype,
+                          ulysses_dtype_t o_dtype, void* stream) {
+  bool empty = false;
+  ulysses_status_t st = check_attn_shape(B, n, Hq, Hkv, D, softmax_scale, causal, in_dtype, o_dtype, &empty);
+  if (st != ULYSSES_OK || empty) return st;
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || lse == nullptr) return ULYSSES_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
+      !aligned(doc_start, 4))
+    return ULYSSES_ERR_INVALID_ARG;
+  const bool bf16_in = in_dtype == ULYSSES_DTYPE_BF16;
+  if (!bf16_in && o_dtype != ULYSSES_DTYPE_F32) return ULYSSES_ERR_UNSUPPORTED;
+  const uint64_t ei = elem_size(in_dtype), eo = elem_size(o_dtype);
+  const uint64_t nq = uint64_t(B) * n * Hq * D, nkv = uint64_t(B) * n * Hkv * D;
+  const uint64_t bo = nq * eo, bl = uint64_t(B) * Hq * n * 4;
+  const void* ins[5] = {q, k, v, key_valid, doc_start};
+  const uint64_t inb[5] = {nq * ei, nkv * ei, nkv * ei, key_valid ? uint64_t(B) * n : 0,
+                           doc_start ? uint64_t(B) * n * 4 : 0};
+  for (int i = 0; i < 5; ++i)
+    if (overlap(o, bo, ins[i], inb[i]) || overlap(lse, bl, ins[i], inb[i])) return ULYSSES_ERR_INVALID_ARG;
+  if (overlap(o, bo, lse, bl)) return ULYSSES_ERR_INVALID_ARG;
+  AttnShape s{B, n, Hq, Hkv, D, softmax_scale, causal};
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (bf16_in)
+    return from_hip(
+        ulysses::launch_attn_fwd_bf16(q, k, v, key_valid, doc_start, o, lse, s, o_dtype == ULYSSES_DTYPE_F32, hs));
+  return from_hip(ulysses::launch_attn_fwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
+                                               static_cast<const float*>(v), key_valid, doc_start,
+                                               static_cast<float*>(o), lse, s, hs));
+}
+
+// Backward with an optional per-row document bound (doc_start, causal only).
+ulysses_status_t attn_bwd(const void* q, const void* k, const void* v, const uint8_t* key_valid,
+                          const int32_t* doc_start, const void* o, const float* lse, const void* dout, float* dq,
+                          float* dk, float* dv, void* workspace, size_t workspace_bytes, int32_t B, int64_t n,
+                          int32_t Hq, int32_t Hkv, int32_t D, float softmax_scale, int32_t causal,
+                          ulysses_dtype_t in_dtype, ulysses_dtype_t o_dtype, void* stream) {
+  bool empty = false;
+  ulysses_status_t st = check_attn_shape(B, n, Hq, Hkv, D, softmax_scale, causal, in_dtype, o_dtype, &empty);
+  if (st != ULYSSES_OK || empty) return st;
+  if (in_dtype != ULYSSES_DTYPE_BF16) return ULYSSES_ERR_UNSUPPORTED;
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || lse == nullptr || dout == nullptr ||
+      dq == nullptr || dk == nullptr || dv == nullptr || workspace == nullptr)
+    return ULYSSES_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
+      !aligned(lse, 4) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(workspace, 256) ||
+      !aligned(doc_start, 4))
+    return ULYSSES_ERR_INVALID_ARG;
+  const size_t need = ulysses::attn_bwd_workspace_bytes(B, n, Hq);
+  if (workspace_bytes < need) return ULYSSES_ERR_INVALID_ARG;
+  const uint64_t nq = uint64_t(B) * n * Hq * D, nkv = uint64_t(B) * n * Hkv * D;
+  const void* ins[8] = {q, k, v, key_valid, o, lse, dout, doc_start};
+  const uint64_t inb[8] = {nq * 2, nkv * 2, nkv * 2, key_valid ? uint64_t(B) * n : 0,
+                           nq * elem_size(o_dtype), uint64_t(B) * Hq * n * 4, nq * 2,
+                           doc_start ? uint64_t(B) * n * 4 : 0};
+  const void* outs[4] = {dq, dk, dv, workspace};
+  const uint64_t outb[4] = {nq * 4, nkv * 4, nkv * 4, need};
+  for (int a = 0; a < 4; ++a) {
+    for (int i = 0; i < 8; ++i)
+      if (overlap(outs[a], outb[a], ins[i], inb[i])) return ULYSSES_ERR_INVALID_ARG;
+    for (int c = a + 1; c < 4; ++c)
+      if (overlap(outs[a], outb[a], outs[c], outb[c])) return ULYSSES_ERR_INVALID_ARG;
+  }
+  AttnShape s{B, n, Hq, Hkv, D, softmax_scale, causal};
+  return from_hip(ulysses::launch_attn_bwd_bf16(q, k, v, key_valid, doc_start, o, lse, dout, dq, dk, dv,
+                                                static_cast<float*>(workspace), s, o_dtype == ULYSSES_DTYPE_F32,
+                                                static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -95,29 +166,17 @@ ulysses_status_t ulysses_attn_fwd(const void* q, const void* k, const void* v, c
                                   float* lse, int32_t B, int64_t n, int32_t Hq, int32_t Hkv, int32_t D,
                                   float softmax_scale, int32_t causal, ulysses_dtype_t in_dtype,
                                   ulysses_dtype_t o_dtype, void* stream) {
-  bool empty = false;
-  ulysses_status_t st = check_attn_shape(B, n, Hq, Hkv, D, softmax_scale, causal, in_dtype, o_dtype, &empty);
-  if (st != ULYSSES_OK || empty) return st;
-  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || lse == nullptr) return ULYSSES_ERR_INVALID_ARG;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
-    return ULYSSES_ERR_INVALID_ARG;
-  const bool bf16_in = in_dtype == ULYSSES_DTYPE_BF16;
-  if (!bf16_in && o_dtype != ULYSSES_DTYPE_F32) return ULYSSES_ERR_UNSUPPORTED;
-  const uint64_t ei = elem_size(in_dtype), eo = elem_size(o_dtype);
-  const uint64_t nq = uint64_t(B) * n * Hq * D, nkv = uint64_t(B) * n * Hkv * D;
-  const uint64_t bo = nq * eo, bl = uint64_t(B) * Hq * n * 4;
-  const void* ins[4] = {q, k, v, key_valid};
-  const uint64_t inb[4] = {nq * ei, nkv * ei, nkv * ei, key_valid ? uint64_t(B) * n : 0};
-  for (int i = 0; i < 4; ++i)
-    if (overlap(o, bo, ins[i], inb[i]) || overlap(lse, bl, ins[i], inb[i])) return ULYSSES_ERR_INVALID_ARG;
-  if (overlap(o, bo, lse, bl)) return ULYSSES_ERR_INVALID_ARG;
-  AttnShape s{B, n, Hq, Hkv, D, softmax_scale, causal};
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  if (bf16_in)
-    return from_hip(ulysses::launch_attn_fwd_bf16(q, k, v, key_valid, o, lse, s, o_dtype == ULYSSES_DTYPE_F32, hs));
-  return from_hip(ulysses::launch_attn_fwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
-                                               static_cast<const float*>(v), key_valid, static_cast<float*>(o), lse,
-                                               s, hs));
+  return attn_fwd(q, k, v, key_valid, nullptr, o, lse, B, n, Hq, Hkv, D, softmax_scale, causal, in_dtype, o_dtype,
+                  stream);
+}
+
+ulysses_status_t ulysses_attn_fwd_docs(const void* q, const void* k, const void* v, const uint8_t* key_valid,
+                                       const int32_t* doc_start, void* o, float* lse, int32_t B, int64_t n,
+                                       int32_t Hq, int32_t Hkv, int32_t D, float softmax_scale,
+                                       ulysses_dtype_t in_dtype, ulysses_dtype_t o_dtype, void* stream) {
+  if (doc_start == nullptr && B > 0 && n > 0) return ULYSSES_ERR_INVALID_ARG;
+  return attn_fwd(q, k, v, key_valid, doc_start, o, lse, B, n, Hq, Hkv, D, softmax_scale, 1, in_dtype, o_dtype,
+                  stream);
 }
 
 size_t ulysses_attn_bwd_workspace_bytes(int32_t B, int64_t n, int32_t Hq, int32_t Hkv, int32_t D) {
@@ -132,34 +191,19 @@ ulysses_status_t ulysses_attn_bwd(const void* q, const void* k, const void* v, c
                                   void* workspace, size_t workspace_bytes, int32_t B, int64_t n, int32_t Hq,
                                   int32_t Hkv, int32_t D, float softmax_scale, int32_t causal,
                                   ulysses_dtype_t in_dtype, ulysses_dtype_t o_dtype, void* stream) {
-  bool empty = false;
-  ulysses_status_t st = check_attn_shape(B, n, Hq, Hkv, D, softmax_scale, causal, in_dtype, o_dtype, &empty);
-  if (st != ULYSSES_OK || empty) return st;
-  if (in_dtype != ULYSSES_DTYPE_BF16) return ULYSSES_ERR_UNSUPPORTED;
-  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || lse == nullptr || dout == nullptr ||
-      dq == nullptr || dk == nullptr || dv == nullptr || workspace == nullptr)
-    return ULYSSES_ERR_INVALID_ARG;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
-      !aligned(lse, 4) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(workspace, 256))
-    return ULYSSES_ERR_INVALID_ARG;
-  const size_t need = ulysses::attn_bwd_workspace_bytes(B, n, Hq);
-  if (workspace_bytes < need) return ULYSSES_ERR_INVALID_ARG;
-  const uint64_t nq = uint64_t(B) * n * Hq * D, nkv = uint64_t(B) * n * Hkv * D;
-  const void* ins[7] = {q, k, v, key_valid, o, lse, dout};
-  const uint64_t inb[7] = {nq * 2, nkv * 2, nkv * 2, key_valid ? uint64_t(B) * n : 0,
-                           nq * elem_size(o_dtype), uint64_t(B) * Hq * n * 4, nq * 2};
-  const void* outs[4] = {dq, dk, dv, workspace};
-  const uint64_t outb[4] = {nq * 4, nkv * 4, nkv * 4, need};
-  for (int a = 0; a < 4; ++a) {
-    for (int i = 0; i < 7; ++i)
-      if (overlap(outs[a], outb[a], ins[i], inb[i])) return ULYSSES_ERR_INVALID_ARG;
-    for (int c = a + 1; c < 4; ++c)
-      if (overlap(outs[a], outb[a], outs[c], outb[c])) return ULYSSES_ERR_INVALID_ARG;
-  }
-  AttnShape s{B, n, Hq, Hkv, D, softmax_scale, causal};
-  return from_hip(ulysses::launch_attn_bwd_bf16(q, k, v, key_valid, o, lse, dout, dq, dk, dv,
-                                                static_cast<float*>(workspace), s, o_dtype == ULYSSES_DTYPE_F32,
-                                                static_cast<hipStream_t>(stream)));
+  return attn_bwd(q, k, v, key_valid, nullptr, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, n, Hq, Hkv,
+                  D, softmax_scale, causal, in_dtype, o_dtype, stream);
+}
+
+ulysses_status_t ulysses_attn_bwd_docs(const void* q, const void* k, const void* v, const uint8_t* key_valid,
+                                       const int32_t* doc_start, const void* o, const float* lse, const void* dout,
+                                       float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes,
+                                       int32_t B, int64_t n, int32_t Hq, int32_t Hkv, int32_t D,
+                                       float softmax_scale, ulysses_dtype_t in_dtype, ulysses_dtype_t o_dtype,
+                                       void* stream) {
+  if (doc_start == nullptr && B > 0 && n > 0) return ULYSSES_ERR_INVALID_ARG;
+  return attn_bwd(q, k, v, key_valid, doc_start, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, n, Hq, Hkv,
+                  D, softmax_scale, 1, in_dtype, o_dtype, stream);
 }
 
 }  // extern "C"

@@ -32,6 +32,12 @@
 //     makes every gradient deterministic.
 // Rows below kSplitRows use a hi/lo bf16 split of P and dS (two MFMAs) for
 // accuracy where few keys carry large weights.
+// Packed documents (a per-row lower bound on the visible keys, the first
+// position of the row's document): dq starts at the tile holding its first
+// row's bound, as the forward does; a dkdv workgroup finds the end of the
+// last document its keys belong to (a 64-lane search over the bounds) and
+// visits only the query tiles up to it, sweeping down from there so that the
+// workgroups of one document read the same tiles at the same time.
 #include <type_traits>
 
 #include "device_common.h"
@@ -51,6 +57,7 @@ struct BwdParams {
   const uint16_t* k;
   const uint16_t* v;
   const uint8_t* valid;
+  const int32_t* doc_start;   // [B][n] first position of each row's document, or null
   const void* o;
   const float* lse;
   const uint16_t* dout;
@@ -110,7 +117,7 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const BwdParams p) {
 }
 
 // ------------------------------------------------------------------- dkdv
-template <int D>
+template <int D, bool DOCS>
 struct DkdvLayout {
   static constexpr int kRows = 64;                        // query rows per tile
   static constexpr int kRowBytes = 2 * D;
@@ -120,17 +127,18 @@ struct DkdvLayout {
   static constexpr int kOffDO = kOffQ + kBytesRM;
   static constexpr int kOffLSE = kOffDO + kBytesRM;
   static constexpr int kOffDL = kOffLSE + kRows * 4;
-  static constexpr int kStage = kOffDL + kRows * 4;
+  static constexpr int kOffLO = kOffDL + kRows * 4;       // document bounds of the rows (DOCS)
+  static constexpr int kStage = kOffLO + (DOCS ? kRows * 4 : 0);
   static constexpr int kStageAligned = (kStage + 127) / 128 * 128;
 };
 
 // DMA the query tile t0 .. t0+63 of query head `head`: Q and dO rows into the
-// swizzled row-major tiles, the base-2 logsumexp and Dl values into two float
-// arrays (rows past n read as zero).
-template <int D>
+// swizzled row-major tiles, the base-2 logsumexp and Dl values (and with
+// documents the rows' bounds) into arrays of 64 (rows past n read as zero).
+template <int D, bool DOCS>
 __device__ __forceinline__ void dkdv_issue(uint8_t* stage, const BwdParams& p, int b, int head, int t0, int wave,
                                            int lane) {
-  using L = DkdvLayout<D>;
+  using L = DkdvLayout<D, DOCS>;
   const int rows_ok = min(L::kRows, p.n - t0);
   const int64_t off = ((int64_t(b) * p.n + t0) * p.Hq + head) * D;
   const int stride = p.Hq * D * 2;
@@ -139,6 +147,8 @@ __device__ __forceinline__ void dkdv_issue(uint8_t* stage, const BwdParams& p, i
   const int64_t roff = (int64_t(b) * p.Hq + head) * p.n + t0;
   if (wave == 0) dma4(buffer_rsrc(p.lse2 + roff, uint32_t(rows_ok) * 4u), stage + L::kOffLSE, lane * 4);
   if (wave == 1) dma4(buffer_rsrc(p.rowdot + roff, uint32_t(rows_ok) * 4u), stage + L::kOffDL, lane * 4);
+  if (DOCS && wave == 2)
+    dma4(buffer_rsrc(p.doc_start + int64_t(b) * p.n + t0, uint32_t(rows_ok) * 4u), stage + L::kOffLO, lane * 4);
 }
 
 // Pack 8 floats (x[0..7]) as the bf16 B operand of one MFMA, and optionally
@@ -159,12 +169,14 @@ __device__ __forceinline__ u32x4 pack8_residual(const float* x, const u32x4 hi) 
 
 // One 32-row block of a staged query tile against this wave's 32 keys, after
 // S and dP are in registers: P, dS, then dV^T += dO^T P and dK^T += Q^T dS.
-// SPLIT adds the bf16 residuals of P and dS as second MFMAs.
-template <int D, bool CAUSAL, bool SPLIT>
+// SPLIT adds the bf16 residuals of P and dS as second MFMAs.  LOWER applies
+// the rows' document bounds (key u is visible to row t only if u >= bound).
+template <int D, bool DOCS, bool CAUSAL, bool SPLIT, bool LOWER>
 __device__ __forceinline__ void dkdv_rows(const uint8_t* qs, const uint8_t* dos, const float* lses, const float* dls,
-                                          const f32x16& s, const f32x16& dp, int rb, int t0, int u, bool key_ok,
-                                          int hh, int lane, float c, f32x16 (&dka)[D / 32], f32x16 (&dva)[D / 32]) {
-  using L = DkdvLayout<D>;
+                                          const int32_t* los, const f32x16& s, const f32x16& dp, int rb, int t0, int u,
+                                          bool key_ok, int hh, int lane, float c, f32x16 (&dka)[D / 32],
+                                          f32x16 (&dva)[D / 32]) {
+  using L = DkdvLayout<D, DOCS>;
   constexpr int DJ = D / 32;
   float pr[16], ds[16];
   // element i is query row t0 + 4hh + C_i (C_i = rb*32 + (i/4)*8 + i%4, a
@@ -175,11 +187,13 @@ __device__ __forceinline__ void dkdv_rows(const uint8_t* qs, const uint8_t* dos,
     const int rr = rb * 32 + g4 * 8 + hh * 4;
     const f32x4 l4 = *reinterpret_cast<const f32x4*>(lses + rr);
     const f32x4 d4 = *reinterpret_cast<const f32x4*>(dls + rr);
+    i32x4 b4 = i32x4{0, 0, 0, 0};
+    if (LOWER) b4 = *reinterpret_cast<const i32x4*>(los + rr);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = g4 * 4 + e;
       const int ci = rb * 32 + g4 * 8 + e;
-      const bool ok = key_ok && ci >= lim;
+      const bool ok = key_ok && ci >= lim && (!LOWER || b4[e] <= u);
       // invisible keys, and rows with no visible key (base-2 LSE = +inf), get
       // exponent -inf: exp2(-inf) = 0 exactly
       const float x = ok ? fmaf(s[i], c, -l4[e]) : -INFINITY;
@@ -213,6 +227,32 @@ __device__ __forceinline__ void dkdv_rows(const uint8_t* qs, const uint8_t* dos,
   }
 }
 
+// End (exclusive) of the rows that can see key `klast`: the first row t >
+// klast whose bound exceeds klast, or n.  The bounds never decrease along a
+// batch row, so the answer is found by a search over positions: each round
+// the 64 lanes probe 64 evenly spaced rows of the remaining range and the
+// first probe above klast narrows it to one gap (three rounds for 2^18
+// rows).  Every probe is in [klast+1, n), whatever the array holds.
+__device__ __forceinline__ int doc_rows_end(const int32_t* rs, int klast, int n, int lane) {
+  int lo = klast + 1, hi = n;           // the answer lies in [lo, hi]
+  while (lo < hi) {
+    const int step = (hi - lo + 63) / 64;
+    const int pos = lo + lane * step;
+    const bool above = pos < hi && rs[pos] > klast;
+    const uint64_t m = __ballot(above);
+    if (m == 0) {
+      // every probe below hi is at or under klast: the answer is past the last one
+      const int last = min(63, (hi - 1 - lo) / step);
+      lo = lo + last * step + 1;
+    } else {
+      const int j = __builtin_ctzll(m);
+      hi = lo + j * step;
+      if (j > 0) lo = lo + (j - 1) * step + 1;
+    }
+  }
+  return lo;
+}
+
 // Work items and tile order.  A work item is one key block (non-causal) or,
 // for causal attention, the pair of key blocks (nkb-1-w, w): the first one
 // sweeps the query tiles from the last down to its diagonal, the second from
@@ -221,9 +261,12 @@ __device__ __forceinline__ void dkdv_rows(const uint8_t* qs, const uint8_t* dos,
 // resident workgroup reads, at unit U, either tile ntq-1-U/g (first phase) or
 // tile U/g + 2nkb-2-ntq (second phase) of query head U%g: the workgroups of
 // one XCD share two tiles at a time, which the XCD's L2 keeps.
-template <int D, bool HAS_MASK, bool CAUSAL>
+// With documents a work item is one key block, swept down from the last tile
+// of its last document: the blocks of one document start on the same tile.
+template <int D, bool HAS_MASK, bool CAUSAL, bool DOCS>
 __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdParams p) {
-  using L = DkdvLayout<D>;
+  static_assert(CAUSAL || !DOCS, "documents are causal");
+  using L = DkdvLayout<D, DOCS>;
   constexpr int KK = D / 16;
   constexpr int DJ = D / 32;
   constexpr int kKeys = 128;                      // keys per workgroup (4 waves x 32)
@@ -244,11 +287,11 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdParams p) {
   const int b = rem / p.Hkv;
   const int kvh = rem % p.Hkv;
   const int ntq = (p.n + L::kRows - 1) / L::kRows;   // query tiles per head
-  const int nph = (CAUSAL && p.n_kblocks - 1 - w != w) ? 2 : 1;
+  const int nph = (CAUSAL && !DOCS && p.n_kblocks - 1 - w != w) ? 2 : 1;
 
   for (int ph = 0; ph < nph; ++ph) {
     const bool down = CAUSAL && ph == 0;
-    const int kb = down ? p.n_kblocks - 1 - w : w;
+    const int kb = (down && !DOCS) ? p.n_kblocks - 1 - w : w;
     const int k0w = kb * kKeys + wave * 32;        // first key of this wave
     const int u = k0w + l32;                       // this lane's key
     const bool wave_live = k0w < p.n;
@@ -273,34 +316,55 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdParams p) {
       dva[j] = f32x16{};
     }
 
-    // query tiles tfirst .. ntq-1 hold every row that can see the block's keys
+    // query tiles tfirst .. tend-1 hold every row that can see the block's
+    // keys.  Rows from split_end on see at least kSplitRows keys.  With
+    // documents, the rows that see the keys end at rend (the end of the last
+    // document holding one of them), and the per-row lower mask is needed if
+    // any visited row -- up to the end of the last tile, past rend -- has its
+    // bound above the block's first key.
     const int tfirst = CAUSAL ? (kb * kKeys) / L::kRows : 0;
-    const int niter = (ntq - tfirst) * p.g;
+    int tend = ntq;
+    int split_end = kSplitRows;
+    bool lower = false;
+    if (DOCS) {
+      const int32_t* rs = p.doc_start + int64_t(b) * p.n;
+      const int kfirst = kb * kKeys;
+      const int klast = min(kfirst + kKeys, p.n) - 1;
+      const int rend = doc_rows_end(rs, klast, p.n, lane);
+      tend = (rend + L::kRows - 1) / L::kRows;
+      split_end = doc_lower(rs, rend - 1) + kSplitRows;
+      lower = doc_lower(rs, min(tend * L::kRows, p.n) - 1) > kfirst;
+    }
+    const int niter = (tend - tfirst) * p.g;
     // unit it -> (tile, head of the group)
-    auto tile_of = [&](int it) { return down ? ntq - 1 - it / p.g : tfirst + it / p.g; };
+    auto tile_of = [&](int it) { return down ? tend - 1 - it / p.g : tfirst + it / p.g; };
 
-    if (niter > 0) dkdv_issue<D>(smem, p, b, kvh * p.g, tile_of(0) * L::kRows, wave, lane);
+    if (niter > 0) dkdv_issue<D, DOCS>(smem, p, b, kvh * p.g, tile_of(0) * L::kRows, wave, lane);
     wait_vmem();
     __syncthreads();
 
-    // units [it0, it1), all on tiles of one kind: rows below kSplitRows (hi/lo
-    // split) or not.  Keeping the choice out of the loop body matters: a
-    // branch inside it makes the two sides allocate the 128 dK/dV accumulator
-    // registers differently and copy all of them at every merge.
-    auto run = [&](int it0, int it1, auto split_tag) {
+    // units [it0, it1), all on tiles of one kind: rows below split_end (hi/lo
+    // split) or not, lower mask or not.  Keeping the choice out of the loop
+    // body matters: a branch inside it makes the two sides allocate the 128
+    // dK/dV accumulator registers differently and copy all of them at every
+    // merge.
+    // (forced inline: as a call the wave index would arrive in a vector register)
+    auto run = [&](int it0, int it1, auto split_tag, auto lower_tag) __attribute__((always_inline)) {
       constexpr bool SPLIT = decltype(split_tag)::value;
+      constexpr bool LOWER = decltype(lower_tag)::value;
       for (int it = it0; it < it1; ++it) {
         // prefetch unit it+1 into the other buffer while computing on this one
         uint8_t* cur = smem + (it & 1) * L::kStageAligned;
         if (it + 1 < niter)
-          dkdv_issue<D>(smem + ((it + 1) & 1) * L::kStageAligned, p, b, kvh * p.g + (it + 1) % p.g,
-                        tile_of(it + 1) * L::kRows, wave, lane);
+          dkdv_issue<D, DOCS>(smem + ((it + 1) & 1) * L::kStageAligned, p, b, kvh * p.g + (it + 1) % p.g,
+                              tile_of(it + 1) * L::kRows, wave, lane);
         const int t0 = tile_of(it) * L::kRows;
         if (wave_live) {
           const uint8_t* qs = cur + L::kOffQ;
           const uint8_t* dos = cur + L::kOffDO;
           const float* lses = reinterpret_cast<const float*>(cur + L::kOffLSE);
           const float* dls = reinterpret_cast<const float*>(cur + L::kOffDL);
+          const int32_t* los = reinterpret_cast<const int32_t*>(cur + L::kOffLO);
           // S[q][key] and dP[q][key] for both 32-row blocks (lane = key, rows
           // q = rb*32 + (i/4)*8 + 4hh + i%4), then P, dS and the dV/dK products
           // block by block, all in one basic block so that one block's
@@ -327,22 +391,30 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdParams p) {
           pipeline_reads_mfma<6, 4 * KK>();
 #pragma unroll
           for (int rb = 0; rb < 2; ++rb)
-            dkdv_rows<D, CAUSAL, SPLIT>(qs, dos, lses, dls, s[rb], dp[rb], rb, t0, u, key_ok, hh, lane, p.c, dka,
-                                        dva);
+            dkdv_rows<D, DOCS, CAUSAL, SPLIT, LOWER>(qs, dos, lses, dls, los, s[rb], dp[rb], rb, t0, u, key_ok, hh,
+                                                     lane, p.c, dka, dva);
         }
         wait_vmem();
         __syncthreads();
       }
     };
-    // tiles below kSplitRows / kRows need the split: tfirst .. min(that, ntq) - 1
-    constexpr int kSplitTiles = kSplitRows / L::kRows;
-    const int nsplit = max(0, min(kSplitTiles, ntq) - tfirst) * p.g;
-    if (down) {                       // split tiles come last
-      run(0, niter - nsplit, std::false_type{});
-      run(niter - nsplit, niter, std::true_type{});
-    } else {                          // split tiles come first
-      run(0, nsplit, std::true_type{});
-      run(nsplit, niter, std::false_type{});
+    // tiles below split_end need the split: tfirst .. min(ceil(split_end / kRows), tend) - 1
+    const int nsplit = max(0, min((split_end + L::kRows - 1) / L::kRows, tend) - tfirst) * p.g;
+    auto sweep = [&](auto lower_tag) __attribute__((always_inline)) {
+      if (down) {                       // split tiles come last
+        run(0, niter - nsplit, std::false_type{}, lower_tag);
+        run(niter - nsplit, niter, std::true_type{}, lower_tag);
+      } else {                          // split tiles come first
+        run(0, nsplit, std::true_type{}, lower_tag);
+        run(nsplit, niter, std::false_type{}, lower_tag);
+      }
+    };
+    if constexpr (DOCS) {
+      if (lower) sweep(std::true_type{});
+      else sweep(std::false_type{});
+    } else {
+      (void)lower;
+      sweep(std::false_type{});
     }
 
     // write dK = scale * dK^T^T and dV: lane = key u, dims 32j + 8*(i/4) + 4hh + i%4
@@ -395,12 +467,13 @@ __device__ __forceinline__ void dq_issue(uint8_t* stage, uint32_t& vbyte, const 
 
 // One 32-key half of a staged K/V tile against this wave's 32 query rows:
 // S^T and dP^T, dS^T, then dQ^T += K^T dS^T.  `lim`: key row C of the half is
-// visible iff C <= lim (and its valid byte is set when HAS_MASK).  SPLIT adds
-// the bf16 residual of dS as second MFMAs.
-template <int D, bool HAS_MASK, bool SPLIT>
+// visible iff C <= lim (and its valid byte is set when HAS_MASK), and with
+// documents iff also C >= lo.  SPLIT adds the bf16 residual of dS as second
+// MFMAs.
+template <int D, bool HAS_MASK, bool SPLIT, bool DOCS>
 __device__ __forceinline__ void dq_half(const uint8_t* ks, const uint8_t* vs, const uint8_t* vb, int half, int lim,
-                                        const u32x4 (&qf)[D / 16], const u32x4 (&df)[D / 16], float lse2, float dl,
-                                        float c, int l32, int hh, int lane, f32x16 (&dqa)[D / 32]) {
+                                        int lo, const u32x4 (&qf)[D / 16], const u32x4 (&df)[D / 16], float lse2,
+                                        float dl, float c, int l32, int hh, int lane, f32x16 (&dqa)[D / 32]) {
   using L = DqLayout<D>;
   constexpr int KK = D / 16;
   constexpr int DJ = D / 32;
@@ -423,7 +496,7 @@ __device__ __forceinline__ void dq_half(const uint8_t* ks, const uint8_t* vs, co
     for (int e = 0; e < 4; ++e) {
       const int i = g4 * 4 + e;
       const int ci = g4 * 8 + e;
-      const bool ok = ci <= lim && (!HAS_MASK || ((vw >> (8 * e)) & 0xffu));
+      const bool ok = ci <= lim && (!DOCS || ci >= lo) && (!HAS_MASK || ((vw >> (8 * e)) & 0xffu));
       // invisible keys (and rows with no visible key: lse2 = +inf) get exponent -inf
       const float x = ok ? fmaf(s[i], c, -lse2) : -INFINITY;
       ds[i] = __builtin_amdgcn_exp2f(x) * (dp[i] - dl);
@@ -448,8 +521,9 @@ __device__ __forceinline__ void dq_half(const uint8_t* ks, const uint8_t* vs, co
   if (!SPLIT) pipeline_tr_reads_mfma<3, 2 * DJ>();
 }
 
-template <int D, bool HAS_MASK, bool CAUSAL>
+template <int D, bool HAS_MASK, bool CAUSAL, bool DOCS>
 __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const BwdParams p) {
+  static_assert(CAUSAL || !DOCS, "documents are causal");
   using L = DqLayout<D>;
   constexpr int KK = D / 16;
   constexpr int DJ = D / 32;
@@ -479,6 +553,18 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const BwdParams p) {
   const int ntiles = (kend + L::kBN - 1) / L::kBN;
   const bool wave_live = p0 < p.n;
 
+  // packed documents: first tile, the last row's bound (tiles below it take
+  // the lower mask), the wave's first row's bound (tiles below it are
+  // skipped) and this lane's row's bound
+  int it_first = 0, lo_last = 0, lo_wave = 0, lo_row = 0;
+  if (DOCS) {
+    const int32_t* rs = p.doc_start + int64_t(b) * p.n;
+    it_first = doc_lower(rs, pb * p.pw) / L::kBN;
+    lo_last = doc_lower(rs, wg_last);
+    lo_wave = wave_live ? doc_lower(rs, p0) : 0;
+    lo_row = t < p.n ? doc_lower(rs, t) : 0;
+  }
+
   u32x4 qf[KK], df[KK];
   float lse2 = INFINITY, dl = 0.f;
   {
@@ -496,27 +582,32 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const BwdParams p) {
     }
   }
 
-  // rows below kSplitRows take the hi/lo path; the choice is made once per
-  // workgroup (its first row) so the common path carries no residuals
+  // rows with fewer than kSplitRows visible keys take the hi/lo path; the
+  // choice is made once per workgroup so the common path carries no
+  // residuals.  Every row sees at least (first row) - (last row's bound) keys.
   auto run = [&](auto split_tag) {
     constexpr bool SPLIT = decltype(split_tag)::value;
     f32x16 dqa[DJ];
 #pragma unroll
     for (int j = 0; j < DJ; ++j) dqa[j] = f32x16{};
 
+    // step j works on tile it_first + j, staged in buffer j & 1 (the LDS
+    // addresses depend on the step counter only)
     uint32_t vbyte = 0;
-    dq_issue<D, HAS_MASK>(smem, vbyte, p, b, kvh, 0, wave, lane, tid);
+    dq_issue<D, HAS_MASK>(smem, vbyte, p, b, kvh, it_first, wave, lane, tid);
     if (HAS_MASK && tid < L::kBN) smem[L::kOffValid + tid] = uint8_t(vbyte);
     wait_vmem();
     __syncthreads();
 
-    for (int it = 0; it < ntiles; ++it) {
+    const int nsteps = ntiles - it_first;
+    for (int j = 0; j < nsteps; ++j) {
+      const int it = it_first + j;
       // prefetch tile it+1 into the other buffer while computing on this one
-      uint8_t* cur = smem + (it & 1) * L::kStageAligned;
-      uint8_t* nxt = smem + ((it + 1) & 1) * L::kStageAligned;
+      uint8_t* cur = smem + (j & 1) * L::kStageAligned;
+      uint8_t* nxt = smem + ((j + 1) & 1) * L::kStageAligned;
       if (it + 1 < ntiles) dq_issue<D, HAS_MASK>(nxt, vbyte, p, b, kvh, it + 1, wave, lane, tid);
       const int tile0 = it * L::kBN;
-      if (wave_live && !(CAUSAL && tile0 > wave_last)) {
+      if (wave_live && !(CAUSAL && tile0 > wave_last) && !(DOCS && tile0 + L::kBN <= lo_wave)) {
         const uint8_t* ks = cur + L::kOffK;
         const uint8_t* vs = cur + L::kOffV;
         const uint8_t* vb = cur + L::kOffValid;
@@ -527,7 +618,9 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const BwdParams p) {
           // visible iff key < n, and key <= t if causal
           int lim = p.n - 1 - key0 - 4 * hh;
           if (CAUSAL) lim = min(lim, t - key0 - 4 * hh);
-          dq_half<D, HAS_MASK, SPLIT>(ks, vs, vb, half, lim, qf, df, lse2, dl, p.c, l32, hh, lane, dqa);
+          // documents: key >= the row's bound (no-op above the last row's bound)
+          const int lo = (DOCS && tile0 < lo_last) ? lo_row - key0 - 4 * hh : -0x7fffffff;
+          dq_half<D, HAS_MASK, SPLIT, DOCS>(ks, vs, vb, half, lim, lo, qf, df, lse2, dl, p.c, l32, hh, lane, dqa);
         }
       }
       if (HAS_MASK && it + 1 < ntiles && tid < L::kBN) nxt[L::kOffValid + tid] = uint8_t(vbyte);
@@ -548,8 +641,24 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const BwdParams p) {
         }
     }
   };
-  if (pb * p.pw < kSplitRows) run(std::true_type{});
+  if (pb * p.pw - lo_last < kSplitRows) run(std::true_type{});
   else run(std::false_type{});
+}
+
+template <int D, bool HAS_MASK, bool CAUSAL, bool DOCS>
+hipError_t launch_grads(const BwdParams& p, int64_t kv_blocks, int64_t q_blocks, hipStream_t stream) {
+  hipLaunchKernelGGL((dkdv_kernel<D, HAS_MASK, CAUSAL, DOCS>), dim3(kv_blocks), dim3(kThreads), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((dq_kernel<D, HAS_MASK, CAUSAL, DOCS>), dim3(q_blocks), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int D, bool HAS_MASK>
+hipError_t dispatch_grads(const BwdParams& p, int64_t kv_blocks, int64_t q_blocks, hipStream_t stream) {
+  if (p.doc_start != nullptr) return launch_grads<D, HAS_MASK, true, true>(p, kv_blocks, q_blocks, stream);
+  if (p.causal) return launch_grads<D, HAS_MASK, true, false>(p, kv_blocks, q_blocks, stream);
+  return launch_grads<D, HAS_MASK, false, false>(p, kv_blocks, q_blocks, stream);
 }
 
 template <int D>
@@ -562,37 +671,14 @@ hipError_t launch_bwd_d(const BwdParams& p, bool has_mask, bool o_f32, hipStream
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  // causal: one workgroup per pair of key blocks (nkb-1-w, w)
-  const int64_t kv_work = p.causal ? (int64_t(p.n_kblocks) + 1) / 2 : p.n_kblocks;
+  // causal: one workgroup per pair of key blocks (nkb-1-w, w); documents:
+  // one per key block
+  const int64_t kv_work = (p.causal && p.doc_start == nullptr) ? (int64_t(p.n_kblocks) + 1) / 2 : p.n_kblocks;
   const int64_t kv_blocks = kv_work * p.Hkv * p.B;
   const int64_t q_blocks = int64_t(p.n_pblocks) * p.n_hsub * p.Hkv * p.B;
   if (kv_blocks > 0x7fffffff || q_blocks > 0x7fffffff) return hipErrorInvalidValue;
-  if (has_mask) {
-    if (p.causal) {
-      hipLaunchKernelGGL((dkdv_kernel<D, true, true>), dim3(kv_blocks), dim3(kThreads), 0, stream, p);
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((dq_kernel<D, true, true>), dim3(q_blocks), dim3(kThreads), 0, stream, p);
-    } else {
-      hipLaunchKernelGGL((dkdv_kernel<D, true, false>), dim3(kv_blocks), dim3(kThreads), 0, stream, p);
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((dq_kernel<D, true, false>), dim3(q_blocks), dim3(kThreads), 0, stream, p);
-    }
-  } else {
-    if (p.causal) {
-      hipLaunchKernelGGL((dkdv_kernel<D, false, true>), dim3(kv_blocks), dim3(kThreads), 0, stream, p);
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((dq_kernel<D, false, true>), dim3(q_blocks), dim3(kThreads), 0, stream, p);
-    } else {
-      hipLaunchKernelGGL((dkdv_kernel<D, false, false>), dim3(kv_blocks), dim3(kThreads), 0, stream, p);
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((dq_kernel<D, false, false>), dim3(q_blocks), dim3(kThreads), 0, stream, p);
-    }
-  }
-  return hipGetLastError();
+  return has_mask ? dispatch_grads<D, true>(p, kv_blocks, q_blocks, stream)
+                  : dispatch_grads<D, false>(p, kv_blocks, q_blocks, stream);
 }
 
 }  // namespace
@@ -608,14 +694,16 @@ size_t row_array_bytes(int32_t B, int64_t n, int32_t Hq) {
 // Dl = dO . O, then the base-2 logsumexp
 size_t attn_bwd_workspace_bytes(int32_t B, int64_t n, int32_t Hq) { return 2 * row_array_bytes(B, n, Hq); }
 
-hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const uint8_t* valid, const void* o,
-                                const float* lse, const void* dout, float* dq, float* dk, float* dv,
-                                float* workspace, const AttnShape& s, int o_f32, hipStream_t stream) {
+hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const uint8_t* valid,
+                                const int32_t* doc_start, const void* o, const float* lse, const void* dout,
+                                float* dq, float* dk, float* dv, float* workspace, const AttnShape& s, int o_f32,
+                                hipStream_t stream) {
   BwdParams p;
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
   p.v = static_cast<const uint16_t*>(v);
   p.valid = valid;
+  p.doc_start = doc_start;
   p.o = o;
   p.lse = lse;
   p.dout = static_cast<const uint16_t*>(dout);

@@ -38,6 +38,11 @@
 //    the error of the few-key rows, whose weights are large, far below 1e-2.
 //  * The grid is launched longest-first (last query blocks first) so the
 //    causal triangle's long blocks do not trail at the end.
+//  * Packed documents (a per-row lower bound on the visible keys, the first
+//    position of the row's document): the workgroup starts at the tile that
+//    holds its first row's bound, so whole tiles of earlier documents are
+//    never loaded, and only tiles below its last row's bound take the
+//    per-row lower mask.
 #include <type_traits>
 
 #include "device_common.h"
@@ -71,6 +76,7 @@ struct FwdParams {
   const uint16_t* k;
   const uint16_t* v;
   const uint8_t* valid;
+  const int32_t* doc_start;   // [B][n] first position of each row's document, or null
   void* o;
   float* lse;
   int32_t B, n, Hq, Hkv;
@@ -103,8 +109,9 @@ __device__ __forceinline__ void fwd_issue(uint8_t* stage, uint32_t& vbyte, const
   }
 }
 
-template <int D, bool HAS_MASK, bool O_F32, bool CAUSAL>
+template <int D, bool HAS_MASK, bool O_F32, bool CAUSAL, bool DOCS>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const FwdParams p) {
+  static_assert(CAUSAL || !DOCS, "documents are causal");
   using L = FwdLayout<D>;
   constexpr int KK = D / 16;     // contraction slices of the score product
   constexpr int DJ = D / 32;     // 32-row blocks of O^T
@@ -137,6 +144,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const FwdPar
   const int ntiles = (kend + kBN - 1) / kBN;
   const bool wave_live = p0 < p.n;
 
+  // ---- packed documents: first tile, and the bounds of the lower mask
+  int it_first = 0;   // first tile holding a key any row of the workgroup sees
+  int lo_last = 0;    // bound of the last row: tiles below it need the lower mask
+  int lo_wave = 0;    // bound of the wave's first row: tiles below it are skipped
+  int lo_row = 0;     // bound of this lane's row
+  if (DOCS) {
+    const int32_t* rs = p.doc_start + int64_t(b) * p.n;
+    it_first = doc_lower(rs, pb * p.pw) / kBN;
+    lo_last = doc_lower(rs, wg_last);
+    lo_wave = wave_live ? doc_lower(rs, p0) : 0;
+    lo_row = t < p.n ? doc_lower(rs, t) : 0;
+  }
+
   // ---- Q fragment (B operand of S^T = K Q^T): lane holds row t, dims 16kk + 8hh .. +7
   u32x4 qf[KK];
   {
@@ -147,9 +167,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const FwdPar
       qf[kk] = ok ? *reinterpret_cast<const u32x4*>(p.q + off + 16 * kk) : u32x4{0, 0, 0, 0};
   }
 
-  // Rows below kSplitRows take the hi/lo path; the choice is made once per
-  // workgroup (its first row), outside the tile loop, so the loop body has
-  // no branch between its matrix instructions.
+  // Rows with fewer than kSplitRows visible keys take the hi/lo path; the
+  // choice is made once per workgroup, outside the tile loop, so the loop
+  // body has no branch between its matrix instructions.  Every row t of the
+  // workgroup sees at least (first row) - (last row's bound) keys.
   auto run = [&](auto split_tag) {
     constexpr bool SPLIT = decltype(split_tag)::value;
     f32x16 oacc[DJ];
@@ -159,7 +180,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const FwdPar
     float lsum = 0.f;          // this half-wave's share of the row sum
 
     uint32_t vbyte = 0;
-    fwd_issue<D, HAS_MASK>(smem, vbyte, p, b, kvh, 0, wave, lane, tid);
+    fwd_issue<D, HAS_MASK>(smem, vbyte, p, b, kvh, it_first, wave, lane, tid);
     if (HAS_MASK && tid < kBN) smem[L::kBytesK + L::kBytesV + tid] = uint8_t(vbyte);
     wait_vmem();
     __syncthreads();
@@ -172,7 +193,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const FwdPar
       if (it + 1 < ntiles) fwd_issue<D, HAS_MASK>(nxt, vbyte, p, b, kvh, it + 1, wave, lane, tid);
 
       const int tile0 = it * kBN;
-      if (wave_live && !(CAUSAL && tile0 > wave_last)) {
+      if (wave_live && !(CAUSAL && tile0 > wave_last) && !(DOCS && tile0 + kBN <= lo_wave)) {
         const uint8_t* ks = cur;
         const uint8_t* vs = cur + L::kBytesK;
 
@@ -198,15 +219,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const FwdPar
         }
         const bool diag = CAUSAL && (tile0 + kBN - 1 > p0);
         const bool tail = !CAUSAL && (tile0 + kBN > p.n);
-        if (diag || tail) {
+        const bool lower = DOCS && tile0 < lo_last;
+        if (diag || tail || lower) {
           // element i holds key tile0 + 4hh + C_i with C_i a compile-time constant;
-          // it is visible iff C_i <= lim.  Causal: key <= t (this also hides keys
-          // >= n, since t < n); otherwise only the tail limit key < n applies.
+          // it is visible iff lo <= C_i <= lim.  Causal: key <= t (this also hides
+          // keys >= n, since t < n); otherwise only the tail limit key < n
+          // applies.  Documents: key >= the row's bound.
           const int lim = (CAUSAL ? t : p.n - 1) - tile0 - 4 * hh;
+          const int lo = DOCS ? lo_row - tile0 - 4 * hh : -0x7fffffff;
 #pragma unroll
           for (int i = 0; i < 32; ++i) {
             const int ci = (i >> 4) * 32 + ((i & 15) >> 2) * 8 + (i & 3);
-            x[i] = (ci > lim) ? -INFINITY : x[i];
+            x[i] = (ci > lim || ci < lo) ? -INFINITY : x[i];
           }
         }
         if (HAS_MASK) {
@@ -285,7 +309,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const FwdPar
       wait_vmem();
       __syncthreads();
     };
-    int it = 0;
+    int it = it_first;
     for (; it + 1 < ntiles; it += 2) {
       tile(it, smem, smem + L::kStageAligned);
       tile(it + 1, smem + L::kStageAligned, smem);
@@ -318,20 +342,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const FwdPar
       }
     }
   };
-  if (pb * p.pw < kSplitRows) run(std::true_type{});
+  if (pb * p.pw - lo_last < kSplitRows) run(std::true_type{});
   else run(std::false_type{});
 }
 
-template <int D, bool HAS_MASK, bool O_F32, bool CAUSAL>
+template <int D, bool HAS_MASK, bool O_F32, bool CAUSAL, bool DOCS>
 hipError_t launch_fwd_t(const FwdParams& p, int blocks, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, HAS_MASK, O_F32, CAUSAL>), dim3(blocks), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, HAS_MASK, O_F32, CAUSAL, DOCS>), dim3(blocks), dim3(kThreads), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
 template <int D, bool HAS_MASK, bool O_F32>
 hipError_t dispatch_causal(const FwdParams& p, int blocks, hipStream_t stream) {
-  return p.causal ? launch_fwd_t<D, HAS_MASK, O_F32, true>(p, blocks, stream)
-                  : launch_fwd_t<D, HAS_MASK, O_F32, false>(p, blocks, stream);
+  if (p.doc_start != nullptr) return launch_fwd_t<D, HAS_MASK, O_F32, true, true>(p, blocks, stream);
+  return p.causal ? launch_fwd_t<D, HAS_MASK, O_F32, true, false>(p, blocks, stream)
+                  : launch_fwd_t<D, HAS_MASK, O_F32, false, false>(p, blocks, stream);
 }
 
 template <int D>
@@ -342,13 +368,15 @@ hipError_t dispatch_fwd(const FwdParams& p, int blocks, bool has_mask, bool o_f3
 
 }  // namespace
 
-hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, const uint8_t* valid, void* o,
-                                float* lse, const AttnShape& s, int o_f32, hipStream_t stream) {
+hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, const uint8_t* valid,
+                                const int32_t* doc_start, void* o, float* lse, const AttnShape& s, int o_f32,
+                                hipStream_t stream) {
   FwdParams p;
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
   p.v = static_cast<const uint16_t*>(v);
   p.valid = valid;
+  p.doc_start = doc_start;
   p.o = o;
   p.lse = lse;
   p.B = s.B;

@@ -10,7 +10,9 @@
 // one query row, each holding half of the head dimension; a workgroup of two
 // waves owns 64 rows of one query head and streams 32-key K/V tiles through
 // LDS.  The online softmax works per tile: scores for 32 keys, one max, one
-// rescale, then the weighted V accumulation.
+// rescale, then the weighted V accumulation.  With packed documents (a
+// per-row lower bound on the keys) the tile loop starts at the tile holding
+// the first row's bound.
 #include "device_common.h"
 #include "internal.h"
 
@@ -27,6 +29,7 @@ struct F32Params {
   const float* k;
   const float* v;
   const uint8_t* valid;
+  const int32_t* doc_start;   // [B][n] first position of each row's document, or null
   float* o;
   float* lse;
   int32_t B, n, Hq, Hkv, g;
@@ -35,7 +38,7 @@ struct F32Params {
   int32_t causal;
 };
 
-template <int D, bool HAS_MASK>
+template <int D, bool HAS_MASK, bool DOCS>
 __global__ __launch_bounds__(kF32Threads) void attn_fwd_f32_kernel(const F32Params p) {
   constexpr int DH = D / 2;
   __shared__ float ks[kF32Keys][D + 1];
@@ -56,6 +59,12 @@ __global__ __launch_bounds__(kF32Threads) void attn_fwd_f32_kernel(const F32Para
   const int t = rb * kF32Rows + wave * 32 + (lane & 31);
   const int wg_last = min(rb * kF32Rows + kF32Rows, p.n) - 1;
   const int kend = p.causal ? wg_last + 1 : p.n;
+  int kbeg = 0, lo_row = 0;
+  if (DOCS) {
+    const int32_t* rs = p.doc_start + int64_t(b) * p.n;
+    kbeg = doc_lower(rs, rb * kF32Rows) / kF32Keys * kF32Keys;
+    lo_row = t < p.n ? doc_lower(rs, t) : 0;
+  }
 
   float qv[DH], acc[DH];
   {
@@ -69,7 +78,7 @@ __global__ __launch_bounds__(kF32Threads) void attn_fwd_f32_kernel(const F32Para
   }
   float m = -INFINITY, lsum = 0.f;
 
-  for (int k0 = 0; k0 < kend; k0 += kF32Keys) {
+  for (int k0 = kbeg; k0 < kend; k0 += kF32Keys) {
     __syncthreads();
     for (int e = tid; e < kF32Keys * D; e += kF32Threads) {
       const int r = e / D, c = e % D;
@@ -101,7 +110,7 @@ __global__ __launch_bounds__(kF32Threads) void attn_fwd_f32_kernel(const F32Para
 #pragma unroll
     for (int j = 0; j < kF32Keys; ++j) {
       const int key = k0 + j;
-      const bool ok = okey[j] && !(p.causal && key > t);
+      const bool ok = okey[j] && !(p.causal && key > t) && !(DOCS && key < lo_row);
       s[j] = ok ? s[j] : -INFINITY;
       mt = fmaxf(mt, s[j]);
     }
@@ -132,10 +141,11 @@ __global__ __launch_bounds__(kF32Threads) void attn_fwd_f32_kernel(const F32Para
 
 }  // namespace
 
-hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, const uint8_t* valid, float* o,
-                               float* lse, const AttnShape& s, hipStream_t stream) {
+hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, const uint8_t* valid,
+                               const int32_t* doc_start, float* o, float* lse, const AttnShape& s,
+                               hipStream_t stream) {
   F32Params p;
-  p.q = q; p.k = k; p.v = v; p.valid = valid; p.o = o; p.lse = lse;
+  p.q = q; p.k = k; p.v = v; p.valid = valid; p.doc_start = doc_start; p.o = o; p.lse = lse;
   p.B = s.B; p.n = int32_t(s.n); p.Hq = s.Hq; p.Hkv = s.Hkv; p.g = s.Hq / s.Hkv;
   p.n_rblocks = int32_t((s.n + kF32Rows - 1) / kF32Rows);
   p.scale = s.scale;
@@ -144,12 +154,23 @@ hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, c
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   const bool m = valid != nullptr;
+  const bool docs = doc_start != nullptr;
   if (s.D == 128) {
-    if (m) hipLaunchKernelGGL((attn_fwd_f32_kernel<128, true>), dim3(blocks), dim3(kF32Threads), 0, stream, p);
-    else hipLaunchKernelGGL((attn_fwd_f32_kernel<128, false>), dim3(blocks), dim3(kF32Threads), 0, stream, p);
+    if (docs) {
+      if (m) hipLaunchKernelGGL((attn_fwd_f32_kernel<128, true, true>), dim3(blocks), dim3(kF32Threads), 0, stream, p);
+      else hipLaunchKernelGGL((attn_fwd_f32_kernel<128, false, true>), dim3(blocks), dim3(kF32Threads), 0, stream, p);
+    } else {
+      if (m) hipLaunchKernelGGL((attn_fwd_f32_kernel<128, true, false>), dim3(blocks), dim3(kF32Threads), 0, stream, p);
+      else hipLaunchKernelGGL((attn_fwd_f32_kernel<128, false, false>), dim3(blocks), dim3(kF32Threads), 0, stream, p);
+    }
   } else {
-    if (m) hipLaunchKernelGGL((attn_fwd_f32_kernel<64, true>), dim3(blocks), dim3(kF32Threads), 0, stream, p);
-    else hipLaunchKernelGGL((attn_fwd_f32_kernel<64, false>), dim3(blocks), dim3(kF32Threads), 0, stream, p);
+    if (docs) {
+      if (m) hipLaunchKernelGGL((attn_fwd_f32_kernel<64, true, true>), dim3(blocks), dim3(kF32Threads), 0, stream, p);
+      else hipLaunchKernelGGL((attn_fwd_f32_kernel<64, false, true>), dim3(blocks), dim3(kF32Threads), 0, stream, p);
+    } else {
+      if (m) hipLaunchKernelGGL((attn_fwd_f32_kernel<64, true, false>), dim3(blocks), dim3(kF32Threads), 0, stream, p);
+      else hipLaunchKernelGGL((attn_fwd_f32_kernel<64, false, false>), dim3(blocks), dim3(kF32Threads), 0, stream, p);
+    }
   }
   return hipGetLastError();
 }

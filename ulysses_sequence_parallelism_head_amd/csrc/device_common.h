@@ -56,6 +56,13 @@ __device__ __forceinline__ float halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Lower bound of the keys row t may see in a packed sequence of documents:
+// the first position of t's document, clamped to [0, t] so that no value of
+// the array can move an index out of its range.
+__device__ __forceinline__ int doc_lower(const int32_t* row_starts, int t) {
+  return min(max(row_starts[t], 0), t);
+}
+
 // Round-up division by an invariant 32-bit divisor (Granlund & Montgomery,
 // "Division by Invariant Integers using Multiplication", PLDI 1994):
 // q = (mulhi(n, m) + n) >> s, exact for every 32-bit n.

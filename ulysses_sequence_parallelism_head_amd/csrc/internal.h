@@ -20,19 +20,26 @@ struct AttnShape {
   int32_t causal;
 };
 
+// doc_start: NULL, or int32 [B][n] per-row lower bound of the visible keys
+// (the first position of the row's document) on top of the causal mask;
+// callers pass it only with s.causal == 1.
+
 // bf16 inputs, matrix cores; o_f32 selects a float32 (else bf16) output.
-hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, const uint8_t* valid, void* o,
-                                float* lse, const AttnShape& s, int o_f32, hipStream_t stream);
+hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, const uint8_t* valid,
+                                const int32_t* doc_start, void* o, float* lse, const AttnShape& s, int o_f32,
+                                hipStream_t stream);
 
 // float32 inputs and output, fp32 arithmetic throughout.
-hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, const uint8_t* valid, float* o,
-                               float* lse, const AttnShape& s, hipStream_t stream);
+hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, const uint8_t* valid,
+                               const int32_t* doc_start, float* o, float* lse, const AttnShape& s,
+                               hipStream_t stream);
 
 // bf16 inputs; o is bf16 or float32 (o_f32); gradients are float32.
-// workspace holds the per-row dO.O values, float32 [B][Hq][n].
-hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const uint8_t* valid, const void* o,
-                                const float* lse, const void* dout, float* dq, float* dk, float* dv,
-                                float* workspace, const AttnShape& s, int o_f32, hipStream_t stream);
+// workspace holds the per-row dO.O values and the base-2 logsumexp.
+hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const uint8_t* valid,
+                                const int32_t* doc_start, const void* o, const float* lse, const void* dout,
+                                float* dq, float* dk, float* dv, float* workspace, const AttnShape& s, int o_f32,
+                                hipStream_t stream);
 
 size_t attn_bwd_workspace_bytes(int32_t B, int64_t n, int32_t Hq);
 
