@@ -49,11 +49,25 @@ HBM_PEAK_GBS = 8000.0
 # summary is under profiles/), valid only for the kernel sources they were
 # measured on: the roofline reports null traffic once those sources change.
 CSRC = os.path.join(ROOT, "ulysses_sequence_parallelism_head_amd", "csrc")
-MEASURED_TRAFFIC = {      # keyed by (call, workload name)
-    ("attn_bwd", "gqa-n65536-8q2kv-d128-bf16-fwd+repack"): {"bytes": 6.515e9, "sources": ("attn_bwd.hip", "device_common.h", "internal.h"),
-                 "sha256": "e74095a5acdfd659993bbdcca95552639bbbb1c0884df0801237ea93ff1fe7cf"},
-    ("attn_fwd", "gqa-n65536-8q2kv-d128-bf16-fwd+repack"): {"bytes": 4.426e9, "sources": ("attn_fwd.hip", "device_common.h", "internal.h"),
-                 "sha256": "e8eb0fdda703015bea134c5e2744855f1b22a3469b90c4f616a11355c553965a"},
+MEASURED_TRAFFIC = {      # keyed by (call, workload as named in the config)
+    ("attn_bwd", "gqa-n65536-8q2kv-d128-bf16-fwd+repack"): {
+        "bytes": 6.534e9, "sources": ("attn_bwd.hip", "device_common.h", "internal.h"),
+        "sha256": "cca5ab10f05fd48592003a7e5aa58364d7eff8bf3c7a8c6ae6e79ebee76a8444"},
+    ("attn_fwd", "gqa-n65536-8q2kv-d128-bf16-fwd+repack"): {
+        "bytes": 3.138e9, "sources": ("attn_fwd.hip", "device_common.h", "internal.h"),
+        "sha256": "2fbec7078e7c52da64120cdbbbea628b7d4caea78f1b453938f62189c88b8bd0"},
+    ("attn_bwd", "gqa-n98304-8q2kv-d128-bf16-docs-fwd+bwd+document-mask"): {
+        "bytes": 8.870e9, "sources": ("attn_bwd.hip", "device_common.h", "internal.h"),
+        "sha256": "cca5ab10f05fd48592003a7e5aa58364d7eff8bf3c7a8c6ae6e79ebee76a8444"},
+    ("attn_fwd", "gqa-n98304-8q2kv-d128-bf16-docs-fwd+bwd+document-mask"): {
+        "bytes": 2.460e9, "sources": ("attn_fwd.hip", "device_common.h", "internal.h"),
+        "sha256": "2fbec7078e7c52da64120cdbbbea628b7d4caea78f1b453938f62189c88b8bd0"},
+    ("attn_bwd", "gqa-n98304-8q2kv-d128-bf16-docs-fwd+bwd"): {
+        "bytes": 12.620e9, "sources": ("attn_bwd.hip", "device_common.h", "internal.h"),
+        "sha256": "cca5ab10f05fd48592003a7e5aa58364d7eff8bf3c7a8c6ae6e79ebee76a8444"},
+    ("attn_fwd", "gqa-n98304-8q2kv-d128-bf16-docs-fwd+bwd"): {
+        "bytes": 6.344e9, "sources": ("attn_fwd.hip", "device_common.h", "internal.h"),
+        "sha256": "2fbec7078e7c52da64120cdbbbea628b7d4caea78f1b453938f62189c88b8bd0"},
 }
 
 
@@ -278,7 +292,7 @@ def main():
     achieved = dom_flops / (avg[dom] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                "traffic": measured_traffic(dom, w.name)}
+                "traffic": measured_traffic(dom, w.name + ("+document-mask" if args.docs else ""))}
 
     metric = "causal attn TFLOP/s @64K, 8q/2kv heads d128 bf16; % MFMA peak; repack GB/s"
     if args.docs:
