@@ -22,6 +22,10 @@ padding keys masked); adding ``--docs`` also applies the document mask (a
 token sees only earlier tokens of its own document, the ``*_docs`` calls),
 so the work is the tokens' own documents' pairs.  The flop count is always
 that of the visible (query, key) pairs, counted exactly from the masks.
+``--rope-loss`` runs the step as a model would around the path: Q and K go
+through the first exchange fused with the rotary embedding at global
+positions (base 1e6), V through the plain one, and the step ends with the
+valid-token-weighted loss aggregation over the P shards' token losses.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C] [--docs] [--no-cpu-baseline]
 Prints ONE JSON line on stdout.
@@ -135,6 +139,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--rope-loss", action="store_true",
+                    help="fuse the rotary embedding into Q/K's first exchange and aggregate the loss")
     ap.add_argument("--docs", action="store_true",
                     help="document-masked attention (workloads with packed documents only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -211,8 +217,18 @@ def main():
     dk_seq = torch.empty((P, 1, nl, w.Hkv_global, D), dtype=f32, device=dev)
     dv_seq = torch.empty((P, 1, nl, w.Hkv_global, D), dtype=f32, device=dev)
     ws = torch.empty(max(256, U.ulysses_attn_bwd_workspace_bytes(1, n, hq, hkv, D)), dtype=torch.uint8, device=dev)
+    rope_base = 1e6
+    if args.rope_loss:
+        # per-token losses of each rank's shard; counted where the key is valid
+        tok_loss = torch.from_numpy(np.abs(g[synth.STREAM_BITS].standard_normal((P, nl), dtype=np.float32))).to(dev)
+        tok_valid = None if valid_np is None else torch.from_numpy(valid_np.reshape(P, nl)).to(dev)
+        l_sum = torch.empty(P, dtype=torch.float64, device=dev)
+        l_cnt = torch.empty(P, dtype=torch.int64, device=dev)
+        l_val = torch.empty(1, dtype=torch.float32, device=dev)
 
     names = ["seq2head_qkv", "attn_fwd", "seq2head_do", "attn_bwd", "head2seq_o", "head2seq_dqkv"]
+    if args.rope_loss:
+        names.append("loss_aggregate")
     Ev = torch.cuda.Event
 
     def step(events=None):
@@ -220,8 +236,12 @@ def main():
             if events is not None:
                 events[i].record()
         mark(0)
-        U.ulysses_repack_seq2head(q_seq, q_h)
-        U.ulysses_repack_seq2head(k_seq, k_h)
+        if args.rope_loss:
+            U.ulysses_repack_seq2head_rope(q_seq, rope_base, out=q_h)
+            U.ulysses_repack_seq2head_rope(k_seq, rope_base, out=k_h)
+        else:
+            U.ulysses_repack_seq2head(q_seq, q_h)
+            U.ulysses_repack_seq2head(k_seq, k_h)
         U.ulysses_repack_seq2head(v_seq, v_h)
         mark(1)
         if ds_t is None:
@@ -244,6 +264,9 @@ def main():
         U.ulysses_repack_head2seq(dk_h, dk_seq)
         U.ulysses_repack_head2seq(dv_h, dv_seq)
         mark(6)
+        if args.rope_loss:
+            U.ulysses_loss_aggregate(tok_loss, tok_valid, l_sum, l_cnt, l_val)
+            mark(7)
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -252,7 +275,8 @@ def main():
 
     log(f"[bench] timing {args.steps} steps")
     per = {k: [] for k in names}
-    evs = [[Ev(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    nev = len(names) + 1
+    evs = [[Ev(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
@@ -264,7 +288,7 @@ def main():
         e = evs[s]
         for i, k in enumerate(names):
             per[k].append(e[i].elapsed_time(e[i + 1]))
-        step_ms.append(e[0].elapsed_time(e[6]))
+        step_ms.append(e[0].elapsed_time(e[nev - 1]))
     ms_step = wall * 1e3 / args.steps
     avg = {k: float(np.mean(v)) for k, v in per.items()}
 
@@ -297,6 +321,8 @@ def main():
     metric = "causal attn TFLOP/s @64K, 8q/2kv heads d128 bf16; % MFMA peak; repack GB/s"
     if args.docs:
         metric = f"document-masked causal attn TFLOP/s @{n // 1024}K, {hq}q/{hkv}kv heads d{D} bf16"
+    if args.rope_loss:
+        metric += " (rotary embedding fused into the first exchange, loss aggregation)"
     elif w.number != 3:
         metric = f"causal attn TFLOP/s @{n // 1024}K, {hq}q/{hkv}kv heads d{D} bf16"
     result = {
@@ -315,6 +341,7 @@ def main():
         "config": {"workload": w.name + ("+document-mask" if args.docs else ""), "n": n, "P": P, "q_heads": hq,
                    "kv_heads": hkv, "head_dim": D, "global_q_shape": [P, 1, nl, w.Hq_global, D], "causal": True,
                    "padding_mask": valid_np is not None, "document_mask": bool(args.docs),
+                   "rope_fused": bool(args.rope_loss), "loss_aggregation": bool(args.rope_loss),
                    "visible_pairs_per_head": pairs},
         "breakdown_ms": {k: round(v, 4) for k, v in avg.items()},
         "attn_fwd_tflops": round(fwd_tf, 2),

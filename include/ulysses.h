@@ -13,12 +13,16 @@
  *                                               (ulysses_repack_head2seq)
  * and, for packed sequences of variable-length documents, the attention
  * calls with a document mask (ulysses_attn_fwd_docs, ulysses_attn_bwd_docs).
+ * Beside the path: the first exchange fused with the rotary position
+ * embedding at global positions (ulysses_repack_seq2head_rope), and the
+ * loss aggregated over shards by valid tokens (ulysses_loss_aggregate).
  *
  * Sources (web pages, cited by title and section):
  *   [ALST]  "Paralelismul de Secvență Ulysses: Antrenarea modelelor AI cu
  *           contexte de un milion de token-uri" (world.tibi.club)
  *   [HFSUM] "Ulysses 序列平行化：突破百萬標記長上下文的訓練瓶頸"
  *           (agents-report.net)
+ *   [SWIFT] "ms-swift性能优化：Ulysses并行技术降低长文本显存" (hotelren.com)
  *
  * Conventions shared by every call
  * --------------------------------
@@ -270,6 +274,68 @@ ULYSSES_API ulysses_status_t ulysses_attn_bwd_docs(const void* q, const void* k,
                                        float softmax_scale,
                                        ulysses_dtype_t in_dtype, ulysses_dtype_t o_dtype,
                                        void* stream);
+
+/*
+ * ulysses_repack_seq2head_rope -- ulysses_repack_seq2head with the rotary
+ * position embedding applied on the way, at each token's global position.
+ *
+ * Source: the rotary encoding must follow a shard's offset in the sequence
+ * ([SWIFT] section "6. 使用建议与避坑指南", troubleshooting table: repeated
+ * tokens when it does not; linear position scaling named as a workaround);
+ * shards are contiguous ([ALST] "Mecanismul de funcționare Ulysses", step
+ * 1), so rank i's local token s has global position pos = i*n_local + s.
+ * The rotation (not on the pages; the form of the pages' Qwen models) pairs
+ * dimension d with d + D/2, for d in [0, D/2):
+ *   theta = (pos / rope_scale) * rope_base^(-2d/D)
+ *   out[d]       = x[d] cos(theta) - x[d+D/2] sin(theta)
+ *   out[d+D/2]   = x[d+D/2] cos(theta) + x[d] sin(theta)
+ * then out lands where ulysses_repack_seq2head would put x:
+ *   dst[j][b][i*n_local + s][h][c] = out(src[i][b][s][j*H/P + h])[c]
+ *
+ *   src, dst   as for ulysses_repack_seq2head (Q or K; V takes the plain call)
+ *   rope_base  rotary base (> 0, finite; 1e6 for the workloads' Qwen heads)
+ *   rope_scale linear position scaling factor (> 0, finite; 1 = none)
+ *
+ * Arithmetic: angles in double precision (reduced to [-pi, pi] before the
+ * sine and cosine), the rotation in float32, one rounding to dtype.
+ * Built: dtype BF16 or F32, D 64 or 128.
+ * Errors: as ulysses_repack_seq2head, plus INVALID_ARG for a base or scale
+ * that is not finite and positive and for src/dst not 16-byte aligned;
+ * UNSUPPORTED for other D, n_local >= 2^31 or P*B*n_local >= 2^37.
+ */
+ULYSSES_API ulysses_status_t ulysses_repack_seq2head_rope(const void* src, void* dst,
+                                              int32_t P, int32_t B, int64_t n_local,
+                                              int32_t H, int32_t D,
+                                              double rope_base, double rope_scale,
+                                              ulysses_dtype_t dtype, void* stream);
+
+/*
+ * ulysses_loss_aggregate -- the loss of a sequence split over P ranks,
+ * weighted by each rank's valid tokens.
+ *
+ * Source: [ALST] section "Integrarea cu Accelerate" (each rank's loss covers
+ * its part of the sequence; the losses are combined weighted by the number
+ * of valid tokens per rank, padding and masked prompt tokens excluded) and
+ * section "Cele mai bune practici și recomandări", item 6.
+ *
+ *   token_loss [P][per_rank] float32   per-token losses of each rank's shard
+ *                                      (per_rank = B * n_local)
+ *   valid      [P][per_rank] uint8     nonzero = counted, or NULL (all counted)
+ *   rank_sum   [P] float64  (output)   sum of rank r's counted losses
+ *   rank_count [P] int64    (output)   number of rank r's counted tokens
+ *   loss       [1] float32  (output)   sum of rank_sum / sum of rank_count,
+ *                                      NaN when nothing is counted
+ *
+ * Sums are accumulated in double precision in a fixed order (deterministic).
+ * Errors: INVALID_ARG for P < 1 or P > 65535, per_rank < 0, a null output,
+ * a null token_loss with per_rank > 0, misalignment (token_loss and loss 4
+ * bytes, rank_sum and rank_count 8), or an output overlapping an input or
+ * another output.
+ */
+ULYSSES_API ulysses_status_t ulysses_loss_aggregate(const float* token_loss, const uint8_t* valid,
+                                        int32_t P, int64_t per_rank,
+                                        double* rank_sum, int64_t* rank_count, float* loss,
+                                        void* stream);
 
 #ifdef __cplusplus
 }

@@ -149,3 +149,28 @@ def test_docs_validation(lib):
     assert _bwd_docs(lib, docs=None) == INVALID
     assert _bwd_docs(lib, dq=ctypes.c_void_p(0xA000000 - 4096)) == INVALID   # dq overlaps doc_start
     assert _bwd_docs(lib, n=0, docs=None) == OK
+
+
+def test_rope_validation(lib):
+    f = lib.ulysses_repack_seq2head_rope
+    assert f(FAKE, FAKE2, 4, 1, 16, 6, 128, 1e6, 1.0, BF16, None) == INVALID          # H % P != 0
+    assert f(FAKE, FAKE2, 4, 1, 16, 32, 96, 1e6, 1.0, BF16, None) == UNSUPPORTED      # D
+    assert f(FAKE, FAKE2, 4, 1, 16, 32, 128, 0.0, 1.0, BF16, None) == INVALID         # base
+    assert f(FAKE, FAKE2, 4, 1, 16, 32, 128, float("nan"), 1.0, BF16, None) == INVALID
+    assert f(FAKE, FAKE2, 4, 1, 16, 32, 128, 1e6, -2.0, BF16, None) == INVALID        # scale
+    assert f(FAKE, FAKE2, 4, 1, 16, 32, 128, 1e6, 1.0, 7, None) == INVALID            # dtype
+    assert f(FAKE, ctypes.c_void_p(0x10000 + 64), 4, 1, 16, 32, 128, 1e6, 1.0, BF16, None) == INVALID   # overlap
+    assert f(ctypes.c_void_p(0x10008), FAKE2, 4, 1, 16, 32, 128, 1e6, 1.0, BF16, None) == INVALID       # alignment
+    assert f(None, None, 4, 0, 16, 32, 128, 1e6, 1.0, BF16, None) == OK               # empty
+
+
+def test_loss_validation(lib):
+    f = lib.ulysses_loss_aggregate
+    S, C, L = ctypes.c_void_p(0x5000000), ctypes.c_void_p(0x6000000), ctypes.c_void_p(0x7000000)
+    assert f(FAKE, None, 0, 10, S, C, L, None) == INVALID                     # P < 1
+    assert f(FAKE, None, 2, -1, S, C, L, None) == INVALID                     # per_rank < 0
+    assert f(None, None, 2, 10, S, C, L, None) == INVALID                     # token_loss required
+    assert f(FAKE, None, 2, 10, None, C, L, None) == INVALID                  # outputs required
+    assert f(FAKE, None, 2, 10, ctypes.c_void_p(0x5000004), C, L, None) == INVALID   # rank_sum alignment
+    assert f(FAKE, None, 2, 10, S, ctypes.c_void_p(0x5000008), L, None) == INVALID   # overlapping outputs
+    assert f(FAKE, None, 2, 10, ctypes.c_void_p(0x10000 + 8), C, L, None) == INVALID  # output overlaps input

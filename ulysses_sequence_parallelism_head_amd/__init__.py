@@ -62,6 +62,11 @@ _SIGS = {
                                              ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                              ctypes.c_int32, ctypes.c_float, ctypes.c_int, ctypes.c_int,
                                              ctypes.c_void_p]),
+    "ulysses_repack_seq2head_rope": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                                    ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_double,
+                                                    ctypes.c_double, ctypes.c_int, ctypes.c_void_p]),
+    "ulysses_loss_aggregate": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
 }
 
 EXPORTED = tuple(_SIGS)
@@ -151,6 +156,48 @@ def ulysses_repack_head2seq(src: torch.Tensor, out: torch.Tensor | None = None) 
     _check(lib.ulysses_repack_head2seq(_ptr(src), _ptr(out), P, B, nl, H, D, _dtype_code(src), _stream(src.device)),
            "ulysses_repack_head2seq")
     return out
+
+
+def ulysses_repack_seq2head_rope(src: torch.Tensor, rope_base: float, rope_scale: float = 1.0,
+                                 out: torch.Tensor | None = None) -> torch.Tensor:
+    """Like :func:`ulysses_repack_seq2head`, rotating each head vector at its
+    token's global position on the way (Q and K before the first exchange)."""
+    lib = load_library()
+    _need_contig_cuda(src, out)
+    P, B, nl, H, D = src.shape
+    if H % P != 0 or H < P:
+        _check(ERR_INVALID_ARG, "ulysses_repack_seq2head_rope")
+    if out is None:
+        out = torch.empty((P, B, P * nl, H // P, D), dtype=src.dtype, device=src.device)
+    elif tuple(out.shape) != (P, B, P * nl, H // P, D) or out.dtype != src.dtype:
+        raise ValueError("out has the wrong shape or dtype")
+    _check(lib.ulysses_repack_seq2head_rope(_ptr(src), _ptr(out), P, B, nl, H, D, float(rope_base), float(rope_scale),
+                                            _dtype_code(src), _stream(src.device)),
+           "ulysses_repack_seq2head_rope")
+    return out
+
+
+def ulysses_loss_aggregate(token_loss: torch.Tensor, valid: torch.Tensor | None = None, rank_sum=None,
+                           rank_count=None, loss=None):
+    """token_loss float32 ``[P][...]`` (one row of per-token losses per rank),
+    valid uint8 of the same shape or None.  Returns ``(rank_sum float64 [P],
+    rank_count int64 [P], loss float32 [1])``."""
+    lib = load_library()
+    _need_contig_cuda(token_loss, valid, rank_sum, rank_count, loss)
+    if token_loss.dtype != torch.float32:
+        raise ValueError("token_loss must be float32")
+    if valid is not None and (valid.dtype != torch.uint8 or valid.shape != token_loss.shape):
+        raise ValueError("valid must be uint8 with token_loss's shape")
+    P = token_loss.shape[0]
+    per_rank = token_loss.numel() // P if P else 0
+    dev = token_loss.device
+    rank_sum = torch.empty(P, dtype=torch.float64, device=dev) if rank_sum is None else rank_sum
+    rank_count = torch.empty(P, dtype=torch.int64, device=dev) if rank_count is None else rank_count
+    loss = torch.empty(1, dtype=torch.float32, device=dev) if loss is None else loss
+    _check(lib.ulysses_loss_aggregate(_ptr(token_loss), _ptr(valid), P, per_rank, _ptr(rank_sum), _ptr(rank_count),
+                                      _ptr(loss), _stream(dev)),
+           "ulysses_loss_aggregate")
+    return rank_sum, rank_count, loss
 
 
 def _check_docs(doc_start, B, n):
@@ -252,5 +299,5 @@ def _attn_bwd(q, k, v, o, lse, dout, key_valid, doc_start, softmax_scale, causal
 __all__ = [
     "load_library", "EXPORTED", "LIB_PATH", "ulysses_abi_version", "ulysses_repack_seq2head",
     "ulysses_repack_head2seq", "ulysses_attn_fwd", "ulysses_attn_bwd", "ulysses_attn_bwd_workspace_bytes",
-    "ulysses_attn_fwd_docs", "ulysses_attn_bwd_docs",
+    "ulysses_attn_fwd_docs", "ulysses_attn_bwd_docs", "ulysses_repack_seq2head_rope", "ulysses_loss_aggregate",
 ]

@@ -206,4 +206,45 @@ ulysses_status_t ulysses_attn_bwd_docs(const void* q, const void* k, const void*
                   D, softmax_scale, 1, in_dtype, o_dtype, stream);
 }
 
+ulysses_status_t ulysses_repack_seq2head_rope(const void* src, void* dst, int32_t P, int32_t B, int64_t n_local,
+                                              int32_t H, int32_t D, double rope_base, double rope_scale,
+                                              ulysses_dtype_t dtype, void* stream) {
+  if (P < 1 || B < 0 || n_local < 0 || H < 1 || D < 1) return ULYSSES_ERR_INVALID_ARG;
+  if (H < P || H % P != 0) return ULYSSES_ERR_INVALID_ARG;
+  if (!known_dtype(dtype)) return ULYSSES_ERR_INVALID_ARG;
+  if (!isfinite(rope_base) || !(rope_base > 0.0) || !isfinite(rope_scale) || !(rope_scale > 0.0))
+    return ULYSSES_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return ULYSSES_ERR_UNSUPPORTED;
+  if (B == 0 || n_local == 0) return ULYSSES_OK;
+  if (src == nullptr || dst == nullptr) return ULYSSES_ERR_INVALID_ARG;
+  if (!aligned(src, 16) || !aligned(dst, 16)) return ULYSSES_ERR_INVALID_ARG;
+  if (n_local >= (int64_t(1) << 31) || int64_t(P) * B * n_local >= (int64_t(1) << 37)) return ULYSSES_ERR_UNSUPPORTED;
+  const uint64_t total = uint64_t(P) * uint64_t(B) * uint64_t(n_local) * uint64_t(H) * uint64_t(D) * elem_size(dtype);
+  if (overlap(src, total, dst, total)) return ULYSSES_ERR_INVALID_ARG;
+  return from_hip(ulysses::launch_seq2head_rope(src, dst, P, B, int32_t(n_local), H, D, int(elem_size(dtype)),
+                                                rope_base, rope_scale, static_cast<hipStream_t>(stream)));
+}
+
+ulysses_status_t ulysses_loss_aggregate(const float* token_loss, const uint8_t* valid, int32_t P, int64_t per_rank,
+                                        double* rank_sum, int64_t* rank_count, float* loss, void* stream) {
+  if (P < 1 || P > 65535 || per_rank < 0) return ULYSSES_ERR_INVALID_ARG;
+  if (rank_sum == nullptr || rank_count == nullptr || loss == nullptr) return ULYSSES_ERR_INVALID_ARG;
+  if (per_rank > 0 && token_loss == nullptr) return ULYSSES_ERR_INVALID_ARG;
+  if (!aligned(token_loss, 4) || !aligned(rank_sum, 8) || !aligned(rank_count, 8) || !aligned(loss, 4))
+    return ULYSSES_ERR_INVALID_ARG;
+  const uint64_t nt = uint64_t(P) * uint64_t(per_rank);
+  const void* ins[2] = {token_loss, per_rank > 0 ? valid : nullptr};
+  const uint64_t inb[2] = {nt * 4, valid ? nt : 0};
+  const void* outs[3] = {rank_sum, rank_count, loss};
+  const uint64_t outb[3] = {uint64_t(P) * 8, uint64_t(P) * 8, 4};
+  for (int a = 0; a < 3; ++a) {
+    for (int i = 0; i < 2; ++i)
+      if (overlap(outs[a], outb[a], ins[i], inb[i])) return ULYSSES_ERR_INVALID_ARG;
+    for (int c = a + 1; c < 3; ++c)
+      if (overlap(outs[a], outb[a], outs[c], outb[c])) return ULYSSES_ERR_INVALID_ARG;
+  }
+  return from_hip(ulysses::launch_loss_aggregate(token_loss, per_rank > 0 ? valid : nullptr, P, per_rank, rank_sum,
+                                                 rank_count, loss, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -16,14 +16,14 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// Round two floats to bfloat16 (nearest, ties to even) and pack them
-// little-endian into one 32-bit word: `lo` in bits 0..15.
 // acc + (low bf16 of w) + (high bf16 of w), one v_dot2 with ones
 __device__ __forceinline__ float sum_bf16x2(uint32_t w, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, 0x3f803f80u), acc,
                                          false);
 }
 
+// Round two floats to bfloat16 (nearest, ties to even) and pack them
+// little-endian into one 32-bit word: `lo` in bits 0..15.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   f32x2 f = {lo, hi};
   bf16x2 b = __builtin_convertvector(f, bf16x2);

@@ -43,4 +43,13 @@ hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, con
 
 size_t attn_bwd_workspace_bytes(int32_t B, int64_t n, int32_t Hq);
 
+// seq2head fused with the rotary embedding at global positions; elem_bytes
+// 2 (bf16) or 4 (fp32), D 64 or 128, H % P == 0.
+hipError_t launch_seq2head_rope(const void* src, void* dst, int32_t P, int32_t B, int32_t n_local, int32_t H,
+                                int32_t D, int elem_bytes, double base, double scale, hipStream_t stream);
+
+// per-rank sums and counts of the valid tokens' losses, and their ratio
+hipError_t launch_loss_aggregate(const float* token_loss, const uint8_t* valid, int32_t P, int64_t per_rank,
+                                 double* rank_sum, int64_t* rank_count, float* loss, hipStream_t stream);
+
 }  // namespace ulysses
