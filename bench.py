@@ -26,6 +26,11 @@ that of the visible (query, key) pairs, counted exactly from the masks.
 through the first exchange fused with the rotary embedding at global
 positions (base 1e6), V through the plain one, and the step ends with the
 valid-token-weighted loss aggregation over the P shards' token losses.
+``--ring`` times the ring-attention alternative instead (forward only): each
+of the P emulated ranks keeps all heads of its query shard and merges the
+key/value shards of its hops with ``ulysses_attn_fwd_block``; the same
+attention is timed the Ulysses way (P head-shard forwards over the whole
+sequence) beside it.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C] [--docs] [--no-cpu-baseline]
 Prints ONE JSON line on stdout.
@@ -133,6 +138,86 @@ def cpu_baseline(workload, docs: bool, budget_s: float = 12.0):
                       f"(fp64 NumPy, {spent:.1f} s)"}
 
 
+def bench_ring(args, w):
+    """Ring attention (forward) on P emulated ranks against Ulysses' forward
+    of the same attention; one JSON line."""
+    import torch
+    import synth
+    import ulysses_sequence_parallelism_head_amd as U
+    dev = torch.device("cuda:0")
+    P, nl, n, D = w.P, w.n_local, w.n, w.D
+    g = synth.streams(w.number)
+
+    def dev_bits(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    log(f"[bench] ring emulation, workload {w.name}")
+    q_seq = dev_bits(synth.normal_bf16(g[synth.STREAM_Q], (P, 1, nl, w.Hq_global, D)))
+    k_seq = dev_bits(synth.normal_bf16(g[synth.STREAM_K], (P, 1, nl, w.Hkv_global, D)))
+    v_seq = dev_bits(synth.normal_bf16(g[synth.STREAM_V], (P, 1, nl, w.Hkv_global, D)))
+    o_ring = torch.empty((P, 1, nl, w.Hq_global, D), dtype=torch.float32, device=dev)
+    l_ring = torch.empty((P, 1, w.Hq_global, nl), dtype=torch.float32, device=dev)
+    q_h = U.ulysses_repack_seq2head(q_seq)
+    k_h = U.ulysses_repack_seq2head(k_seq)
+    v_h = U.ulysses_repack_seq2head(v_seq)
+    o_uly = torch.empty((P, 1, n, w.hq, D), dtype=torch.float32, device=dev)
+    l_uly = torch.empty((P, 1, w.hq, n), dtype=torch.float32, device=dev)
+    hops = [(i, j) for i in range(P) for j in ((i - h) % P for h in range(P)) if j <= i]
+
+    def ring():
+        for i, j in hops:
+            U.ulysses_attn_fwd_block(q_seq[i], k_seq[j], v_seq[j], o_ring[i], l_ring[i], (i - j) * nl, None,
+                                     w.scale, True, accumulate=j != i)
+
+    def ulysses():
+        for j in range(P):
+            U.ulysses_attn_fwd(q_h[j], k_h[j], v_h[j], None, w.scale, True, o_dtype=torch.float32,
+                               out=o_uly[j], lse=l_uly[j])
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        t0 = time.perf_counter()
+        e[0].record()
+        for s_ in range(args.steps):
+            fn()
+            e[s_ + 1].record()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / args.steps
+        return wall * 1e3, [e[s_].elapsed_time(e[s_ + 1]) for s_ in range(args.steps)]
+
+    ms_ring, per_ring = timed(ring)
+    ms_uly, _ = timed(ulysses)
+    flops = 4.0 * D * w.Hq_global * float(visible_keys(n).sum())
+    ring_tf = flops / (np.mean(per_ring) * 1e-3) / 1e12
+    result = {
+        "metric": f"ring-attention emulation: causal attn fwd TFLOP/s @{n // 1024}K, {w.Hq_global}q/{w.Hkv_global}kv "
+                  f"heads d{D} bf16 on P={P} ranks",
+        "value": round(flops / (ms_ring * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_ring, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name + "+ring", "n": n, "P": P, "q_heads": w.Hq_global, "kv_heads": w.Hkv_global,
+                   "head_dim": D, "hops_launched": len(hops), "causal": True},
+        "ring_fwd_ms": round(ms_ring, 3),
+        "ulysses_fwd_all_ranks_ms": round(ms_uly, 3),
+        "ring_over_ulysses_time": round(ms_ring / ms_uly, 4),
+        "roofline": {"bound": "mfma", "kernel": "attn_fwd_block (all hops of all ranks)", "achieved": round(ring_tf, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(ring_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None},
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -141,6 +226,7 @@ def main():
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--rope-loss", action="store_true",
                     help="fuse the rotary embedding into Q/K's first exchange and aggregate the loss")
+    ap.add_argument("--ring", action="store_true", help="time the ring-attention emulation (forward)")
     ap.add_argument("--docs", action="store_true",
                     help="document-masked attention (workloads with packed documents only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -183,6 +269,9 @@ def main():
         print(f"--docs needs a workload with packed documents (workload {w.number} has none)", file=sys.stderr)
         sys.exit(2)
 
+    if args.ring:
+        bench_ring(args, w)
+        return
     log(f"[bench] generating workload {w.name}")
     g = synth.streams(w.number)
 

@@ -13,6 +13,9 @@
  *                                               (ulysses_repack_head2seq)
  * and, for packed sequences of variable-length documents, the attention
  * calls with a document mask (ulysses_attn_fwd_docs, ulysses_attn_bwd_docs).
+ * For the ring-attention alternative the pages compare against, the
+ * forward over one separate key block with an exact merge of partial
+ * results (ulysses_attn_fwd_block).
  * Beside the path: the first exchange fused with the rotary position
  * embedding at global positions (ulysses_repack_seq2head_rope), and the
  * loss aggregated over shards by valid tokens (ulysses_loss_aggregate).
@@ -274,6 +277,46 @@ ULYSSES_API ulysses_status_t ulysses_attn_bwd_docs(const void* q, const void* k,
                                        float softmax_scale,
                                        ulysses_dtype_t in_dtype, ulysses_dtype_t o_dtype,
                                        void* stream);
+
+/*
+ * ulysses_attn_fwd_block -- the forward of ulysses_attn_fwd over one
+ * separate block of keys, optionally merged into a running result: the
+ * step a rank of Ring Attention takes at each hop.
+ *
+ * Source: Ring Attention keeps each rank's query shard and passes the
+ * key/value shards around a ring in P - 1 point-to-point hops ([HFSUM]
+ * section "與 Ring Attention 的比較"; [ALST] sections "Complexitatea
+ * comunicațională" and "Comparând Ulysses cu Ring Attention").  The pages
+ * do not say how the hops' results combine; the exact combination of
+ * softmax attentions over disjoint key sets is used:
+ *   L = ln(e^L_old + e^L_blk),  O = e^(L_old - L) O_old + e^(L_blk - L) O_blk
+ *
+ * For batch b, query head h (KV head h / (Hq/Hkv)), block row t:
+ *   allowed keys u of the block: (u <= t + causal_offset if causal) and
+ *   (key_valid == NULL or key_valid[b][u] != 0)
+ * and O_blk, L_blk are the attention and logsumexp over those keys (a row
+ * with none gets O_blk = 0, L_blk = -inf).  For query rows at global
+ * positions q0.. and keys at k0.., causal_offset = q0 - k0.
+ *
+ *   q          [B][nq][Hq][D]   bf16
+ *   k, v       [B][nk][Hkv][D]  bf16
+ *   key_valid  [B][nk] uint8 or NULL
+ *   o          [B][nq][Hq][D]   float32  accumulate = 0: overwritten with O_blk;
+ *                                        accumulate = 1: holds O_old, replaced by O
+ *   lse        [B][Hq][nq]      float32  likewise L_blk, or L_old -> L (natural log)
+ *   causal_offset  any value; values past [-nq, nk] act as the nearest end
+ *   causal     1: the mask above; 0: every key of the block is visible
+ *
+ * Built: bf16 inputs, D 64 or 128 (the bf16 forward's kernels).
+ * Errors: as ulysses_attn_fwd (with nq as n), plus INVALID_ARG for nk < 1
+ * or accumulate not 0/1; UNSUPPORTED for float32 inputs or nq + nk >= 2^31.
+ */
+ULYSSES_API ulysses_status_t ulysses_attn_fwd_block(const void* q, const void* k, const void* v,
+                                        const uint8_t* key_valid, float* o, float* lse,
+                                        int32_t B, int64_t nq, int64_t nk, int32_t Hq, int32_t Hkv,
+                                        int32_t D, float softmax_scale, int64_t causal_offset,
+                                        int32_t causal, int32_t accumulate,
+                                        ulysses_dtype_t in_dtype, void* stream);
 
 /*
  * ulysses_repack_seq2head_rope -- ulysses_repack_seq2head with the rotary

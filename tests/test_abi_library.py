@@ -174,3 +174,19 @@ def test_loss_validation(lib):
     assert f(FAKE, None, 2, 10, ctypes.c_void_p(0x5000004), C, L, None) == INVALID   # rank_sum alignment
     assert f(FAKE, None, 2, 10, S, ctypes.c_void_p(0x5000008), L, None) == INVALID   # overlapping outputs
     assert f(FAKE, None, 2, 10, ctypes.c_void_p(0x10000 + 8), C, L, None) == INVALID  # output overlaps input
+
+
+def test_block_validation(lib):
+    f = lib.ulysses_attn_fwd_block
+    O, LS = ctypes.c_void_p(0x3000000), ctypes.c_void_p(0x4000000)
+    def call(nk=64, acc=0, it=BF16, causal=1, o=O, D=128, nq=64):
+        return f(FAKE, ctypes.c_void_p(0x1000000), ctypes.c_void_p(0x2000000), None, o, LS, 1, nq, nk, 8, 2, D, 0.1,
+                 5, causal, acc, it, None)
+    assert call(nk=0) == INVALID
+    assert call(acc=2) == INVALID
+    assert call(causal=3) == INVALID
+    assert call(it=F32) == UNSUPPORTED
+    assert call(D=96) == UNSUPPORTED
+    assert call(nk=(1 << 31) - 100) == UNSUPPORTED
+    assert call(o=ctypes.c_void_p(0x1000000 + 256)) == INVALID     # o overlaps k
+    assert call(nq=0) == OK                                        # empty

@@ -62,6 +62,11 @@ _SIGS = {
                                              ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                              ctypes.c_int32, ctypes.c_float, ctypes.c_int, ctypes.c_int,
                                              ctypes.c_void_p]),
+    "ulysses_attn_fwd_block": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                              ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                              ctypes.c_float, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                              ctypes.c_int, ctypes.c_void_p]),
     "ulysses_repack_seq2head_rope": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                                     ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_double,
                                                     ctypes.c_double, ctypes.c_int, ctypes.c_void_p]),
@@ -156,6 +161,27 @@ def ulysses_repack_head2seq(src: torch.Tensor, out: torch.Tensor | None = None) 
     _check(lib.ulysses_repack_head2seq(_ptr(src), _ptr(out), P, B, nl, H, D, _dtype_code(src), _stream(src.device)),
            "ulysses_repack_head2seq")
     return out
+
+
+def ulysses_attn_fwd_block(q, k, v, o, lse, causal_offset: int, key_valid=None, softmax_scale=None,
+                           causal: bool = True, accumulate: bool = False):
+    """Forward of the bf16 rows ``q`` ``[B][nq][Hq][D]`` over the key block
+    ``k``/``v`` ``[B][nk][Hkv][D]`` (key u visible to row t iff
+    u <= t + causal_offset when causal).  ``o`` (float32 ``[B][nq][Hq][D]``)
+    and ``lse`` (float32 ``[B][Hq][nq]``) are overwritten, or merged into
+    when ``accumulate``.  Returns ``(o, lse)``."""
+    lib = load_library()
+    _need_contig_cuda(q, k, v, o, lse, key_valid)
+    B, nq, Hq, D = q.shape
+    nk, Hkv = k.shape[1], k.shape[2]
+    if o.dtype != torch.float32 or lse.dtype != torch.float32:
+        raise ValueError("o and lse must be float32")
+    scale = D ** -0.5 if softmax_scale is None else float(softmax_scale)
+    _check(lib.ulysses_attn_fwd_block(_ptr(q), _ptr(k), _ptr(v), _ptr(key_valid), _ptr(o), _ptr(lse), B, nq, nk,
+                                      Hq, Hkv, D, scale, int(causal_offset), int(bool(causal)),
+                                      int(bool(accumulate)), _dtype_code(q), _stream(q.device)),
+           "ulysses_attn_fwd_block")
+    return o, lse
 
 
 def ulysses_repack_seq2head_rope(src: torch.Tensor, rope_base: float, rope_scale: float = 1.0,
@@ -300,4 +326,5 @@ __all__ = [
     "load_library", "EXPORTED", "LIB_PATH", "ulysses_abi_version", "ulysses_repack_seq2head",
     "ulysses_repack_head2seq", "ulysses_attn_fwd", "ulysses_attn_bwd", "ulysses_attn_bwd_workspace_bytes",
     "ulysses_attn_fwd_docs", "ulysses_attn_bwd_docs", "ulysses_repack_seq2head_rope", "ulysses_loss_aggregate",
+    "ulysses_attn_fwd_block",
 ]

@@ -206,6 +206,38 @@ ulysses_status_t ulysses_attn_bwd_docs(const void* q, const void* k, const void*
                   D, softmax_scale, 1, in_dtype, o_dtype, stream);
 }
 
+ulysses_status_t ulysses_attn_fwd_block(const void* q, const void* k, const void* v, const uint8_t* key_valid,
+                                        float* o, float* lse, int32_t B, int64_t nq, int64_t nk, int32_t Hq,
+                                        int32_t Hkv, int32_t D, float softmax_scale, int64_t causal_offset,
+                                        int32_t causal, int32_t accumulate, ulysses_dtype_t in_dtype,
+                                        void* stream) {
+  bool empty = false;
+  ulysses_status_t st =
+      check_attn_shape(B, nq, Hq, Hkv, D, softmax_scale, causal, in_dtype, ULYSSES_DTYPE_F32, &empty);
+  if (st != ULYSSES_OK) return st;
+  if (nk < 1 || (accumulate != 0 && accumulate != 1)) return ULYSSES_ERR_INVALID_ARG;
+  if (in_dtype != ULYSSES_DTYPE_BF16) return ULYSSES_ERR_UNSUPPORTED;
+  if (nk >= (int64_t(1) << 31) - 256 || nq + nk >= (int64_t(1) << 31) - 256) return ULYSSES_ERR_UNSUPPORTED;
+  if (int64_t(B) * nk * Hkv * D >= (int64_t(1) << 40)) return ULYSSES_ERR_UNSUPPORTED;
+  if (empty) return ULYSSES_OK;
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || lse == nullptr) return ULYSSES_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return ULYSSES_ERR_INVALID_ARG;
+  const uint64_t nqe = uint64_t(B) * nq * Hq * D, nke = uint64_t(B) * nk * Hkv * D;
+  const uint64_t bo = nqe * 4, bl = uint64_t(B) * Hq * nq * 4;
+  const void* ins[4] = {q, k, v, key_valid};
+  const uint64_t inb[4] = {nqe * 2, nke * 2, nke * 2, key_valid ? uint64_t(B) * nk : 0};
+  for (int i = 0; i < 4; ++i)
+    if (overlap(o, bo, ins[i], inb[i]) || overlap(lse, bl, ins[i], inb[i])) return ULYSSES_ERR_INVALID_ARG;
+  if (overlap(o, bo, lse, bl)) return ULYSSES_ERR_INVALID_ARG;
+  // offsets past the block's extent change nothing: clamp to [-nq, nk]
+  const int64_t delta = causal_offset < -nq ? -nq : (causal_offset > nk ? nk : causal_offset);
+  ulysses::KeyBlock kb{nk, causal ? delta : nk, accumulate};
+  AttnShape s{B, nq, Hq, Hkv, D, softmax_scale, causal};
+  return from_hip(ulysses::launch_attn_fwd_bf16(q, k, v, key_valid, nullptr, o, lse, s, 1,
+                                                static_cast<hipStream_t>(stream), &kb));
+}
+
 ulysses_status_t ulysses_repack_seq2head_rope(const void* src, void* dst, int32_t P, int32_t B, int64_t n_local,
                                               int32_t H, int32_t D, double rope_base, double rope_scale,
                                               ulysses_dtype_t dtype, void* stream) {

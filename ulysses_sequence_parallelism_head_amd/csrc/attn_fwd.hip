@@ -43,6 +43,11 @@
 //    holds its first row's bound, so whole tiles of earlier documents are
 //    never loaded, and only tiles below its last row's bound take the
 //    per-row lower mask.
+//  * Key blocks (ring attention's hops): the keys may be a separate block of
+//    nk positions whose causal relation to the rows is an offset delta (key
+//    u of the block is visible to row t iff u <= t + delta); the epilogue can
+//    merge this block's (O, LSE) into a running float32 result already in
+//    the output, by the exact logsumexp combination for disjoint key sets.
 #include <type_traits>
 
 #include "device_common.h"
@@ -80,6 +85,9 @@ struct FwdParams {
   void* o;
   float* lse;
   int32_t B, n, Hq, Hkv;
+  int32_t nk;         // keys (n, or the length of a separate key block)
+  int32_t delta;      // causal offset: key u visible to row t iff u <= t + delta (0 for one sequence)
+  int32_t accumulate; // merge into the float32 (O, LSE) already in the output
   int32_t g;          // query heads per KV head
   int32_t gh;         // query heads per workgroup
   int32_t pw;         // positions per workgroup
@@ -98,14 +106,14 @@ __device__ __forceinline__ void fwd_issue(uint8_t* stage, uint32_t& vbyte, const
                                           int tile, int wave, int lane, int tid) {
   using L = FwdLayout<D>;
   const int key0 = tile * kBN;
-  const int rows_ok = min(kBN, p.n - key0);
-  const int64_t off = ((int64_t(b) * p.n + key0) * p.Hkv + kvh) * D;
+  const int rows_ok = min(kBN, p.nk - key0);
+  const int64_t off = ((int64_t(b) * p.nk + key0) * p.Hkv + kvh) * D;
   const int stride = p.Hkv * D * 2;
   dma_tile<D, kBN, kWaves>(stage, p.k + off, stride, rows_ok, wave, lane);
   dma_tile<D, kBN, kWaves>(stage + L::kBytesK, p.v + off, stride, rows_ok, wave, lane);
   if (HAS_MASK && tid < kBN) {
     const int key = key0 + tid;
-    vbyte = (key < p.n) ? (p.valid[int64_t(b) * p.n + key] != 0 ? 1u : 0u) : 0u;
+    vbyte = (key < p.nk) ? (p.valid[int64_t(b) * p.nk + key] != 0 ? 1u : 0u) : 0u;
   }
 }
 
@@ -140,7 +148,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const FwdPar
   const int t = p0 + l32;                               // this lane's query row
   const int wave_last = min(p0 + 31, p.n - 1);
   const int wg_last = min(pb * p.pw + p.pw, p.n) - 1;
-  const int kend = CAUSAL ? wg_last + 1 : p.n;
+  const int kend = CAUSAL ? min(wg_last + 1 + p.delta, p.nk) : p.nk;
   const int ntiles = (kend + kBN - 1) / kBN;
   const bool wave_live = p0 < p.n;
 
@@ -193,7 +201,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const FwdPar
       if (it + 1 < ntiles) fwd_issue<D, HAS_MASK>(nxt, vbyte, p, b, kvh, it + 1, wave, lane, tid);
 
       const int tile0 = it * kBN;
-      if (wave_live && !(CAUSAL && tile0 > wave_last) && !(DOCS && tile0 + kBN <= lo_wave)) {
+      if (wave_live && !(CAUSAL && tile0 > wave_last + p.delta) && !(DOCS && tile0 + kBN <= lo_wave)) {
         const uint8_t* ks = cur;
         const uint8_t* vs = cur + L::kBytesK;
 
@@ -217,15 +225,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const FwdPar
           x[i] = s0[i];
           x[16 + i] = s1[i];
         }
-        const bool diag = CAUSAL && (tile0 + kBN - 1 > p0);
-        const bool tail = !CAUSAL && (tile0 + kBN > p.n);
+        const bool diag = CAUSAL && (tile0 + kBN - 1 > p0 + p.delta);
+        const bool tail = tile0 + kBN > p.nk;
         const bool lower = DOCS && tile0 < lo_last;
         if (diag || tail || lower) {
           // element i holds key tile0 + 4hh + C_i with C_i a compile-time constant;
-          // it is visible iff lo <= C_i <= lim.  Causal: key <= t (this also hides
-          // keys >= n, since t < n); otherwise only the tail limit key < n
-          // applies.  Documents: key >= the row's bound.
-          const int lim = (CAUSAL ? t : p.n - 1) - tile0 - 4 * hh;
+          // it is visible iff lo <= C_i <= lim.  Causal: key <= t + delta; always
+          // key < nk.  Documents: key >= the row's bound.
+          const int lim = (CAUSAL ? min(t + p.delta, p.nk - 1) : p.nk - 1) - tile0 - 4 * hh;
           const int lo = DOCS ? lo_row - tile0 - 4 * hh : -0x7fffffff;
 #pragma unroll
           for (int i = 0; i < 32; ++i) {
@@ -319,30 +326,54 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const FwdPar
     // ---- epilogue: normalise, write O (row t, dims 32j + 8*(i/4) + 4hh + i%4) and LSE
     if (t < p.n) {
       const float ltot = halves_sum(lsum);
-      const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
       const int64_t obase = ((int64_t(b) * p.n + t) * p.Hq + head) * D;
+      const int64_t lidx = (int64_t(b) * p.Hq + head) * p.n + t;
+      float lse_out = ltot > 0.f ? (m_ref + __log2f(ltot)) * kLn2 : -INFINITY;
+      float w_new = ltot > 0.f ? 1.0f / ltot : 0.f;   // scales the accumulator to this block's O
+      float w_old = 0.f;                              // weight of the O already in the output
+      if (O_F32 && p.accumulate) {
+        // L = ln(e^L_old + e^L_new), O = e^(L_old - L) O_old + e^(L_new - L) O_new
+        const float l_old = p.lse[lidx];
+        const float m = fmaxf(l_old, lse_out);
+        if (m == -INFINITY) {
+          w_new = 0.f;
+        } else {
+          const float a = expf(l_old - m), c = expf(lse_out - m);
+          const float sum = a + c;
+          w_old = a / sum;
+          w_new *= c / sum;
+          lse_out = m + logf(sum);
+        }
+      }
 #pragma unroll
       for (int j = 0; j < DJ; ++j) {
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
           const int d0 = j * 32 + i4 * 8 + hh * 4;
-          const float v0 = oacc[j][i4 * 4 + 0] * inv, v1 = oacc[j][i4 * 4 + 1] * inv;
-          const float v2 = oacc[j][i4 * 4 + 2] * inv, v3 = oacc[j][i4 * 4 + 3] * inv;
+          float v0 = oacc[j][i4 * 4 + 0] * w_new, v1 = oacc[j][i4 * 4 + 1] * w_new;
+          float v2 = oacc[j][i4 * 4 + 2] * w_new, v3 = oacc[j][i4 * 4 + 3] * w_new;
           if (O_F32) {
-            *reinterpret_cast<f32x4*>(static_cast<float*>(p.o) + obase + d0) = f32x4{v0, v1, v2, v3};
+            f32x4* op = reinterpret_cast<f32x4*>(static_cast<float*>(p.o) + obase + d0);
+            if (p.accumulate) {
+              const f32x4 prev = *op;
+              v0 = fmaf(w_old, prev[0], v0);
+              v1 = fmaf(w_old, prev[1], v1);
+              v2 = fmaf(w_old, prev[2], v2);
+              v3 = fmaf(w_old, prev[3], v3);
+            }
+            *op = f32x4{v0, v1, v2, v3};
           } else {
             *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.o) + obase + d0) =
                 u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
           }
         }
       }
-      if (hh == 0) {
-        p.lse[(int64_t(b) * p.Hq + head) * p.n + t] =
-            ltot > 0.f ? (m_ref + __log2f(ltot)) * kLn2 : -INFINITY;
-      }
+      // both half-waves have read the old LSE above; only one writes it
+      if (hh == 0) p.lse[lidx] = lse_out;
     }
   };
-  if (pb * p.pw - lo_last < kSplitRows) run(std::true_type{});
+  // fewest keys of any row: min(first row + delta, nk - 1) + 1 - (last row's bound)
+  if (min(pb * p.pw + p.delta, p.nk - 1) - lo_last < kSplitRows) run(std::true_type{});
   else run(std::false_type{});
 }
 
@@ -370,7 +401,7 @@ hipError_t dispatch_fwd(const FwdParams& p, int blocks, bool has_mask, bool o_f3
 
 hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, const uint8_t* valid,
                                 const int32_t* doc_start, void* o, float* lse, const AttnShape& s, int o_f32,
-                                hipStream_t stream) {
+                                hipStream_t stream, const KeyBlock* kb) {
   FwdParams p;
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
@@ -381,6 +412,9 @@ hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, con
   p.lse = lse;
   p.B = s.B;
   p.n = int32_t(s.n);
+  p.nk = kb ? int32_t(kb->nk) : int32_t(s.n);
+  p.delta = kb ? int32_t(kb->delta) : 0;
+  p.accumulate = kb ? kb->accumulate : 0;
   p.Hq = s.Hq;
   p.Hkv = s.Hkv;
   p.g = s.Hq / s.Hkv;

@@ -24,10 +24,20 @@ struct AttnShape {
 // (the first position of the row's document) on top of the causal mask;
 // callers pass it only with s.causal == 1.
 
-// bf16 inputs, matrix cores; o_f32 selects a float32 (else bf16) output.
+// A separate key block for the forward: nk keys, key u visible to row t iff
+// u <= t + delta (causal); accumulate merges into the float32 (O, LSE)
+// already in the outputs.  Callers keep nk >= 1, -n <= delta <= nk.
+struct KeyBlock {
+  int64_t nk;
+  int64_t delta;
+  int32_t accumulate;
+};
+
+// bf16 inputs, matrix cores; o_f32 selects a float32 (else bf16) output;
+// kb = nullptr: the keys are the rows' own sequence (nk = n, delta = 0).
 hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, const uint8_t* valid,
                                 const int32_t* doc_start, void* o, float* lse, const AttnShape& s, int o_f32,
-                                hipStream_t stream);
+                                hipStream_t stream, const KeyBlock* kb = nullptr);
 
 // float32 inputs and output, fp32 arithmetic throughout.
 hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, const uint8_t* valid,
