@@ -16,6 +16,8 @@ Contents
 ``rope``       rotary position embedding at global positions before the first
                exchange.
 ``loss``       the loss aggregated over shards, weighted by valid tokens.
+``proj``       the QKV projection before the first exchange and the output
+               projection after the second.
 ``ring``       the ring-attention alternative: block attention and the exact
                logsumexp merge over the P hops.
 
@@ -26,7 +28,7 @@ Sources (web pages; cited by title and section):
           (agents-report.net)
   [SWIFT] "ms-swift性能优化：Ulysses并行技术降低长文本显存" (hotelren.com)
 """
-from . import exchange, attention, rope, loss, ring  # noqa: F401
+from . import exchange, attention, rope, loss, ring, proj  # noqa: F401
 from .exchange import shard, unshard, seq2head, head2seq, check_constraints  # noqa: F401
 from .attention import (  # noqa: F401
     attn_fwd, attn_bwd, attn_bwd_sampled, pipeline_fwd, pipeline_bwd, kv_head_of,
