@@ -31,6 +31,10 @@ of the P emulated ranks keeps all heads of its query shard and merges the
 key/value shards of its hops with ``ulysses_attn_fwd_block``; the same
 attention is timed the Ulysses way (P head-shard forwards over the whole
 sequence) beside it.
+``--proj`` times the projections fused with the exchanges (QKV projection
+writing the head-sharded layout, output projection reading it) at the
+workload's model width (hidden = Hq * D), beside the same work done unfused
+with torch's library GEMM followed by the plain exchange.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C] [--docs] [--no-cpu-baseline]
 Prints ONE JSON line on stdout.
@@ -218,6 +222,107 @@ def bench_ring(args, w):
     print(json.dumps(result), flush=True)
 
 
+def bench_proj(args, w):
+    """QKV projection + first exchange and second exchange + output
+    projection, fused, against library GEMM + plain exchange; one JSON line."""
+    import torch
+    import synth
+    import ulysses_sequence_parallelism_head_amd as U
+    dev = torch.device("cuda:0")
+    P, nl, n, D = w.P, w.n_local, w.n, w.D
+    Hq, Hkv = w.Hq_global, w.Hkv_global
+    hidden = Hq * D
+    g = synth.streams(w.number)
+
+    def dev_bits(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def weights(gen, rows, cols):
+        return dev_bits(synth.f32_to_bf16_bits(gen.standard_normal((rows, cols), dtype=np.float32)
+                                               / np.float32(np.sqrt(cols))))
+
+    log(f"[bench] projections, workload {w.name}, hidden {hidden}")
+    x = dev_bits(synth.normal_bf16(g[synth.STREAM_Q], (P, 1, nl, hidden)))
+    w_qkv = weights(g[synth.STREAM_K], (Hq + 2 * Hkv) * D, hidden)
+    w_o = weights(g[synth.STREAM_V], hidden, Hq * D)
+    q_h = torch.empty((P, 1, n, Hq // P, D), dtype=torch.bfloat16, device=dev)
+    k_h = torch.empty((P, 1, n, Hkv // P, D), dtype=torch.bfloat16, device=dev)
+    v_h = torch.empty_like(k_h)
+    y = torch.empty((P, 1, nl, hidden), dtype=torch.bfloat16, device=dev)
+    # unfused reference path: library GEMM, then the plain exchange
+    o_seq = torch.empty((P, 1, nl, Hq, D), dtype=torch.bfloat16, device=dev)
+
+    def fused_qkv():
+        U.ulysses_qkv_proj_seq2head(x, w_qkv, Hq, Hkv, D, q_h, k_h, v_h)
+
+    def fused_out():
+        U.ulysses_head2seq_out_proj(q_h, w_o, y)
+
+    yq = torch.empty((P, 1, nl, Hq, D), dtype=torch.bfloat16, device=dev)
+    yk = torch.empty((P, 1, nl, Hkv, D), dtype=torch.bfloat16, device=dev)
+    yv = torch.empty_like(yk)
+
+    def unfused_qkv():
+        # library GEMMs into separate Q, K, V buffers, then the plain exchange of each
+        xf = x.view(-1, hidden)
+        torch.matmul(xf, w_qkv[:Hq * D].t(), out=yq.view(-1, Hq * D))
+        torch.matmul(xf, w_qkv[Hq * D:(Hq + Hkv) * D].t(), out=yk.view(-1, Hkv * D))
+        torch.matmul(xf, w_qkv[(Hq + Hkv) * D:].t(), out=yv.view(-1, Hkv * D))
+        U.ulysses_repack_seq2head(yq, q_h)
+        U.ulysses_repack_seq2head(yk, k_h)
+        U.ulysses_repack_seq2head(yv, v_h)
+
+    def unfused_out():
+        U.ulysses_repack_head2seq(q_h, o_seq)
+        torch.matmul(o_seq.view(-1, Hq * D), w_o.t(), out=y.view(-1, hidden))
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms_qkv, ms_out = timed(fused_qkv), timed(fused_out)
+    ms_uq, ms_uo = timed(unfused_qkv), timed(unfused_out)
+    tokens = P * nl
+    f_qkv = 2.0 * tokens * hidden * (Hq + 2 * Hkv) * D
+    f_out = 2.0 * tokens * Hq * D * hidden
+    tf_qkv = f_qkv / (ms_qkv * 1e-3) / 1e12
+    tf_out = f_out / (ms_out * 1e-3) / 1e12
+    result = {
+        "metric": f"projections fused with the exchanges TFLOP/s @{n // 1024}K, hidden {hidden}, {Hq}q/{Hkv}kv heads "
+                  f"d{D} bf16, P={P}",
+        "value": round((f_qkv + f_out) / ((ms_qkv + ms_out) * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_qkv + ms_out, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name + "+projections", "n": n, "P": P, "hidden": hidden, "q_heads": Hq,
+                   "kv_heads": Hkv, "head_dim": D},
+        "qkv_proj_seq2head_ms": round(ms_qkv, 4),
+        "qkv_proj_seq2head_tflops": round(tf_qkv, 2),
+        "head2seq_out_proj_ms": round(ms_out, 4),
+        "head2seq_out_proj_tflops": round(tf_out, 2),
+        "unfused_library_gemm_then_exchange_ms": {"qkv": round(ms_uq, 4), "out": round(ms_uo, 4)},
+        "roofline": {"bound": "mfma", "kernel": "proj_kernel (QKV)", "achieved": round(tf_qkv, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf_qkv / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None},
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -227,6 +332,7 @@ def main():
     ap.add_argument("--rope-loss", action="store_true",
                     help="fuse the rotary embedding into Q/K's first exchange and aggregate the loss")
     ap.add_argument("--ring", action="store_true", help="time the ring-attention emulation (forward)")
+    ap.add_argument("--proj", action="store_true", help="time the projections fused with the exchanges")
     ap.add_argument("--docs", action="store_true",
                     help="document-masked attention (workloads with packed documents only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -271,6 +377,9 @@ def main():
 
     if args.ring:
         bench_ring(args, w)
+        return
+    if args.proj:
+        bench_proj(args, w)
         return
     log(f"[bench] generating workload {w.name}")
     g = synth.streams(w.number)

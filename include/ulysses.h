@@ -16,6 +16,8 @@
  * For the ring-attention alternative the pages compare against, the
  * forward over one separate key block with an exact merge of partial
  * results (ulysses_attn_fwd_block).
+ * Around the path, the projections fused with their exchanges
+ * (ulysses_qkv_proj_seq2head, ulysses_head2seq_out_proj).
  * Beside the path: the first exchange fused with the rotary position
  * embedding at global positions (ulysses_repack_seq2head_rope), and the
  * loss aggregated over shards by valid tokens (ulysses_loss_aggregate).
@@ -351,6 +353,60 @@ ULYSSES_API ulysses_status_t ulysses_repack_seq2head_rope(const void* src, void*
                                               int32_t H, int32_t D,
                                               double rope_base, double rope_scale,
                                               ulysses_dtype_t dtype, void* stream);
+
+/*
+ * ulysses_qkv_proj_seq2head -- the QKV projection of every sequence shard
+ * fused with the first exchange: the projected heads are written straight
+ * into the head-sharded layout.
+ *
+ * Source: [ALST] "Mecanismul de funcționare Ulysses", steps 2-3 (each rank
+ * projects query, key and value for its own shard, then the first
+ * all-to-all); [HFSUM] "Ulysses 序列平行化的原理".  The weight layout is a
+ * reading: W is [out features][in features] and stacks the Hq query heads,
+ * the Hkv key heads and the Hkv value heads, D features each.
+ *
+ *   x   [P][B][n_local][hidden]   bf16, the sequence shards
+ *   w   [(Hq + 2 Hkv) * D][hidden] bf16
+ *   q   [P][B][P*n_local][Hq/P][D]  bf16 (output)   q[j][b][i*n_local + s][h][c] =
+ *       sum_e x[i][b][s][e] * w[(j*Hq/P + h)*D + c][e]
+ *   k, v [P][B][P*n_local][Hkv/P][D] bf16 (outputs), rows (Hq + head)*D + c and
+ *       (Hq + Hkv + head)*D + c of w likewise
+ *
+ * Arithmetic: bf16 products on the matrix cores, float32 accumulation, one
+ * rounding to bf16.  Errors: INVALID_ARG for P < 1, B < 0, n_local < 0,
+ * sizes < 1, Hq or Hkv not divisible by P, null or not 16-byte aligned
+ * pointers (non-empty problem), any output overlapping an input or another
+ * output; UNSUPPORTED for D other than 64 and 128, hidden not a multiple
+ * of 64, or sizes past the kernel's index range.
+ */
+ULYSSES_API ulysses_status_t ulysses_qkv_proj_seq2head(const void* x, const void* w,
+                                           void* q, void* k, void* v,
+                                           int32_t P, int32_t B, int64_t n_local, int32_t hidden,
+                                           int32_t Hq, int32_t Hkv, int32_t D, void* stream);
+
+/*
+ * ulysses_head2seq_out_proj -- the second exchange fused with each shard's
+ * output projection: the attention output is read straight from the
+ * head-sharded layout.
+ *
+ * Source: [ALST] "Mecanismul de funcționare Ulysses", steps 5-6 (the second
+ * all-to-all restores the sequence sharding, then each rank's output
+ * projection of its shard).  Reading: a token's attention output is its Hq
+ * heads concatenated in head order; W_o is [hidden][Hq * D].
+ *
+ *   o    [P][B][P*n_local][Hq/P][D]  bf16, the attention output, head-sharded
+ *   w_o  [hidden][Hq * D]            bf16
+ *   y    [P][B][n_local][hidden]     bf16 (output)
+ *        y[i][b][s][f] = sum_{h,c} o[h / (Hq/P)][b][i*n_local + s][h % (Hq/P)][c] * w_o[f][h*D + c]
+ *
+ * Arithmetic as ulysses_qkv_proj_seq2head.  Errors: INVALID_ARG as there
+ * (with Hq % P), y overlapping o or w_o; UNSUPPORTED for D other than 64 and
+ * 128, (Hq/P)*D not a multiple of 64, hidden not a multiple of 4, or sizes
+ * past the kernel's index range.
+ */
+ULYSSES_API ulysses_status_t ulysses_head2seq_out_proj(const void* o, const void* w_o, void* y,
+                                           int32_t P, int32_t B, int64_t n_local,
+                                           int32_t Hq, int32_t D, int32_t hidden, void* stream);
 
 /*
  * ulysses_loss_aggregate -- the loss of a sequence split over P ranks,

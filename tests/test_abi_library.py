@@ -190,3 +190,20 @@ def test_block_validation(lib):
     assert call(nk=(1 << 31) - 100) == UNSUPPORTED
     assert call(o=ctypes.c_void_p(0x1000000 + 256)) == INVALID     # o overlaps k
     assert call(nq=0) == OK                                        # empty
+
+
+def test_proj_validation(lib):
+    f = lib.ulysses_qkv_proj_seq2head
+    Q, K, V = ctypes.c_void_p(0x3000000), ctypes.c_void_p(0x4000000), ctypes.c_void_p(0x5000000)
+    W = ctypes.c_void_p(0x1000000)
+    assert f(FAKE, W, Q, K, V, 4, 1, 16, 4096, 30, 8, 128, None) == INVALID       # Hq % P
+    assert f(FAKE, W, Q, K, V, 4, 1, 16, 4096, 32, 8, 96, None) == UNSUPPORTED    # D
+    assert f(FAKE, W, Q, K, V, 4, 1, 16, 4000, 32, 8, 128, None) == UNSUPPORTED   # hidden % 64
+    assert f(FAKE, W, ctypes.c_void_p(0x1000000 + 64), K, V, 4, 1, 16, 4096, 32, 8, 128, None) == INVALID   # q overlaps w
+    assert f(FAKE, W, Q, K, ctypes.c_void_p(0x3000010), 4, 1, 16, 4096, 32, 8, 128, None) == INVALID  # v overlaps q
+    assert f(None, None, None, None, None, 4, 0, 16, 4096, 32, 8, 128, None) == OK                    # empty
+    g = lib.ulysses_head2seq_out_proj
+    Y = ctypes.c_void_p(0x6000000)
+    assert g(FAKE, W, Y, 4, 1, 16, 30, 128, 4096, None) == INVALID                # Hq % P
+    assert g(FAKE, W, Y, 4, 1, 16, 32, 128, 4098, None) == UNSUPPORTED           # hidden % 4
+    assert g(FAKE, W, ctypes.c_void_p(0x10000 + 16), 4, 1, 16, 32, 128, 4096, None) == INVALID   # y overlaps o

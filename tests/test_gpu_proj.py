@@ -1,0 +1,116 @@
+"""GPU parity of the projections fused with the exchanges
+(ulysses_qkv_proj_seq2head, ulysses_head2seq_out_proj) against the fp64
+oracle on the same bf16 inputs.
+
+Tolerance (derived from the arithmetic): bf16 products are exact in the
+float32 accumulator, K float32 additions add at most K * 2^-24 * sum|x w|,
+and the result is rounded once to bf16 (2^-8 relative), so
+  |got - ref| <= 2^-8 |ref| + K 2^-24 (|x| @ |w|^T)
+elementwise.  Shapes cover ragged token and feature tiles, every split of
+heads over shards, both head dims, and the 64K workload's shapes (hidden
+4096, 32q/8kv heads, d128) on sampled tokens.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import ulysses_sequence_parallelism_head_amd as U
+from tests.gpu_helpers import say, bits_to_device, to_f64, to_host_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _weights(gen, rows, cols):
+    return synth.f32_to_bf16_bits(gen.standard_normal((rows, cols), dtype=np.float32) / np.float32(np.sqrt(cols)))
+
+
+def _check(name, got, ref, bound_terms, K):
+    bound = 2.0 ** -8 * np.abs(ref) + K * 2.0 ** -24 * bound_terms
+    err = np.abs(got - ref)
+    worst = float(np.max(err / bound)) if err.size else 0.0
+    say(f"  {name}: max_abs_err={float(err.max()):.3e} worst err/bound={worst:.3f}")
+    assert not np.any(np.isnan(got)) and np.all(err <= bound), f"{name}: err/bound {worst}"
+
+
+QKV_CASES = [
+    # P, B, nl, hidden, Hq, Hkv, D
+    (1, 1, 1, 64, 1, 1, 64),
+    (2, 1, 37, 128, 4, 2, 64),
+    (4, 2, 130, 256, 8, 4, 128),
+    (4, 1, 260, 512, 32, 8, 128),
+    (2, 1, 129, 192, 6, 2, 128),
+]
+
+
+@pytest.mark.parametrize("P,B,nl,hidden,Hq,Hkv,D", QKV_CASES)
+def test_qkv_proj(P, B, nl, hidden, Hq, Hkv, D):
+    say(f"qkv proj P={P} B={B} nl={nl} hidden={hidden} Hq={Hq} Hkv={Hkv} D={D}")
+    g = synth.streams(400 + nl)
+    x = synth.normal_bf16(g[0], (P, B, nl, hidden))
+    w = _weights(g[1], (Hq + 2 * Hkv) * D, hidden)
+    q, k, v = U.ulysses_qkv_proj_seq2head(bits_to_device(x), bits_to_device(w), Hq, Hkv, D)
+    torch.cuda.synchronize()
+    xf, wf = to_f64(x), to_f64(w)
+    rq, rk, rv = oracle.proj.qkv_proj_seq2head(xf, wf, Hq, Hkv, D)
+    aq, ak, av = oracle.proj.qkv_proj_seq2head(np.abs(xf), np.abs(wf), Hq, Hkv, D)
+    for name, got, ref, ab in (("Q", q, rq, aq), ("K", k, rk, ak), ("V", v, rv, av)):
+        _check(name, to_host_f64(got), ref, ab, hidden)
+
+
+OUT_CASES = [
+    # P, B, nl, Hq, D, hidden
+    (1, 1, 1, 1, 64, 64),
+    (2, 1, 37, 4, 64, 100),
+    (4, 2, 130, 8, 128, 256),
+    (4, 1, 260, 32, 128, 512),
+]
+
+
+@pytest.mark.parametrize("P,B,nl,Hq,D,hidden", OUT_CASES)
+def test_out_proj(P, B, nl, Hq, D, hidden):
+    say(f"out proj P={P} B={B} nl={nl} Hq={Hq} D={D} hidden={hidden}")
+    g = synth.streams(500 + nl)
+    o = synth.normal_bf16(g[0], (P, B, P * nl, Hq // P, D))
+    w = _weights(g[1], hidden, Hq * D)
+    y = U.ulysses_head2seq_out_proj(bits_to_device(o), bits_to_device(w))
+    torch.cuda.synchronize()
+    of, wf = to_f64(o), to_f64(w)
+    _check("Y", to_host_f64(y), oracle.proj.head2seq_out_proj(of, wf),
+           oracle.proj.head2seq_out_proj(np.abs(of), np.abs(wf)), Hq * D)
+
+
+def test_proj_64k_sampled():
+    """The 64K workload's shapes: x [4][1][16384][4096], W_qkv [6144][4096],
+    W_o [4096][4096]; Q/K/V and the output projection of the projected Q
+    (as a stand-in attention output) on sampled tokens."""
+    say("projections at the 64K workload, sampled tokens")
+    w3 = synth.WORKLOADS[3]
+    P, nl, D, Hq, Hkv = w3.P, w3.n_local, w3.D, w3.Hq_global, w3.Hkv_global
+    hidden = Hq * D
+    g = synth.streams(w3.number)
+    x = synth.normal_bf16(g[synth.STREAM_Q], (P, 1, nl, hidden))
+    w = _weights(g[synth.STREAM_K], (Hq + 2 * Hkv) * D, hidden)
+    w_o = _weights(g[synth.STREAM_V], hidden, Hq * D)
+    q, k, v = U.ulysses_qkv_proj_seq2head(bits_to_device(x), bits_to_device(w), Hq, Hkv, D)
+    y = U.ulysses_head2seq_out_proj(q, bits_to_device(w_o))
+    torch.cuda.synchronize()
+    tok = synth.sample_rows(g[synth.STREAM_ROWS], P * nl, 24, extra=(0, nl - 1, nl, P * nl - 1))
+    i, s = tok // nl, tok % nl
+    xf, wf = to_f64(x[i, 0, s]), to_f64(w)                  # [R][hidden]
+    ref = xf @ wf.T
+    ab = np.abs(xf) @ np.abs(wf).T
+    qg = to_host_f64(q)                                     # [P][1][n][Hq/P][D]
+    hp = Hq // P
+    got_q = qg[:, 0, tok].transpose(1, 0, 2, 3).reshape(len(tok), Hq * D)
+    _check("Q rows", got_q, ref[:, :Hq * D], ab[:, :Hq * D], hidden)
+    kg = to_host_f64(k)
+    got_k = kg[:, 0, tok].transpose(1, 0, 2, 3).reshape(len(tok), Hkv * D)
+    _check("K rows", got_k, ref[:, Hq * D:(Hq + Hkv) * D], ab[:, Hq * D:(Hq + Hkv) * D], hidden)
+    # output projection of the (bf16) projected Q at the same tokens
+    qrow = got_q                                            # the GPU's bf16 Q, exactly
+    yref = qrow @ to_f64(w_o).T
+    yab = np.abs(qrow) @ np.abs(to_f64(w_o)).T
+    _check("Y rows", to_host_f64(y)[i, 0, s], yref, yab, Hq * D)
+    assert hp * P == Hq

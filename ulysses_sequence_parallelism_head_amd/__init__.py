@@ -67,6 +67,12 @@ _SIGS = {
                                               ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                               ctypes.c_float, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                               ctypes.c_int, ctypes.c_void_p]),
+    "ulysses_qkv_proj_seq2head": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int32, ctypes.c_int32,
+                                                                          ctypes.c_int64] + [ctypes.c_int32] * 4
+                                  + [ctypes.c_void_p]),
+    "ulysses_head2seq_out_proj": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int32, ctypes.c_int32,
+                                                                          ctypes.c_int64] + [ctypes.c_int32] * 3
+                                  + [ctypes.c_void_p]),
     "ulysses_repack_seq2head_rope": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                                     ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_double,
                                                     ctypes.c_double, ctypes.c_int, ctypes.c_void_p]),
@@ -182,6 +188,42 @@ def ulysses_attn_fwd_block(q, k, v, o, lse, causal_offset: int, key_valid=None, 
                                       int(bool(accumulate)), _dtype_code(q), _stream(q.device)),
            "ulysses_attn_fwd_block")
     return o, lse
+
+
+def ulysses_qkv_proj_seq2head(x: torch.Tensor, w: torch.Tensor, Hq: int, Hkv: int, D: int, q=None, k=None, v=None):
+    """x bf16 ``[P][B][n_local][hidden]``, w bf16 ``[(Hq + 2 Hkv) D][hidden]`` ->
+    head-sharded ``(q [P][B][P n_local][Hq/P][D], k, v [P][B][P n_local][Hkv/P][D])``."""
+    lib = load_library()
+    _need_contig_cuda(x, w, q, k, v)
+    P, B, nl, hidden = x.shape
+    if tuple(w.shape) != ((Hq + 2 * Hkv) * D, hidden) or x.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
+        raise ValueError("x and w must be bf16 with w [(Hq + 2 Hkv) D][hidden]")
+    if Hq % P or Hkv % P:
+        _check(ERR_INVALID_ARG, "ulysses_qkv_proj_seq2head")
+    dev = x.device
+    q = torch.empty((P, B, P * nl, Hq // P, D), dtype=torch.bfloat16, device=dev) if q is None else q
+    k = torch.empty((P, B, P * nl, Hkv // P, D), dtype=torch.bfloat16, device=dev) if k is None else k
+    v = torch.empty((P, B, P * nl, Hkv // P, D), dtype=torch.bfloat16, device=dev) if v is None else v
+    _check(lib.ulysses_qkv_proj_seq2head(_ptr(x), _ptr(w), _ptr(q), _ptr(k), _ptr(v), P, B, nl, hidden, Hq, Hkv, D,
+                                         _stream(dev)),
+           "ulysses_qkv_proj_seq2head")
+    return q, k, v
+
+
+def ulysses_head2seq_out_proj(o: torch.Tensor, w_o: torch.Tensor, y=None):
+    """o bf16 ``[P][B][P n_local][Hq/P][D]`` (head-sharded attention output),
+    w_o bf16 ``[hidden][Hq D]`` -> y bf16 ``[P][B][n_local][hidden]``."""
+    lib = load_library()
+    _need_contig_cuda(o, w_o, y)
+    P, B, n, hp, D = o.shape
+    Hq = hp * P
+    hidden = w_o.shape[0]
+    if tuple(w_o.shape) != (hidden, Hq * D) or o.dtype != torch.bfloat16 or w_o.dtype != torch.bfloat16 or n % P:
+        raise ValueError("o and w_o must be bf16 with w_o [hidden][Hq D] and n divisible by P")
+    y = torch.empty((P, B, n // P, hidden), dtype=torch.bfloat16, device=o.device) if y is None else y
+    _check(lib.ulysses_head2seq_out_proj(_ptr(o), _ptr(w_o), _ptr(y), P, B, n // P, Hq, D, hidden, _stream(o.device)),
+           "ulysses_head2seq_out_proj")
+    return y
 
 
 def ulysses_repack_seq2head_rope(src: torch.Tensor, rope_base: float, rope_scale: float = 1.0,
@@ -326,5 +368,5 @@ __all__ = [
     "load_library", "EXPORTED", "LIB_PATH", "ulysses_abi_version", "ulysses_repack_seq2head",
     "ulysses_repack_head2seq", "ulysses_attn_fwd", "ulysses_attn_bwd", "ulysses_attn_bwd_workspace_bytes",
     "ulysses_attn_fwd_docs", "ulysses_attn_bwd_docs", "ulysses_repack_seq2head_rope", "ulysses_loss_aggregate",
-    "ulysses_attn_fwd_block",
+    "ulysses_attn_fwd_block", "ulysses_qkv_proj_seq2head", "ulysses_head2seq_out_proj",
 ]

@@ -257,6 +257,54 @@ ulysses_status_t ulysses_repack_seq2head_rope(const void* src, void* dst, int32_
                                                 rope_base, rope_scale, static_cast<hipStream_t>(stream)));
 }
 
+ulysses_status_t ulysses_qkv_proj_seq2head(const void* x, const void* w, void* q, void* k, void* v, int32_t P,
+                                           int32_t B, int64_t n_local, int32_t hidden, int32_t Hq, int32_t Hkv,
+                                           int32_t D, void* stream) {
+  if (P < 1 || B < 0 || n_local < 0 || hidden < 1 || Hq < 1 || Hkv < 1 || D < 1) return ULYSSES_ERR_INVALID_ARG;
+  if (Hq % P != 0 || Hkv % P != 0) return ULYSSES_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return ULYSSES_ERR_UNSUPPORTED;
+  if (hidden % 64 != 0) return ULYSSES_ERR_UNSUPPORTED;
+  if (n_local >= (int64_t(1) << 31) / P) return ULYSSES_ERR_UNSUPPORTED;
+  const uint64_t tokens = uint64_t(P) * uint64_t(B) * uint64_t(n_local);
+  const uint64_t N = uint64_t(Hq + 2 * Hkv) * D;
+  if (tokens * (uint64_t(hidden) + N) >= (uint64_t(1) << 40) || N >= (uint64_t(1) << 31)) return ULYSSES_ERR_UNSUPPORTED;
+  if (B == 0 || n_local == 0) return ULYSSES_OK;
+  if (x == nullptr || w == nullptr || q == nullptr || k == nullptr || v == nullptr) return ULYSSES_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))
+    return ULYSSES_ERR_INVALID_ARG;
+  const void* ins[2] = {x, w};
+  const uint64_t inb[2] = {tokens * hidden * 2, N * hidden * 2};
+  void* outs[3] = {q, k, v};
+  const uint64_t outb[3] = {tokens * Hq * D * 2, tokens * Hkv * D * 2, tokens * Hkv * D * 2};
+  for (int a = 0; a < 3; ++a) {
+    for (int i = 0; i < 2; ++i)
+      if (overlap(outs[a], outb[a], ins[i], inb[i])) return ULYSSES_ERR_INVALID_ARG;
+    for (int c = a + 1; c < 3; ++c)
+      if (overlap(outs[a], outb[a], outs[c], outb[c])) return ULYSSES_ERR_INVALID_ARG;
+  }
+  return from_hip(ulysses::launch_qkv_proj_seq2head(x, w, q, k, v, P, B, int32_t(n_local), hidden, Hq, Hkv, D,
+                                                    static_cast<hipStream_t>(stream)));
+}
+
+ulysses_status_t ulysses_head2seq_out_proj(const void* o, const void* w_o, void* y, int32_t P, int32_t B,
+                                           int64_t n_local, int32_t Hq, int32_t D, int32_t hidden, void* stream) {
+  if (P < 1 || B < 0 || n_local < 0 || hidden < 1 || Hq < 1 || D < 1) return ULYSSES_ERR_INVALID_ARG;
+  if (Hq % P != 0) return ULYSSES_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return ULYSSES_ERR_UNSUPPORTED;
+  if (((Hq / P) * D) % 64 != 0 || hidden % 4 != 0) return ULYSSES_ERR_UNSUPPORTED;
+  if (n_local >= (int64_t(1) << 31) / P) return ULYSSES_ERR_UNSUPPORTED;
+  const uint64_t tokens = uint64_t(P) * uint64_t(B) * uint64_t(n_local);
+  const uint64_t K = uint64_t(Hq) * D;
+  if (tokens * (K + uint64_t(hidden)) >= (uint64_t(1) << 40) || K >= (uint64_t(1) << 31)) return ULYSSES_ERR_UNSUPPORTED;
+  if (B == 0 || n_local == 0) return ULYSSES_OK;
+  if (o == nullptr || w_o == nullptr || y == nullptr) return ULYSSES_ERR_INVALID_ARG;
+  if (!aligned(o, 16) || !aligned(w_o, 16) || !aligned(y, 16)) return ULYSSES_ERR_INVALID_ARG;
+  const uint64_t yb = tokens * hidden * 2;
+  if (overlap(y, yb, o, tokens * K * 2) || overlap(y, yb, w_o, uint64_t(hidden) * K * 2)) return ULYSSES_ERR_INVALID_ARG;
+  return from_hip(ulysses::launch_head2seq_out_proj(o, w_o, y, P, B, int32_t(n_local), Hq, D, hidden,
+                                                    static_cast<hipStream_t>(stream)));
+}
+
 ulysses_status_t ulysses_loss_aggregate(const float* token_loss, const uint8_t* valid, int32_t P, int64_t per_rank,
                                         double* rank_sum, int64_t* rank_count, float* loss, void* stream) {
   if (P < 1 || P > 65535 || per_rank < 0) return ULYSSES_ERR_INVALID_ARG;

@@ -58,6 +58,14 @@ size_t attn_bwd_workspace_bytes(int32_t B, int64_t n, int32_t Hq);
 hipError_t launch_seq2head_rope(const void* src, void* dst, int32_t P, int32_t B, int32_t n_local, int32_t H,
                                 int32_t D, int elem_bytes, double base, double scale, hipStream_t stream);
 
+// the projections fused with their exchanges (bf16; hidden and Hq*D multiples
+// of 64, (Hq/P)*D a multiple of 64, D 64 or 128)
+hipError_t launch_qkv_proj_seq2head(const void* x, const void* w, void* q, void* k, void* v, int32_t P, int32_t B,
+                                    int32_t n_local, int32_t hidden, int32_t Hq, int32_t Hkv, int32_t D,
+                                    hipStream_t stream);
+hipError_t launch_head2seq_out_proj(const void* o, const void* w_o, void* y, int32_t P, int32_t B, int32_t n_local,
+                                    int32_t Hq, int32_t D, int32_t hidden, hipStream_t stream);
+
 // per-rank sums and counts of the valid tokens' losses, and their ratio
 hipError_t launch_loss_aggregate(const float* token_loss, const uint8_t* valid, int32_t P, int64_t per_rank,
                                  double* rank_sum, int64_t* rank_count, float* loss, hipStream_t stream);
