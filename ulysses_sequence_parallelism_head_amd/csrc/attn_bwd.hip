@@ -253,6 +253,29 @@ __device__ __forceinline__ int doc_rows_end(const int32_t* rs, int klast, int n,
   return lo;
 }
 
+// Run of key block kb (128 keys; last key klast): the blocks whose last key
+// lies between the bound of kb's last key and the end of the rows that see
+// it, [r0, r1) = [bound / 128, rend / 128) (r1 = nkb when rend = n).  For
+// documents these are the blocks whose last keys share a document.  The
+// partner r0 + r1 - 1 - kb is used only if it computes the same run, so the
+// pairing is an involution whatever the bounds hold; otherwise kb is done
+// alone.  Both indices always stay in [0, nkb).
+__device__ __forceinline__ int docs_run_end(const int32_t* rs, int kb, int n, int nkb, int lane, int* r0) {
+  const int klast = min(kb * 128 + 127, n - 1);
+  const int rend = doc_rows_end(rs, klast, n, lane);
+  *r0 = doc_lower(rs, klast) / 128;
+  return rend >= n ? nkb : rend / 128;
+}
+
+__device__ __forceinline__ int docs_partner(const int32_t* rs, int kb, int n, int nkb, int lane) {
+  int r0, q0;
+  const int r1 = docs_run_end(rs, kb, n, nkb, lane, &r0);
+  const int partner = r0 + r1 - 1 - kb;
+  if (partner == kb) return kb;
+  const int q1 = docs_run_end(rs, partner, n, nkb, lane, &q0);
+  return (q0 == r0 && q1 == r1) ? partner : kb;
+}
+
 // Work items and tile order.  A work item is one key block (non-causal) or,
 // for causal attention, the pair of key blocks (nkb-1-w, w): the first one
 // sweeps the query tiles from the last down to its diagonal, the second from
@@ -261,8 +284,13 @@ __device__ __forceinline__ int doc_rows_end(const int32_t* rs, int klast, int n,
 // resident workgroup reads, at unit U, either tile ntq-1-U/g (first phase) or
 // tile U/g + 2nkb-2-ntq (second phase) of query head U%g: the workgroups of
 // one XCD share two tiles at a time, which the XCD's L2 keeps.
-// With documents a work item is one key block, swept down from the last tile
-// of its last document: the blocks of one document start on the same tile.
+// With documents the same pairing is made inside each run of key blocks
+// whose last keys lie in one document (they share the end of their rows):
+// block r0 + t goes with block r1 - 1 - t, the later one swept down from the
+// document's last tile, then the earlier one up to it, so the pairs of a
+// run do equal work and read the same tile at the same time.  The workgroup
+// of the earlier block does the pair; the later block's exits at once.
+// Which blocks form a run is read from the bounds (see docs_partner below).
 template <int D, bool HAS_MASK, bool CAUSAL, bool DOCS>
 __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdParams p) {
   static_assert(CAUSAL || !DOCS, "documents are causal");
@@ -287,11 +315,18 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdParams p) {
   const int b = rem / p.Hkv;
   const int kvh = rem % p.Hkv;
   const int ntq = (p.n + L::kRows - 1) / L::kRows;   // query tiles per head
-  const int nph = (CAUSAL && !DOCS && p.n_kblocks - 1 - w != w) ? 2 : 1;
+  int nph = (CAUSAL && p.n_kblocks - 1 - w != w) ? 2 : 1;
+  int kb_first = p.n_kblocks - 1 - w;   // the block of the first phase (the pair's later block)
+  if (DOCS) {
+    kb_first = docs_partner(p.doc_start + int64_t(b) * p.n, w, p.n, p.n_kblocks, lane);
+    if (kb_first < w) return;           // the partner's workgroup does this pair (uniform: no barrier passed yet)
+    nph = kb_first == w ? 1 : 2;
+  }
 
   for (int ph = 0; ph < nph; ++ph) {
+    // causal: the first phase (the later block, or a block alone) sweeps down, the second up
     const bool down = CAUSAL && ph == 0;
-    const int kb = (down && !DOCS) ? p.n_kblocks - 1 - w : w;
+    const int kb = down ? kb_first : w;
     const int k0w = kb * kKeys + wave * 32;        // first key of this wave
     const int u = k0w + l32;                       // this lane's key
     const bool wave_live = k0w < p.n;
