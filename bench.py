@@ -381,10 +381,25 @@ def main():
     def dev_bits(bits):
         return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
 
-    q_seq = dev_bits(synth.normal_bf16(g[synth.STREAM_Q], (P, 1, nl, w.Hq_global, D)))
-    k_seq = dev_bits(synth.normal_bf16(g[synth.STREAM_K], (P, 1, nl, w.Hkv_global, D)))
-    v_seq = dev_bits(synth.normal_bf16(g[synth.STREAM_V], (P, 1, nl, w.Hkv_global, D)))
-    do_seq = dev_bits(synth.normal_bf16(g[synth.STREAM_DO], (P, 1, nl, w.Hq_global, D)))
+    big = P * nl * w.Hq_global * D > (1 << 30)
+    if big:
+        # tensors of several GB (the 1M-token workload's 32 shards): drawn on the device from a
+        # seeded generator (same shapes and N(0,1) bf16 values; host generation would take minutes)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(w.number)
+
+        def draw(shape):
+            return torch.randn(shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+
+        q_seq = draw((P, 1, nl, w.Hq_global, D))
+        k_seq = draw((P, 1, nl, w.Hkv_global, D))
+        v_seq = draw((P, 1, nl, w.Hkv_global, D))
+        do_seq = draw((P, 1, nl, w.Hq_global, D))
+    else:
+        q_seq = dev_bits(synth.normal_bf16(g[synth.STREAM_Q], (P, 1, nl, w.Hq_global, D)))
+        k_seq = dev_bits(synth.normal_bf16(g[synth.STREAM_K], (P, 1, nl, w.Hkv_global, D)))
+        v_seq = dev_bits(synth.normal_bf16(g[synth.STREAM_V], (P, 1, nl, w.Hkv_global, D)))
+        do_seq = dev_bits(synth.normal_bf16(g[synth.STREAM_DO], (P, 1, nl, w.Hq_global, D)))
     # packed documents (global positions, the same on every rank after the exchange)
     valid_np = ds_np = valid_t = ds_t = None
     if w.docs:
@@ -529,7 +544,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic",
+        "data": "synthetic" + (" (drawn on the device, seeded)" if big else ""),
         "config": {"workload": w.name + ("+document-mask" if args.docs else ""), "n": n, "P": P, "q_heads": hq,
                    "kv_heads": hkv, "head_dim": D, "global_q_shape": [P, 1, nl, w.Hq_global, D], "causal": True,
                    "padding_mask": valid_np is not None, "document_mask": bool(args.docs),
