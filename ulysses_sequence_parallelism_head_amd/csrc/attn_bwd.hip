@@ -169,19 +169,21 @@ __device__ __forceinline__ u32x4 pack8_residual(const float* x, const u32x4 hi) 
 
 // One 32-row block of a staged query tile against this wave's 32 keys, after
 // S and dP are in registers: P, dS, then dV^T += dO^T P and dK^T += Q^T dS.
-// SPLIT adds the bf16 residuals of P and dS as second MFMAs.  LOWER applies
-// the rows' document bounds (key u is visible to row t only if u >= bound).
-template <int D, bool DOCS, bool CAUSAL, bool SPLIT, bool LOWER>
+// SPLIT adds the bf16 residuals of P and dS as second MFMAs.  DIAG applies
+// the causal mask (only tiles that reach above the block's last key need
+// it).  LOWER applies the rows' document bounds (key u is visible to row t
+// only if u >= bound).
+template <int D, bool DOCS, bool CAUSAL, bool SPLIT, bool DIAG, bool LOWER>
 __device__ __forceinline__ void dkdv_rows(const uint8_t* qs, const uint8_t* dos, const float* lses, const float* dls,
                                           const int32_t* los, const f32x16& s, const f32x16& dp, int rb, int t0, int u,
-                                          bool key_ok, int hh, int lane, float c, f32x16 (&dka)[D / 32],
+                                          int hh, int lane, float c, f32x16 (&dka)[D / 32],
                                           f32x16 (&dva)[D / 32]) {
   using L = DkdvLayout<D, DOCS>;
   constexpr int DJ = D / 32;
   float pr[16], ds[16];
   // element i is query row t0 + 4hh + C_i (C_i = rb*32 + (i/4)*8 + i%4, a
   // compile-time constant); the key is visible iff u <= row, i.e. C_i >= lim
-  const int lim = CAUSAL ? u - t0 - 4 * hh : -0x7fffffff;
+  const int lim = (CAUSAL && DIAG) ? u - t0 - 4 * hh : -0x7fffffff;
 #pragma unroll
   for (int g4 = 0; g4 < 4; ++g4) {
     const int rr = rb * 32 + g4 * 8 + hh * 4;
@@ -193,9 +195,11 @@ __device__ __forceinline__ void dkdv_rows(const uint8_t* qs, const uint8_t* dos,
     for (int e = 0; e < 4; ++e) {
       const int i = g4 * 4 + e;
       const int ci = rb * 32 + g4 * 8 + e;
-      const bool ok = key_ok && ci >= lim && (!LOWER || b4[e] <= u);
+      const bool ok = (!(CAUSAL && DIAG) || ci >= lim) && (!LOWER || b4[e] <= u);
       // invisible keys, and rows with no visible key (base-2 LSE = +inf), get
-      // exponent -inf: exp2(-inf) = 0 exactly
+      // exponent -inf: exp2(-inf) = 0 exactly.  A key that is padding or past
+      // n is not masked here: its P and dS reach only its own column of dV^T
+      // and dK^T (the lane's key), which the epilogue writes as zero.
       const float x = ok ? fmaf(s[i], c, -l4[e]) : -INFINITY;
       const float pv = __builtin_amdgcn_exp2f(x);
       pr[i] = pv;
@@ -384,8 +388,9 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdParams p) {
     // dK/dV accumulator registers differently and copy all of them at every
     // merge.
     // (forced inline: as a call the wave index would arrive in a vector register)
-    auto run = [&](int it0, int it1, auto split_tag, auto lower_tag) __attribute__((always_inline)) {
+    auto run = [&](int it0, int it1, auto split_tag, auto diag_tag, auto lower_tag) __attribute__((always_inline)) {
       constexpr bool SPLIT = decltype(split_tag)::value;
+      constexpr bool DIAG = decltype(diag_tag)::value;
       constexpr bool LOWER = decltype(lower_tag)::value;
       for (int it = it0; it < it1; ++it) {
         // prefetch unit it+1 into the other buffer while computing on this one
@@ -426,22 +431,40 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdParams p) {
           pipeline_reads_mfma<6, 4 * KK>();
 #pragma unroll
           for (int rb = 0; rb < 2; ++rb)
-            dkdv_rows<D, DOCS, CAUSAL, SPLIT, LOWER>(qs, dos, lses, dls, los, s[rb], dp[rb], rb, t0, u, key_ok, hh,
-                                                     lane, p.c, dka, dva);
+            dkdv_rows<D, DOCS, CAUSAL, SPLIT, DIAG, LOWER>(qs, dos, lses, dls, los, s[rb], dp[rb], rb, t0, u, hh,
+                                                           lane, p.c, dka, dva);
         }
         wait_vmem();
         __syncthreads();
       }
     };
-    // tiles below split_end need the split: tfirst .. min(ceil(split_end / kRows), tend) - 1
+    // tiles below split_end need the split: tfirst .. min(ceil(split_end / kRows), tend) - 1.
+    // The causal mask is needed on the tiles whose first row lies below the
+    // block's last key: tfirst and tfirst + 1 (the block starts a tile and
+    // spans two).  Both ranges sit at the diagonal end of the sweep, so the
+    // units split into at most three runs: both kinds, one kind, neither.
     const int nsplit = max(0, min((split_end + L::kRows - 1) / L::kRows, tend) - tfirst) * p.g;
+    const int ndiag = CAUSAL ? min(kKeys / L::kRows, tend - tfirst) * p.g : 0;
     auto sweep = [&](auto lower_tag) __attribute__((always_inline)) {
-      if (down) {                       // split tiles come last
-        run(0, niter - nsplit, std::false_type{}, lower_tag);
-        run(niter - nsplit, niter, std::true_type{}, lower_tag);
-      } else {                          // split tiles come first
-        run(0, nsplit, std::true_type{}, lower_tag);
-        run(nsplit, niter, std::false_type{}, lower_tag);
+      using T = std::true_type;
+      using F = std::false_type;
+      const int n1 = min(nsplit, ndiag), n2 = max(nsplit, ndiag);
+      // runs by distance from the diagonal end: [0, n1) both, [n1, n2) one, [n2, niter) neither
+      auto seg = [&](int a, int z, auto split_tag, auto diag_tag) __attribute__((always_inline)) {
+        if (a >= z) return;
+        if (down) run(niter - z, niter - a, split_tag, diag_tag, lower_tag);
+        else run(a, z, split_tag, diag_tag, lower_tag);
+      };
+      if (down) {                       // the diagonal end comes last
+        seg(n2, niter, F{}, F{});
+        if (nsplit > ndiag) seg(n1, n2, T{}, F{});
+        else seg(n1, n2, F{}, T{});
+        seg(0, n1, T{}, T{});
+      } else {                          // the diagonal end comes first
+        seg(0, n1, T{}, T{});
+        if (nsplit > ndiag) seg(n1, n2, T{}, F{});
+        else seg(n1, n2, F{}, T{});
+        seg(n2, niter, F{}, F{});
       }
     };
     if constexpr (DOCS) {
@@ -452,7 +475,9 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdParams p) {
       sweep(std::false_type{});
     }
 
-    // write dK = scale * dK^T^T and dV: lane = key u, dims 32j + 8*(i/4) + 4hh + i%4
+    // write dK = scale * dK^T^T and dV: lane = key u, dims 32j + 8*(i/4) + 4hh + i%4;
+    // a padding key's gradients are zero (selected, not multiplied: its
+    // unmasked column may hold any value, inf or NaN included)
     if (u < p.n) {
       const int64_t base = ((int64_t(b) * p.n + u) * p.Hkv + kvh) * D;
 #pragma unroll
@@ -460,11 +485,12 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdParams p) {
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
           const int d0 = j * 32 + i4 * 8 + hh * 4;
-          *reinterpret_cast<f32x4*>(p.dk + base + d0) =
-              f32x4{dka[j][i4 * 4] * p.scale, dka[j][i4 * 4 + 1] * p.scale, dka[j][i4 * 4 + 2] * p.scale,
-                    dka[j][i4 * 4 + 3] * p.scale};
-          *reinterpret_cast<f32x4*>(p.dv + base + d0) =
-              f32x4{dva[j][i4 * 4], dva[j][i4 * 4 + 1], dva[j][i4 * 4 + 2], dva[j][i4 * 4 + 3]};
+          f32x4 kv4 = f32x4{dka[j][i4 * 4] * p.scale, dka[j][i4 * 4 + 1] * p.scale, dka[j][i4 * 4 + 2] * p.scale,
+                            dka[j][i4 * 4 + 3] * p.scale};
+          f32x4 vv4 = f32x4{dva[j][i4 * 4], dva[j][i4 * 4 + 1], dva[j][i4 * 4 + 2], dva[j][i4 * 4 + 3]};
+          if (!key_ok) kv4 = vv4 = f32x4{0.f, 0.f, 0.f, 0.f};
+          *reinterpret_cast<f32x4*>(p.dk + base + d0) = kv4;
+          *reinterpret_cast<f32x4*>(p.dv + base + d0) = vv4;
         }
     }
   }
