@@ -527,11 +527,13 @@ __device__ __forceinline__ void dq_issue(uint8_t* stage, uint32_t& vbyte, const 
 }
 
 // One 32-key half of a staged K/V tile against this wave's 32 query rows:
-// S^T and dP^T, dS^T, then dQ^T += K^T dS^T.  `lim`: key row C of the half is
-// visible iff C <= lim (and its valid byte is set when HAS_MASK), and with
-// documents iff also C >= lo.  SPLIT adds the bf16 residual of dS as second
-// MFMAs.
-template <int D, bool HAS_MASK, bool SPLIT, bool DOCS>
+// S^T and dP^T, dS^T, then dQ^T += K^T dS^T.  With MASKED, key row C of the
+// half is visible iff C <= lim, and with documents iff also C >= lo;
+// without it every key is (the tile lies wholly below the diagonal and
+// inside n).  With HAS_MASK a key is visible
+// only if its valid byte is set.  SPLIT adds the bf16 residual of dS as
+// second MFMAs.
+template <int D, bool HAS_MASK, bool SPLIT, bool DOCS, bool MASKED>
 __device__ __forceinline__ void dq_half(const uint8_t* ks, const uint8_t* vs, const uint8_t* vb, int half, int lim,
                                         int lo, const u32x4 (&qf)[D / 16], const u32x4 (&df)[D / 16], float lse2,
                                         float dl, float c, int l32, int hh, int lane, f32x16 (&dqa)[D / 32]) {
@@ -557,7 +559,7 @@ __device__ __forceinline__ void dq_half(const uint8_t* ks, const uint8_t* vs, co
     for (int e = 0; e < 4; ++e) {
       const int i = g4 * 4 + e;
       const int ci = g4 * 8 + e;
-      const bool ok = ci <= lim && (!DOCS || ci >= lo) && (!HAS_MASK || ((vw >> (8 * e)) & 0xffu));
+      const bool ok = (!MASKED || (ci <= lim && (!DOCS || ci >= lo))) && (!HAS_MASK || ((vw >> (8 * e)) & 0xffu));
       // invisible keys (and rows with no visible key: lse2 = +inf) get exponent -inf
       const float x = ok ? fmaf(s[i], c, -lse2) : -INFINITY;
       ds[i] = __builtin_amdgcn_exp2f(x) * (dp[i] - dl);
@@ -660,8 +662,19 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const BwdParams p) {
     wait_vmem();
     __syncthreads();
 
+    // Tiles that need the index masks: the causal diagonal (tiles reaching
+    // past the workgroup's first row) and the tail past n, the last ones.
+    // The steps split into a run without and a run with them, decided
+    // outside the loop.  With documents every tile takes the masks (measured:
+    // the split gained nothing there).
     const int nsteps = ntiles - it_first;
-    for (int j = 0; j < nsteps; ++j) {
+    const int first_row = pb * p.pw;
+    int mask_from = CAUSAL ? max(first_row - L::kBN + 1, 0) : p.n - L::kBN + 1;   // first key0 of a masked tile
+    mask_from = min(mask_from, p.n - L::kBN + 1);
+    const int j_hi = DOCS ? 0 : min(max((mask_from + L::kBN - 1) / L::kBN - it_first, 0), nsteps);   // steps >= j_hi masked
+    auto steps = [&](int j0, int j1, auto masked_tag) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    for (int j = j0; j < j1; ++j) {
       const int it = it_first + j;
       // prefetch tile it+1 into the other buffer while computing on this one
       uint8_t* cur = smem + (j & 1) * L::kStageAligned;
@@ -681,13 +694,17 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const BwdParams p) {
           if (CAUSAL) lim = min(lim, t - key0 - 4 * hh);
           // documents: key >= the row's bound (no-op above the last row's bound)
           const int lo = (DOCS && tile0 < lo_last) ? lo_row - key0 - 4 * hh : -0x7fffffff;
-          dq_half<D, HAS_MASK, SPLIT, DOCS>(ks, vs, vb, half, lim, lo, qf, df, lse2, dl, p.c, l32, hh, lane, dqa);
+          dq_half<D, HAS_MASK, SPLIT, DOCS, MASKED>(ks, vs, vb, half, lim, lo, qf, df, lse2, dl, p.c, l32, hh, lane,
+                                                    dqa);
         }
       }
       if (HAS_MASK && it + 1 < ntiles && tid < L::kBN) nxt[L::kOffValid + tid] = uint8_t(vbyte);
       wait_vmem();
       __syncthreads();
     }
+    };
+    if (!DOCS) steps(0, j_hi, std::false_type{});
+    steps(j_hi, nsteps, std::true_type{});
 
     if (t < p.n) {
       const int64_t base = ((int64_t(b) * p.n + t) * p.Hq + head) * D;
