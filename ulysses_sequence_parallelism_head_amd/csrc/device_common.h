@@ -131,9 +131,28 @@ __device__ __forceinline__ u32x2 ds_read_tr16_b64(const uint8_t* lds) {
 template <int ROW_BYTES>
 __device__ __forceinline__ u32x4 tr_operand(const uint8_t* tile, int r0, int col0, int lane) {
   const int hh = lane >> 5;
-  const int r = r0 + 4 * hh + ((lane & 15) >> 2);
+  // the swizzle depends on the low four row bits only, so the 16-row-aligned
+  // r0 is a plain byte offset (an immediate when r0 is a constant)
+  const int rr = 4 * hh + ((lane & 15) >> 2);
   const int col = col0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   const int sub = (col & 7) * 2;                    // byte offset inside the 16-byte chunk (0 or 8)
+  const uint8_t* t = tile + r0 * ROW_BYTES + sub;
+  const u32x2 a = ds_read_tr16_b64(t + rm_off<ROW_BYTES>(rr, col >> 3));
+  const u32x2 b = ds_read_tr16_b64(t + rm_off<ROW_BYTES>(rr + 8, col >> 3));
+  return u32x4{a[0], a[1], b[0], b[1]};
+}
+
+// The same operand with r0 inside the swizzled row index.  Identical
+// addresses; for kernels at the edge of their register budget this form
+// lets the compiler recompute addresses instead of keeping one per 16-row
+// block live across the loop (in dkdv the folded form parks them in
+// accumulator registers and costs more moves than it saves adds).
+template <int ROW_BYTES>
+__device__ __forceinline__ u32x4 tr_operand_rows(const uint8_t* tile, int r0, int col0, int lane) {
+  const int hh = lane >> 5;
+  const int r = r0 + 4 * hh + ((lane & 15) >> 2);
+  const int col = col0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int sub = (col & 7) * 2;
   const u32x2 a = ds_read_tr16_b64(tile + rm_off<ROW_BYTES>(r, col >> 3) + sub);
   const u32x2 b = ds_read_tr16_b64(tile + rm_off<ROW_BYTES>(r + 8, col >> 3) + sub);
   return u32x4{a[0], a[1], b[0], b[1]};
