@@ -189,3 +189,45 @@ def test_bwd_pipeline_matches_unsharded():
     assert_close("dQ", oracle.unshard(to_host_f64(dq_seq)), dQ, 1e-2)
     assert_close("dK", oracle.unshard(to_host_f64(dk_seq)), dK, 1e-2)
     assert_close("dV", oracle.unshard(to_host_f64(dv_seq)), dV, 1e-2)
+
+
+@pytest.mark.parametrize("docs", [False, True])
+def test_bwd_padding_keys_extreme_values(docs):
+    """Padding keys whose K and V rows are huge (scores far above every
+    row's logsumexp, so an unmasked exp would overflow): the key-stationary
+    pass leaves such keys unmasked and writes their dK/dV as zero, so every
+    gradient must stay finite, padding keys must get exactly zero dK/dV and
+    the rest must match the oracle, which never looks at padding keys."""
+    n, Hq, Hkv, D = 300, 8, 2, 128
+    say(f"bwd padding keys with extreme values, n={n}, documents={docs}")
+    q, k, v, do, valid = _inputs(5150 + docs, n, Hq, Hkv, D, True)
+    pad = valid[0] == 0
+    assert pad.any() and (~pad).any()
+    k = np.where(pad[None, :, None, None], np.uint16(0x4270), k)   # bf16 60.0 in every dim
+    v = np.where(pad[None, :, None, None], np.uint16(0xC270), v)   # bf16 -60.0
+    scale = D ** -0.5
+    ds = None
+    if docs:
+        starts = np.array([0, 97, 98, 211])
+        ds = np.zeros((1, n), np.int32)
+        for s0 in starts:
+            ds[0, s0:] = s0
+    dQ, dK, dV, _, _ = oracle.attn_bwd(to_f64(q), to_f64(k), to_f64(v), to_f64(do), scale, True, valid,
+                                       **({} if ds is None else {"doc_start": ds}))
+    tq, tk, tv, tdo = bits_to_device(q), bits_to_device(k), bits_to_device(v), bits_to_device(do)
+    tval = torch.from_numpy(valid).to("cuda:0")
+    if docs:
+        tds = torch.from_numpy(ds).to("cuda:0")
+        o, lse = U.ulysses_attn_fwd_docs(tq, tk, tv, tds, tval, scale, o_dtype=torch.float32)
+        dq, dk, dv = U.ulysses_attn_bwd_docs(tq, tk, tv, o, lse, tdo, tds, tval, scale)
+    else:
+        o, lse = U.ulysses_attn_fwd(tq, tk, tv, tval, scale, True, o_dtype=torch.float32)
+        dq, dk, dv = U.ulysses_attn_bwd(tq, tk, tv, o, lse, tdo, tval, scale, True)
+    torch.cuda.synchronize()
+    dq, dk, dv = to_host_f64(dq), to_host_f64(dk), to_host_f64(dv)
+    for name, x in (("dQ", dq), ("dK", dk), ("dV", dv)):
+        assert np.all(np.isfinite(x)), f"{name}: non-finite value"
+    assert np.all(dk[0, pad] == 0.0) and np.all(dv[0, pad] == 0.0)
+    assert_close("dQ", dq, dQ, 1e-2)
+    assert_close("dK", dk, dK, 1e-2)
+    assert_close("dV", dv, dV, 1e-2)
