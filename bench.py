@@ -64,17 +64,17 @@ HBM_PEAK_GBS = 8000.0
 CSRC = os.path.join(ROOT, "ulysses_sequence_parallelism_head_amd", "csrc")
 MEASURED_TRAFFIC = {      # keyed by (call, workload as named in the config)
     ("attn_bwd", "gqa-n65536-8q2kv-d128-bf16-fwd+repack"): {
-        "bytes": 6.990e9, "sources": ("attn_bwd.hip", "device_common.h", "internal.h"),
-        "sha256": "f2c981e9f998ade69a0f3f5ce1048ca9c167218baaf22c97363f1d90e5d57037"},
+        "bytes": 6.787e9, "sources": ("attn_bwd.hip", "device_common.h", "internal.h"),
+        "sha256": "db5a6e58eca61e83afc312b1a7bd0b3de725b0f287e527633e81ea32e1edf995"},
     ("attn_fwd", "gqa-n65536-8q2kv-d128-bf16-fwd+repack"): {
-        "bytes": 3.037e9, "sources": ("attn_fwd.hip", "device_common.h", "internal.h"),
-        "sha256": "4ce050035ff61e6892558e7aec2c9524c2e92b5093bb50b1aafd8379c3559ee2"},
+        "bytes": 3.158e9, "sources": ("attn_fwd.hip", "device_common.h", "internal.h"),
+        "sha256": "3c5f387ee4c874ff1d7657a0fd6b547040edcc8c24abfe57128e083467788abd"},
     ("attn_bwd", "gqa-n98304-8q2kv-d128-bf16-docs-fwd+bwd+document-mask"): {
-        "bytes": 6.277e9, "sources": ("attn_bwd.hip", "device_common.h", "internal.h"),
-        "sha256": "f2c981e9f998ade69a0f3f5ce1048ca9c167218baaf22c97363f1d90e5d57037"},
+        "bytes": 6.224e9, "sources": ("attn_bwd.hip", "device_common.h", "internal.h"),
+        "sha256": "db5a6e58eca61e83afc312b1a7bd0b3de725b0f287e527633e81ea32e1edf995"},
     ("attn_fwd", "gqa-n98304-8q2kv-d128-bf16-docs-fwd+bwd+document-mask"): {
-        "bytes": 2.516e9, "sources": ("attn_fwd.hip", "device_common.h", "internal.h"),
-        "sha256": "4ce050035ff61e6892558e7aec2c9524c2e92b5093bb50b1aafd8379c3559ee2"},
+        "bytes": 2.514e9, "sources": ("attn_fwd.hip", "device_common.h", "internal.h"),
+        "sha256": "3c5f387ee4c874ff1d7657a0fd6b547040edcc8c24abfe57128e083467788abd"},
 }
 
 
@@ -549,7 +549,8 @@ def main():
                    "kv_heads": hkv, "head_dim": D, "global_q_shape": [P, 1, nl, w.Hq_global, D], "causal": True,
                    "padding_mask": valid_np is not None, "document_mask": bool(args.docs),
                    "rope_fused": bool(args.rope_loss), "loss_aggregation": bool(args.rope_loss),
-                   "visible_pairs_per_head": pairs},
+                   "visible_pairs_per_head": pairs,
+                   "step": "seq2head(q,k,v) > attn_fwd > seq2head(dO) > attn_bwd > head2seq(o) > head2seq(dq,dk,dv)"},
         "breakdown_ms": {k: round(v, 4) for k, v in avg.items()},
         "attn_fwd_tflops": round(fwd_tf, 2),
         "attn_fwd_frac_mfma_peak": round(fwd_tf / MFMA_BF16_PEAK_TFLOPS, 4),
