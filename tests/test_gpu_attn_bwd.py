@@ -151,6 +151,25 @@ def test_bwd_96k_docs_workload_sampled():
     assert_close("dV rows", dv[:, k_rows], dVs, 1e-2)
 
 
+def test_bwd_64k_workload_sampled():
+    """Workload 3 at full size (n = 65536, 8q/2kv, d128, causal: the shapes
+    bench.py times): dQ on stratified rows, dK/dV on key rows in the last
+    1024 positions (where the oracle needs few rows)."""
+    say("bwd workload 3 (64K) sampled")
+    d = synth.local_attention_inputs(3, with_grad=True)
+    w = d["workload"]
+    q_rows = synth.stratified_rows(d["row_gen"], w.n, 40)
+    # keys in the last 1024 positions: seeded picks, the ends and 64/128-key tile edges
+    k_rows = (w.n - 1024) + synth.sample_rows(d["row_gen"], 1024, 12, extra=(0, 1, 511, 512, 895, 896, 959, 960,
+                                                                            1022, 1023))
+    dq, dk, dv = _gpu_fwd_bwd(d["q"], d["k"], d["v"], d["do"], None, w.scale, True, torch.float32)
+    dQs, dKs, dVs = oracle.attn_bwd_sampled(to_f64(d["q"]), to_f64(d["k"]), to_f64(d["v"]), to_f64(d["do"]),
+                                            w.scale, True, None, q_rows=q_rows, k_rows=k_rows)
+    assert_close("dQ rows", dq[:, q_rows], dQs, 1e-2)
+    assert_close("dK rows", dk[:, k_rows], dKs, 1e-2)
+    assert_close("dV rows", dv[:, k_rows], dVs, 1e-2)
+
+
 def test_bwd_deterministic():
     say("bwd determinism")
     q, k, v, do, valid = _inputs(77, 900, 8, 2, 128, True)
