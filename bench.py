@@ -499,6 +499,22 @@ def main():
     ms_step = wall * 1e3 / args.steps
     avg = {k: float(np.mean(v)) for k, v in per.items()}
 
+    # reference for the repacks, outside the timed steps: a plain 512 MiB device-to-device
+    # copy on the same stream (HIP events, median of 5)
+    csrc = torch.empty(1 << 28, dtype=torch.int16, device=dev).fill_(1)
+    cdst = torch.empty_like(csrc)
+    cdst.copy_(csrc)
+    cms = []
+    for _ in range(5):
+        c0, c1 = Ev(enable_timing=True), Ev(enable_timing=True)
+        c0.record()
+        cdst.copy_(csrc)
+        c1.record()
+        torch.cuda.synchronize()
+        cms.append(c0.elapsed_time(c1))
+    copy_gbs = 2 * csrc.numel() * 2 / (float(np.median(cms)) * 1e-3) / 1e9
+    del csrc, cdst
+
     pairs = int(visible_keys(n, valid_np, ds_np if args.docs else None).sum())
     fwd_flops = 4.0 * D * hq * pairs
     bwd_flops = 10.0 * D * hq * pairs
@@ -558,6 +574,8 @@ def main():
         "attn_bwd_frac_mfma_peak": round(bwd_tf / MFMA_BF16_PEAK_TFLOPS, 4),
         "repack_GBs": {k: round(v, 1) for k, v in rep.items()},
         "repack_frac_hbm_peak": {k: round(v / HBM_PEAK_GBS, 4) for k, v in rep.items()},
+        "device_copy_512MiB_GBs": round(copy_gbs, 1),
+        "repack_frac_device_copy": {k: round(v / copy_gbs, 4) for k, v in rep.items()},
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
