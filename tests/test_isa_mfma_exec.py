@@ -1,6 +1,7 @@
 """The compiled gfx950 kernels never reach a matrix-core instruction with an
 empty EXEC mask (MFMA ignores EXEC, so such an instruction would add garbage
-to an accumulator).  Compiles every HIP source to assembly with hipcc."""
+to an accumulator), and none uses scratch memory (register spills).
+Compiles every HIP source to assembly with hipcc."""
 import shutil
 
 import pytest
@@ -23,6 +24,18 @@ def test_scanner_flags_unskipped_mfma():
     ])
     bad = isa_check.scan(asm)
     assert len(bad) == 1 and bad[0][1] == 4
+
+
+def test_scratch_parser():
+    asm = "\n".join([
+        "\t.amdhsa_kernel kern_a",
+        "\t\t.amdhsa_private_segment_fixed_size 0",
+        "\t.end_amdhsa_kernel",
+        "\t.amdhsa_kernel kern_b",
+        "\t\t.amdhsa_private_segment_fixed_size 28",
+        "\t.end_amdhsa_kernel",
+    ])
+    assert isa_check.scratch_kernels(asm) == [("kern_b", 28)]
 
 
 @pytest.mark.skipif(shutil.which("hipcc") is None and not __import__("os").path.exists(isa_check.HIPCC),

@@ -221,10 +221,14 @@ __device__ __forceinline__ void dkdv_rows(const uint8_t* qs, const uint8_t* dos,
   for (int f = 0; f < 2; ++f) {
 #pragma unroll
     for (int j = 0; j < DJ; ++j) {
-      const u32x4 adt = tr_operand_rows<L::kRowBytes>(dos, rb * 32 + 16 * f, 32 * j, lane);
+      // (the document variants take the folded row offset: with their extra
+      // live values the row-wise form spills)
+      const u32x4 adt = DOCS ? tr_operand<L::kRowBytes>(dos, rb * 32 + 16 * f, 32 * j, lane)
+                             : tr_operand_rows<L::kRowBytes>(dos, rb * 32 + 16 * f, 32 * j, lane);
       dva[j] = mfma32x32x16(adt, ph[f], dva[j]);
       if (SPLIT) dva[j] = mfma32x32x16(adt, pl[f], dva[j]);
-      const u32x4 aqt = tr_operand_rows<L::kRowBytes>(qs, rb * 32 + 16 * f, 32 * j, lane);
+      const u32x4 aqt = DOCS ? tr_operand<L::kRowBytes>(qs, rb * 32 + 16 * f, 32 * j, lane)
+                             : tr_operand_rows<L::kRowBytes>(qs, rb * 32 + 16 * f, 32 * j, lane);
       dka[j] = mfma32x32x16(aqt, dh[f], dka[j]);
       if (SPLIT) dka[j] = mfma32x32x16(aqt, dl[f], dka[j]);
     }

@@ -1,5 +1,7 @@
-"""Static check of the generated gfx950 assembly: no matrix-core (MFMA)
-instruction may be reachable with an empty EXEC mask.
+"""Static checks of the generated gfx950 assembly: no matrix-core (MFMA)
+instruction may be reachable with an empty EXEC mask, and no kernel may use
+scratch memory (a register spill costs a memory round trip per use in the
+hot loops; every kernel here is sized to fit its registers).
 
 MFMA instructions do not honour the EXEC mask, so a divergent `if` around one
 (which the compiler lowers to s_and_saveexec ... s_or_b64 exec without a
@@ -54,6 +56,26 @@ def scan(asm: str):
     return bad
 
 
+_KERNEL = re.compile(r"^\s*\.amdhsa_kernel\s+(\S+)")
+_PRIVATE = re.compile(r"^\s*\.amdhsa_private_segment_fixed_size\s+(\d+)")
+
+
+def scratch_kernels(asm: str):
+    """Return [(kernel, bytes per lane)] of kernels whose descriptor asks for
+    a private (scratch) segment."""
+    found = []
+    kernel = None
+    for line in asm.splitlines():
+        m = _KERNEL.match(line)
+        if m:
+            kernel = m.group(1)
+            continue
+        m = _PRIVATE.match(line)
+        if m and kernel is not None and int(m.group(1)) > 0:
+            found.append((kernel, int(m.group(1))))
+    return found
+
+
 def check(verbose: bool = True):
     problems = []
     with tempfile.TemporaryDirectory() as tmp:
@@ -66,10 +88,13 @@ def check(verbose: bool = True):
             with open(out, encoding="utf-8") as f:
                 asm = f.read()
             found = scan(asm)
+            scratch = scratch_kernels(asm)
             n_mfma = sum(1 for l in asm.splitlines() if _MFMA.match(l))
             if verbose:
-                print(f"{os.path.basename(src)}: {n_mfma} MFMA, {len(found)} reachable with an empty EXEC")
+                print(f"{os.path.basename(src)}: {n_mfma} MFMA, {len(found)} reachable with an empty EXEC, "
+                      f"{len(scratch)} kernels with scratch")
             problems += [(os.path.basename(src), *b) for b in found]
+            problems += [(os.path.basename(src), k, 0, f"scratch: {n} bytes per lane") for k, n in scratch]
     return problems
 
 
