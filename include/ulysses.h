@@ -190,7 +190,8 @@ ULYSSES_API size_t ulysses_attn_bwd_workspace_bytes(int32_t B, int64_t n, int32_
  * [ALST] section "Provocarea antrenării cu secvențe lungi"):
  *   P = exp(s - lse), dV = P^T dO, dP = dO V^T, Dl = rowsum(dO * O),
  *   dS = P * (dP - Dl), dQ = scale * dS K, dK = scale * dS^T Q,
- * with dK and dV summed over the query heads sharing a KV head.
+ * with dK and dV summed over the query heads sharing a KV head.  A padding
+ * key (key_valid 0) gets dK = dV = 0 exactly, whatever its K and V rows hold.
  *
  *   q, k, v, key_valid   as for ulysses_attn_fwd (in_dtype)
  *   o          [B][n][Hq][D]   o_dtype   the forward output
