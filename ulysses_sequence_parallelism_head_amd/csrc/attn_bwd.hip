@@ -30,6 +30,11 @@
 //     tile.  Keeping dQ in its own pass
 //     avoids float32 atomics (whose traffic would grow as n^2 / block) and
 //     makes every gradient deterministic.
+// Masks run only on the tiles that need them, chosen per run of tiles
+// outside the loops: dkdv applies the causal compare on the two query tiles
+// at a key block's diagonal and no per-key mask at all (a padding key's P
+// and dS reach only its own dK/dV column, written as zero); dq applies the
+// causal and tail compares on the diagonal and tail tiles.
 // Rows below kSplitRows use a hi/lo bf16 split of P and dS (two MFMAs) for
 // accuracy where few keys carry large weights.
 // Packed documents (a per-row lower bound on the visible keys, the first
