@@ -515,7 +515,7 @@ struct DqLayout {
   static constexpr int kOffK = 0;
   static constexpr int kOffV = kOffK + kBytesRM;
   static constexpr int kOffValid = kOffV + kBytesRM;
-  static constexpr int kStage = kOffValid + kBN;
+  static constexpr int kStage = kOffValid + kBN * 4;     // per-key score bias: 0 (valid) or -inf
   static constexpr int kStageAligned = (kStage + 127) / 128 * 128;
 };
 
@@ -539,9 +539,9 @@ __device__ __forceinline__ void dq_issue(uint8_t* stage, uint32_t& vbyte, const 
 // S^T and dP^T, dS^T, then dQ^T += K^T dS^T.  With MASKED, key row C of the
 // half is visible iff C <= lim, and with documents iff also C >= lo;
 // without it every key is (the tile lies wholly below the diagonal and
-// inside n).  With HAS_MASK a key is visible
-// only if its valid byte is set.  SPLIT adds the bf16 residual of dS as
-// second MFMAs.
+// inside n).  With HAS_MASK the score accumulators start from the keys'
+// bias staged at vb (0, or -inf for a padding key), so the product applies
+// the key mask itself.  SPLIT adds the bf16 residual of dS as second MFMAs.
 template <int D, bool HAS_MASK, bool SPLIT, bool DOCS, bool MASKED>
 __device__ __forceinline__ void dq_half(const uint8_t* ks, const uint8_t* vs, const uint8_t* vb, int half, int lim,
                                         int lo, const u32x4 (&qf)[D / 16], const u32x4 (&df)[D / 16], float lse2,
@@ -551,6 +551,15 @@ __device__ __forceinline__ void dq_half(const uint8_t* ks, const uint8_t* vs, co
   constexpr int DJ = D / 32;
   // S^T[key][q] and dP^T[key][q]: lane = query row, rows key = (i/4)*8 + 4hh + i%4
   f32x16 s = f32x16{}, dp = f32x16{};
+  if (HAS_MASK) {
+    const float* bias = reinterpret_cast<const float*>(vb) + half * 32 + hh * 4;
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const f32x4 b4 = *reinterpret_cast<const f32x4*>(bias + g4 * 8);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[g4 * 4 + e] = b4[e];
+    }
+  }
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
     const int off = rm_off<L::kRowBytes>(half * 32 + l32, 2 * kk + hh);
@@ -562,13 +571,11 @@ __device__ __forceinline__ void dq_half(const uint8_t* ks, const uint8_t* vs, co
   // element i is key row C_i = (i/4)*8 + i%4 of the half (plus 4hh)
 #pragma unroll
   for (int g4 = 0; g4 < 4; ++g4) {
-    uint32_t vw = 0xffffffffu;
-    if (HAS_MASK) vw = *reinterpret_cast<const uint32_t*>(vb + half * 32 + g4 * 8 + hh * 4);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = g4 * 4 + e;
       const int ci = g4 * 8 + e;
-      const bool ok = (!MASKED || (ci <= lim && (!DOCS || ci >= lo))) && (!HAS_MASK || ((vw >> (8 * e)) & 0xffu));
+      const bool ok = !MASKED || (ci <= lim && (!DOCS || ci >= lo));
       // invisible keys (and rows with no visible key: lse2 = +inf) get exponent -inf
       const float x = ok ? fmaf(s[i], c, -lse2) : -INFINITY;
       ds[i] = __builtin_amdgcn_exp2f(x) * (dp[i] - dl);
@@ -667,7 +674,7 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const BwdParams p) {
     // addresses depend on the step counter only)
     uint32_t vbyte = 0;
     dq_issue<D, HAS_MASK>(smem, vbyte, p, b, kvh, it_first, wave, lane, tid);
-    if (HAS_MASK && tid < L::kBN) smem[L::kOffValid + tid] = uint8_t(vbyte);
+    if (HAS_MASK && tid < L::kBN) reinterpret_cast<float*>(smem + L::kOffValid)[tid] = vbyte ? 0.f : -INFINITY;
     wait_vmem();
     __syncthreads();
 
@@ -707,7 +714,8 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const BwdParams p) {
                                                     dqa);
         }
       }
-      if (HAS_MASK && it + 1 < ntiles && tid < L::kBN) nxt[L::kOffValid + tid] = uint8_t(vbyte);
+      if (HAS_MASK && it + 1 < ntiles && tid < L::kBN)
+        reinterpret_cast<float*>(nxt + L::kOffValid)[tid] = vbyte ? 0.f : -INFINITY;
       wait_vmem();
       __syncthreads();
     }

@@ -71,7 +71,7 @@ struct FwdLayout {
   static constexpr int kChunks = D / 8;                  // 16-byte chunks per row
   static constexpr int kBytesK = kBN * kRowBytes;
   static constexpr int kBytesV = kBN * kRowBytes;
-  static constexpr int kBytesValid = kBN;
+  static constexpr int kBytesValid = kBN * 4;            // per-key score bias: 0 (valid) or -inf
   static constexpr int kStage = kBytesK + kBytesV + kBytesValid;
   static constexpr int kStageAligned = (kStage + 127) / 128 * 128;
 };
@@ -189,7 +189,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const FwdPar
 
     uint32_t vbyte = 0;
     fwd_issue<D, HAS_MASK>(smem, vbyte, p, b, kvh, it_first, wave, lane, tid);
-    if (HAS_MASK && tid < kBN) smem[L::kBytesK + L::kBytesV + tid] = uint8_t(vbyte);
+    if (HAS_MASK && tid < kBN) reinterpret_cast<float*>(smem + L::kBytesK + L::kBytesV)[tid] = vbyte ? 0.f : -INFINITY;
     wait_vmem();
     __syncthreads();
 
@@ -208,7 +208,23 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const FwdPar
         // ---- S^T for the two 32-key halves.  On a causal diagonal tile the
         // second half may hold no visible key; it is computed anyway (its
         // scores are masked to -inf below, so it adds exact zeros to O).
+        // With padding the accumulators start from the keys' bias (0, or
+        // -inf for a padding key): the product applies the key mask itself
+        // (element i holds key 32*half + 8*(i/4) + 4hh + i%4).
         f32x16 s0 = f32x16{}, s1 = f32x16{};
+        if (HAS_MASK) {
+          const float* vb = reinterpret_cast<const float*>(cur + L::kBytesK + L::kBytesV);
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x4 b0 = *reinterpret_cast<const f32x4*>(vb + g4 * 8 + hh * 4);
+            const f32x4 b1 = *reinterpret_cast<const f32x4*>(vb + 32 + g4 * 8 + hh * 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              s0[g4 * 4 + e] = b0[e];
+              s1[g4 * 4 + e] = b1[e];
+            }
+          }
+        }
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
           const u32x4 a0 = *reinterpret_cast<const u32x4*>(ks + rm_off<L::kRowBytes>(l32, 2 * kk + hh));
@@ -238,16 +254,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const FwdPar
           for (int i = 0; i < 32; ++i) {
             const int ci = (i >> 4) * 32 + ((i & 15) >> 2) * 8 + (i & 3);
             x[i] = (ci > lim || ci < lo) ? -INFINITY : x[i];
-          }
-        }
-        if (HAS_MASK) {
-          const uint8_t* vb = cur + L::kBytesK + L::kBytesV;
-#pragma unroll
-          for (int grp = 0; grp < 8; ++grp) {
-            const int kt = (grp >> 2) * 32 + (grp & 3) * 8 + hh * 4;
-            const uint32_t w = *reinterpret_cast<const uint32_t*>(vb + kt);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) x[grp * 4 + e] = ((w >> (8 * e)) & 0xffu) ? x[grp * 4 + e] : -INFINITY;
           }
         }
 
@@ -312,7 +318,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const FwdPar
         if (!SPLIT) pipeline_tr_reads_mfma<4, 4 * DJ>();
       }
 
-      if (HAS_MASK && it + 1 < ntiles && tid < kBN) nxt[L::kBytesK + L::kBytesV + tid] = uint8_t(vbyte);
+      if (HAS_MASK && it + 1 < ntiles && tid < kBN)
+        reinterpret_cast<float*>(nxt + L::kBytesK + L::kBytesV)[tid] = vbyte ? 0.f : -INFINITY;
       wait_vmem();
       __syncthreads();
     };
