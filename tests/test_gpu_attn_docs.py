@@ -2,9 +2,9 @@
 documents: a token sees only earlier tokens of its own document) against
 the fp64 oracle, forward and backward, on the same bf16-rounded inputs.
 
-Tolerances are those of the plain attention tests: max-abs 1e-2 (plus the
-bf16 storage rounding of O where O is stored in bf16: one ulp of |O| on O,
-and its propagation into dQ/dK), 5e-5 for the fp32 path.
+Tolerances are those of the plain attention tests: max-abs 1e-2 (a bf16 O
+only widens it where |O| >= 4, by its own storage half-ulp; the gradients
+keep 1e-2 with either O), 5e-5 for the fp32 path.
 
 Layouts cover what the tile skipping and the lower mask must get right:
 documents shorter than a tile, boundaries exactly on and next to tile and
@@ -23,7 +23,6 @@ import oracle
 import synth
 import ulysses_sequence_parallelism_head_amd as U
 from tests.gpu_helpers import say, bits_to_device, f32_to_device, to_f64, to_host_f64, assert_close
-from tests.test_gpu_attn_bwd import o_rounding_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -129,7 +128,7 @@ def test_docs_fwd(n, Hq, Hkv, D, masked, names, o_dtype):
     scale = D ** -0.5
     O, L = oracle.attn_fwd(to_f64(q), to_f64(k), to_f64(v), scale, True, valid, doc_start=ds)
     got = _gpu(q, k, v, None, ds, valid, scale, o_dtype, backward=False)
-    assert_close("O", got["o"], O, 1e-2, rel_bf16_storage=o_dtype == torch.bfloat16)
+    assert_close("O", got["o"], O, 1e-2, bf16_out=o_dtype == torch.bfloat16)
     assert_close("LSE", got["lse"], L, 1e-2)
 
 
@@ -168,13 +167,8 @@ def test_docs_bwd(n, Hq, Hkv, D, masked, names, o_dtype):
     dQ, dK, dV, O, L = oracle.attn_bwd(to_f64(q), to_f64(k), to_f64(v), to_f64(do), scale, True, valid,
                                        doc_start=ds)
     got = _gpu(q, k, v, do, ds, valid, scale, o_dtype)
-    if o_dtype == torch.float32:
-        assert_close("dQ", got["dq"], dQ, 1e-2)
-        assert_close("dK", got["dk"], dK, 1e-2)
-    else:
-        bq, bk = o_rounding_bound(to_f64(q), to_f64(k), to_f64(do), O, L, scale, True, valid, doc_start=ds)
-        assert_close("dQ", got["dq"], dQ, 1e-2 + bq)
-        assert_close("dK", got["dk"], dK, 1e-2 + bk)
+    assert_close("dQ", got["dq"], dQ, 1e-2)
+    assert_close("dK", got["dk"], dK, 1e-2)
     assert_close("dV", got["dv"], dV, 1e-2)
 
 
@@ -241,18 +235,25 @@ def test_docs_96k_workload_sampled():
     rows = np.unique(np.concatenate([rows, synth.stratified_rows(d["row_gen"], w.n, 16, valid[0])]))
     k_rows = synth.sample_rows(d["row_gen"], w.n, 12, extra=(w.n - 1, w.n - 2, w.n - 1024))
     k_rows = k_rows[k_rows >= w.n - 1024]
-    got = _gpu(d["q"], d["k"], d["v"], d["do"], ds, valid, w.scale, torch.float32)
-    pad = valid[0] == 0
-    assert np.all(got["dk"][0, pad] == 0.0) and np.all(got["dv"][0, pad] == 0.0)
+    runs = {}
+    for o_dtype in (torch.bfloat16, torch.float32):
+        got = _gpu(d["q"], d["k"], d["v"], d["do"], ds, valid, w.scale, o_dtype)
+        pad = valid[0] == 0
+        assert np.all(got["dk"][0, pad] == 0.0) and np.all(got["dv"][0, pad] == 0.0)
+        runs[o_dtype] = {"o": got["o"][:, rows], "lse": got["lse"][:, :, rows], "dq": got["dq"][:, rows],
+                         "dk": got["dk"][:, k_rows], "dv": got["dv"][:, k_rows]}
+        del got
     qf, kf, vf, dof = to_f64(d["q"]), to_f64(d["k"]), to_f64(d["v"]), to_f64(d["do"])
     O, L = oracle.attn_fwd(qf, kf, vf, w.scale, True, valid, rows=rows, doc_start=ds)
-    assert_close("O rows", got["o"][:, rows], O, 1e-2)
-    assert_close("LSE rows", got["lse"][:, :, rows], L, 1e-2)
     dQs, dKs, dVs = oracle.attn_bwd_sampled(qf, kf, vf, dof, w.scale, True, valid, q_rows=rows, k_rows=k_rows,
                                             doc_start=ds)
-    assert_close("dQ rows", got["dq"][:, rows], dQs, 1e-2)
-    assert_close("dK rows", got["dk"][:, k_rows], dKs, 1e-2)
-    assert_close("dV rows", got["dv"][:, k_rows], dVs, 1e-2)
+    for o_dtype, got in runs.items():
+        say(f"  O stored as {o_dtype}")
+        assert_close("O rows", got["o"], O, 1e-2, bf16_out=o_dtype == torch.bfloat16)
+        assert_close("LSE rows", got["lse"], L, 1e-2)
+        assert_close("dQ rows", got["dq"], dQs, 1e-2)
+        assert_close("dK rows", got["dk"], dKs, 1e-2)
+        assert_close("dV rows", got["dv"], dVs, 1e-2)
 
 
 def test_docs_deterministic():

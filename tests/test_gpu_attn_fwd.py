@@ -2,8 +2,9 @@
 
 Tolerances (max-abs against the oracle on the same bf16-rounded inputs):
   * bf16 inputs, float32 O: 1e-2 on O and on LSE;
-  * bf16 inputs, bf16 O: 1e-2 plus one bf16 ulp of |O| (the storage rounding
-    of the output itself);
+  * bf16 inputs, bf16 O: 1e-2 (the storage rounding is at most 2^-7 while
+    |O| < 4); an element with |O| >= 4, where half a bf16 ulp alone exceeds
+    that, gets its half-ulp plus the same 1e-2 - 2^-7 compute margin;
   * float32 inputs and O (fp32 path): 5e-5.
 Shapes span several tiles with ragged tails, every GQA group size, both head
 dims, causal and not, with and without a key-padding mask; the full-size
@@ -75,7 +76,7 @@ def test_fwd_bf16_small(n, Hq, Hkv, D, causal, masked):
     assert_close("O(f32 out)", o32, O, 1e-2)
     assert_close("LSE", l32, L, 1e-2)
     o16, l16 = _run(q, k, v, valid, scale, causal, torch.bfloat16)
-    assert_close("O(bf16 out)", o16, O, 1e-2, rel_bf16_storage=True)
+    assert_close("O(bf16 out)", o16, O, 1e-2, bf16_out=True)
     assert np.array_equal(l16, l32)
 
 
@@ -127,7 +128,7 @@ def test_fwd_8k_workload_full():
     assert_close("O(f32 out)", o32, O, 1e-2)
     assert_close("LSE", l32, L, 1e-2)
     o16, _ = _run(d["q"], d["k"], d["v"], None, w.scale, True, torch.bfloat16)
-    assert_close("O(bf16 out)", o16, O, 1e-2, rel_bf16_storage=True)
+    assert_close("O(bf16 out)", o16, O, 1e-2, bf16_out=True)
 
 
 def _sampled(c, count):
@@ -145,6 +146,9 @@ def test_fwd_64k_workload_sampled():
     o32, l32 = _run(d["q"], d["k"], d["v"], None, w.scale, True, torch.float32)
     assert_close("O(f32 out)", o32[:, rows], O, 1e-2)
     assert_close("LSE", l32[:, :, rows], L, 1e-2)
+    o16, l16 = _run(d["q"], d["k"], d["v"], None, w.scale, True, torch.bfloat16)
+    assert_close("O(bf16 out)", o16[:, rows], O, 1e-2, bf16_out=True)
+    assert np.array_equal(l16, l32)
 
 
 def test_fwd_96k_docs_workload_sampled():
@@ -154,7 +158,7 @@ def test_fwd_96k_docs_workload_sampled():
     valid = d["valid"]
     O, L = oracle.attn_fwd(to_f64(d["q"]), to_f64(d["k"]), to_f64(d["v"]), w.scale, True, valid, rows=rows)
     o16, l = _run(d["q"], d["k"], d["v"], valid, w.scale, True, torch.bfloat16)
-    assert_close("O(bf16 out)", o16[:, rows], O, 1e-2, rel_bf16_storage=True)
+    assert_close("O(bf16 out)", o16[:, rows], O, 1e-2, bf16_out=True)
     assert_close("LSE", l[:, :, rows], L, 1e-2)
 
 
@@ -167,7 +171,7 @@ def test_fwd_1m_workload_sampled():
     rows = synth.sample_rows(d["row_gen"], w.n, 64, extra=(0, w.n - 1))
     O, L = oracle.attn_fwd(to_f64(d["q"]), to_f64(d["k"]), to_f64(d["v"]), w.scale, True, rows=rows, block=16)
     o16, l = _run(d["q"], d["k"], d["v"], None, w.scale, True, torch.bfloat16)
-    assert_close("O(bf16 out)", o16[:, rows], O, 1e-2, rel_bf16_storage=True)
+    assert_close("O(bf16 out)", o16[:, rows], O, 1e-2, bf16_out=True)
     assert_close("LSE", l[:, :, rows], L, 1e-2)
 
 

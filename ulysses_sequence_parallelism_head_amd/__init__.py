@@ -132,6 +132,26 @@ def _need_contig_cuda(*ts):
             raise ValueError("tensors must be contiguous and on the GPU")
 
 
+def _expect(t, name: str, shape, dtypes, device) -> None:
+    """The library derives every extent from the leading tensor's shape and
+    receives raw pointers, so a smaller or differently typed buffer would be
+    read or written out of bounds: check shape, dtype and device here, before
+    any call."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} must have shape {tuple(int(x) for x in shape)}, got {tuple(t.shape)}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} must have dtype {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+_F32 = (torch.float32,)
+_BF16 = (torch.bfloat16,)
+_FLOAT = (torch.bfloat16, torch.float32)
+
+
 def ulysses_abi_version() -> int:
     return int(load_library().ulysses_abi_version())
 
@@ -143,10 +163,9 @@ def ulysses_repack_seq2head(src: torch.Tensor, out: torch.Tensor | None = None) 
     P, B, nl, H, D = src.shape
     if H % P != 0 or H < P:
         _check(ERR_INVALID_ARG, "ulysses_repack_seq2head")
+    _expect(out, "out", (P, B, P * nl, H // P, D), (src.dtype,), src.device)
     if out is None:
         out = torch.empty((P, B, P * nl, H // P, D), dtype=src.dtype, device=src.device)
-    elif tuple(out.shape) != (P, B, P * nl, H // P, D) or out.dtype != src.dtype:
-        raise ValueError("out has the wrong shape or dtype")
     _check(lib.ulysses_repack_seq2head(_ptr(src), _ptr(out), P, B, nl, H, D, _dtype_code(src), _stream(src.device)),
            "ulysses_repack_seq2head")
     return out
@@ -160,10 +179,9 @@ def ulysses_repack_head2seq(src: torch.Tensor, out: torch.Tensor | None = None) 
     if n % P != 0:
         _check(ERR_INVALID_ARG, "ulysses_repack_head2seq")
     nl, H = n // P, hp * P
+    _expect(out, "out", (P, B, nl, H, D), (src.dtype,), src.device)
     if out is None:
         out = torch.empty((P, B, nl, H, D), dtype=src.dtype, device=src.device)
-    elif tuple(out.shape) != (P, B, nl, H, D) or out.dtype != src.dtype:
-        raise ValueError("out has the wrong shape or dtype")
     _check(lib.ulysses_repack_head2seq(_ptr(src), _ptr(out), P, B, nl, H, D, _dtype_code(src), _stream(src.device)),
            "ulysses_repack_head2seq")
     return out
@@ -178,10 +196,16 @@ def ulysses_attn_fwd_block(q, k, v, o, lse, causal_offset: int, key_valid=None, 
     when ``accumulate``.  Returns ``(o, lse)``."""
     lib = load_library()
     _need_contig_cuda(q, k, v, o, lse, key_valid)
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be [B][n][H][D]")
     B, nq, Hq, D = q.shape
     nk, Hkv = k.shape[1], k.shape[2]
-    if o.dtype != torch.float32 or lse.dtype != torch.float32:
-        raise ValueError("o and lse must be float32")
+    dev = q.device
+    _expect(k, "k", (B, nk, Hkv, D), (q.dtype,), dev)
+    _expect(v, "v", (B, nk, Hkv, D), (q.dtype,), dev)
+    _expect(key_valid, "key_valid", (B, nk), (torch.uint8,), dev)
+    _expect(o, "o", (B, nq, Hq, D), _F32, dev)
+    _expect(lse, "lse", (B, Hq, nq), _F32, dev)
     scale = D ** -0.5 if softmax_scale is None else float(softmax_scale)
     _check(lib.ulysses_attn_fwd_block(_ptr(q), _ptr(k), _ptr(v), _ptr(key_valid), _ptr(o), _ptr(lse), B, nq, nk,
                                       Hq, Hkv, D, scale, int(causal_offset), int(bool(causal)),
@@ -201,6 +225,10 @@ def ulysses_qkv_proj_seq2head(x: torch.Tensor, w: torch.Tensor, Hq: int, Hkv: in
     if Hq % P or Hkv % P:
         _check(ERR_INVALID_ARG, "ulysses_qkv_proj_seq2head")
     dev = x.device
+    _expect(w, "w", w.shape, _BF16, dev)
+    _expect(q, "q", (P, B, P * nl, Hq // P, D), _BF16, dev)
+    _expect(k, "k", (P, B, P * nl, Hkv // P, D), _BF16, dev)
+    _expect(v, "v", (P, B, P * nl, Hkv // P, D), _BF16, dev)
     q = torch.empty((P, B, P * nl, Hq // P, D), dtype=torch.bfloat16, device=dev) if q is None else q
     k = torch.empty((P, B, P * nl, Hkv // P, D), dtype=torch.bfloat16, device=dev) if k is None else k
     v = torch.empty((P, B, P * nl, Hkv // P, D), dtype=torch.bfloat16, device=dev) if v is None else v
@@ -220,6 +248,8 @@ def ulysses_head2seq_out_proj(o: torch.Tensor, w_o: torch.Tensor, y=None):
     hidden = w_o.shape[0]
     if tuple(w_o.shape) != (hidden, Hq * D) or o.dtype != torch.bfloat16 or w_o.dtype != torch.bfloat16 or n % P:
         raise ValueError("o and w_o must be bf16 with w_o [hidden][Hq D] and n divisible by P")
+    _expect(w_o, "w_o", w_o.shape, _BF16, o.device)
+    _expect(y, "y", (P, B, n // P, hidden), _BF16, o.device)
     y = torch.empty((P, B, n // P, hidden), dtype=torch.bfloat16, device=o.device) if y is None else y
     _check(lib.ulysses_head2seq_out_proj(_ptr(o), _ptr(w_o), _ptr(y), P, B, n // P, Hq, D, hidden, _stream(o.device)),
            "ulysses_head2seq_out_proj")
@@ -235,10 +265,9 @@ def ulysses_repack_seq2head_rope(src: torch.Tensor, rope_base: float, rope_scale
     P, B, nl, H, D = src.shape
     if H % P != 0 or H < P:
         _check(ERR_INVALID_ARG, "ulysses_repack_seq2head_rope")
+    _expect(out, "out", (P, B, P * nl, H // P, D), (src.dtype,), src.device)
     if out is None:
         out = torch.empty((P, B, P * nl, H // P, D), dtype=src.dtype, device=src.device)
-    elif tuple(out.shape) != (P, B, P * nl, H // P, D) or out.dtype != src.dtype:
-        raise ValueError("out has the wrong shape or dtype")
     _check(lib.ulysses_repack_seq2head_rope(_ptr(src), _ptr(out), P, B, nl, H, D, float(rope_base), float(rope_scale),
                                             _dtype_code(src), _stream(src.device)),
            "ulysses_repack_seq2head_rope")
@@ -259,6 +288,9 @@ def ulysses_loss_aggregate(token_loss: torch.Tensor, valid: torch.Tensor | None 
     P = token_loss.shape[0]
     per_rank = token_loss.numel() // P if P else 0
     dev = token_loss.device
+    _expect(rank_sum, "rank_sum", (P,), (torch.float64,), dev)
+    _expect(rank_count, "rank_count", (P,), (torch.int64,), dev)
+    _expect(loss, "loss", (1,), _F32, dev)
     rank_sum = torch.empty(P, dtype=torch.float64, device=dev) if rank_sum is None else rank_sum
     rank_count = torch.empty(P, dtype=torch.int64, device=dev) if rank_count is None else rank_count
     loss = torch.empty(1, dtype=torch.float32, device=dev) if loss is None else loss
@@ -294,15 +326,22 @@ def ulysses_attn_fwd_docs(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, doc
 def _attn_fwd(q, k, v, key_valid, doc_start, softmax_scale, causal, o_dtype, out, lse):
     lib = load_library()
     _need_contig_cuda(q, k, v, key_valid, doc_start, out, lse)
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be [B][n][H][D]")
     B, n, Hq, D = q.shape
     Hkv = k.shape[2]
-    if k.shape != v.shape or k.dtype != q.dtype or v.dtype != q.dtype or k.shape[0] != B or k.shape[1] != n:
-        raise ValueError("k, v must be [B][n][Hkv][D] with q's dtype")
-    if key_valid is not None and (key_valid.dtype != torch.uint8 or tuple(key_valid.shape) != (B, n)):
-        raise ValueError("key_valid must be uint8 [B][n]")
+    dev = q.device
+    _expect(q, "q", q.shape, _FLOAT, dev)
+    _expect(k, "k", (B, n, Hkv, D), (q.dtype,), dev)
+    _expect(v, "v", (B, n, Hkv, D), (q.dtype,), dev)
+    _expect(key_valid, "key_valid", (B, n), (torch.uint8,), dev)
     _check_docs(doc_start, B, n)
+    _expect(doc_start, "doc_start", (B, n), (torch.int32,), dev)
     scale = D ** -0.5 if softmax_scale is None else float(softmax_scale)
-    o_dtype = q.dtype if o_dtype is None else o_dtype
+    if o_dtype is None:
+        o_dtype = q.dtype if out is None else out.dtype
+    _expect(out, "out", (B, n, Hq, D), (o_dtype,), dev)
+    _expect(lse, "lse", (B, Hq, n), _F32, dev)
     if out is None:
         out = torch.empty((B, n, Hq, D), dtype=o_dtype, device=q.device)
     if lse is None:
@@ -338,11 +377,26 @@ def ulysses_attn_bwd_docs(q, k, v, o, lse, dout, doc_start, key_valid=None, soft
 def _attn_bwd(q, k, v, o, lse, dout, key_valid, doc_start, softmax_scale, causal, dq, dk, dv, workspace):
     lib = load_library()
     _need_contig_cuda(q, k, v, o, lse, dout, key_valid, doc_start, dq, dk, dv, workspace)
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be [B][n][H][D]")
     B, n, Hq, D = q.shape
     _check_docs(doc_start, B, n)
     Hkv = k.shape[2]
     scale = D ** -0.5 if softmax_scale is None else float(softmax_scale)
     dev = q.device
+    _expect(q, "q", q.shape, _FLOAT, dev)
+    _expect(k, "k", (B, n, Hkv, D), (q.dtype,), dev)
+    _expect(v, "v", (B, n, Hkv, D), (q.dtype,), dev)
+    _expect(o, "o", (B, n, Hq, D), _FLOAT, dev)
+    _expect(lse, "lse", (B, Hq, n), _F32, dev)
+    _expect(dout, "dout", (B, n, Hq, D), (q.dtype,), dev)
+    _expect(key_valid, "key_valid", (B, n), (torch.uint8,), dev)
+    _expect(doc_start, "doc_start", (B, n), (torch.int32,), dev)
+    _expect(dq, "dq", (B, n, Hq, D), _F32, dev)
+    _expect(dk, "dk", (B, n, Hkv, D), _F32, dev)
+    _expect(dv, "dv", (B, n, Hkv, D), _F32, dev)
+    if workspace is not None and workspace.device != dev:
+        raise ValueError(f"workspace is on {workspace.device}, expected {dev}")
     dq = torch.empty((B, n, Hq, D), dtype=torch.float32, device=dev) if dq is None else dq
     dk = torch.empty((B, n, Hkv, D), dtype=torch.float32, device=dev) if dk is None else dk
     dv = torch.empty((B, n, Hkv, D), dtype=torch.float32, device=dev) if dv is None else dv

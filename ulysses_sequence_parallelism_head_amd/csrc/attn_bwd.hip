@@ -542,10 +542,11 @@ __device__ __forceinline__ void dq_issue(uint8_t* stage, uint32_t& vbyte, const 
 // inside n).  With HAS_MASK the score accumulators start from the keys'
 // bias staged at vb (0, or -inf for a padding key), so the product applies
 // the key mask itself.  SPLIT adds the bf16 residual of dS as second MFMAs.
-template <int D, bool HAS_MASK, bool SPLIT, bool DOCS, bool MASKED>
+template <int D, bool HAS_MASK, bool SPLIT, bool DOCS, bool MASKED, bool DLPASS>
 __device__ __forceinline__ void dq_half(const uint8_t* ks, const uint8_t* vs, const uint8_t* vb, int half, int lim,
                                         int lo, const u32x4 (&qf)[D / 16], const u32x4 (&df)[D / 16], float lse2,
-                                        float dl, float c, int l32, int hh, int lane, f32x16 (&dqa)[D / 32]) {
+                                        float dl, float c, int l32, int hh, int lane, f32x16 (&dqa)[D / 32],
+                                        float& dlacc) {
   using L = DqLayout<D>;
   constexpr int KK = D / 16;
   constexpr int DJ = D / 32;
@@ -567,6 +568,21 @@ __device__ __forceinline__ void dq_half(const uint8_t* ks, const uint8_t* vs, co
     dp = mfma32x32x16(*reinterpret_cast<const u32x4*>(vs + off), df[kk], dp);
   }
   pipeline_reads_mfma<6, 2 * KK>();   // three k-steps of K/V rows in flight
+  if constexpr (DLPASS) {
+    // Dl = sum over the visible keys of P dP, in float32 from the scores
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = g4 * 4 + e;
+        const int ci = g4 * 8 + e;
+        const bool ok = !MASKED || (ci <= lim && (!DOCS || ci >= lo));
+        const float x = ok ? fmaf(s[i], c, -lse2) : -INFINITY;
+        dlacc = fmaf(__builtin_amdgcn_exp2f(x), dp[i], dlacc);
+      }
+    }
+    return;
+  }
   float ds[16];
   // element i is key row C_i = (i/4)*8 + i%4 of the half (plus 4hh)
 #pragma unroll
@@ -661,22 +677,20 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const BwdParams p) {
     }
   }
 
-  // rows with fewer than kSplitRows visible keys take the hi/lo path; the
+  // Rows with fewer than kSplitRows visible keys take the hi/lo path; the
   // choice is made once per workgroup so the common path carries no
-  // residuals.  Every row sees at least (first row) - (last row's bound) keys.
+  // residuals.  Every row sees at least (first row) - (last row's bound)
+  // keys.  Those rows also get their Dl recomputed from the scores, in a
+  // first sweep over the same tiles: Dl = sum_u P dP = dO . (sum_u P v_u) is
+  // dO . O with O exact, where the O handed in may carry bf16 storage
+  // rounding, which on rows with few keys (|O| near the size of a V row)
+  // moves dQ and dK by up to ~1e-2.  The value is written back to the
+  // workspace for the dK/dV pass, which runs after this kernel.
   auto run = [&](auto split_tag) {
     constexpr bool SPLIT = decltype(split_tag)::value;
     f32x16 dqa[DJ];
 #pragma unroll
     for (int j = 0; j < DJ; ++j) dqa[j] = f32x16{};
-
-    // step j works on tile it_first + j, staged in buffer j & 1 (the LDS
-    // addresses depend on the step counter only)
-    uint32_t vbyte = 0;
-    dq_issue<D, HAS_MASK>(smem, vbyte, p, b, kvh, it_first, wave, lane, tid);
-    if (HAS_MASK && tid < L::kBN) reinterpret_cast<float*>(smem + L::kOffValid)[tid] = vbyte ? 0.f : -INFINITY;
-    wait_vmem();
-    __syncthreads();
 
     // Tiles that need the index masks: the causal diagonal (tiles reaching
     // past the workgroup's first row) and the tail past n, the last ones.
@@ -688,40 +702,61 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const BwdParams p) {
     int mask_from = CAUSAL ? max(first_row - L::kBN + 1, 0) : p.n - L::kBN + 1;   // first key0 of a masked tile
     mask_from = min(mask_from, p.n - L::kBN + 1);
     const int j_hi = DOCS ? 0 : min(max((mask_from + L::kBN - 1) / L::kBN - it_first, 0), nsteps);   // steps >= j_hi masked
-    auto steps = [&](int j0, int j1, auto masked_tag) __attribute__((always_inline)) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    for (int j = j0; j < j1; ++j) {
-      const int it = it_first + j;
-      // prefetch tile it+1 into the other buffer while computing on this one
-      uint8_t* cur = smem + (j & 1) * L::kStageAligned;
-      uint8_t* nxt = smem + ((j + 1) & 1) * L::kStageAligned;
-      if (it + 1 < ntiles) dq_issue<D, HAS_MASK>(nxt, vbyte, p, b, kvh, it + 1, wave, lane, tid);
-      const int tile0 = it * L::kBN;
-      if (wave_live && !(CAUSAL && tile0 > wave_last) && !(DOCS && tile0 + L::kBN <= lo_wave)) {
-        const uint8_t* ks = cur + L::kOffK;
-        const uint8_t* vs = cur + L::kOffV;
-        const uint8_t* vb = cur + L::kOffValid;
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int key0 = tile0 + half * 32;
-          if (CAUSAL && key0 > wave_last) break;
-          // visible iff key < n, and key <= t if causal
-          int lim = p.n - 1 - key0 - 4 * hh;
-          if (CAUSAL) lim = min(lim, t - key0 - 4 * hh);
-          // documents: key >= the row's bound (no-op above the last row's bound)
-          const int lo = (DOCS && tile0 < lo_last) ? lo_row - key0 - 4 * hh : -0x7fffffff;
-          dq_half<D, HAS_MASK, SPLIT, DOCS, MASKED>(ks, vs, vb, half, lim, lo, qf, df, lse2, dl, p.c, l32, hh, lane,
-                                                    dqa);
-        }
-      }
-      if (HAS_MASK && it + 1 < ntiles && tid < L::kBN)
-        reinterpret_cast<float*>(nxt + L::kOffValid)[tid] = vbyte ? 0.f : -INFINITY;
+
+    // one sweep over the tiles: the dQ products, or (DLPASS) only the row sums of P dP
+    auto sweep = [&](auto dlpass_tag) __attribute__((always_inline)) {
+      constexpr bool DLPASS = decltype(dlpass_tag)::value;
+      float dlacc = 0.f;
+      // step j works on tile it_first + j, staged in buffer j & 1 (the LDS
+      // addresses depend on the step counter only)
+      uint32_t vbyte = 0;
+      dq_issue<D, HAS_MASK>(smem, vbyte, p, b, kvh, it_first, wave, lane, tid);
+      if (HAS_MASK && tid < L::kBN) reinterpret_cast<float*>(smem + L::kOffValid)[tid] = vbyte ? 0.f : -INFINITY;
       wait_vmem();
       __syncthreads();
-    }
+      auto steps = [&](int j0, int j1, auto masked_tag) __attribute__((always_inline)) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
+        for (int j = j0; j < j1; ++j) {
+          const int it = it_first + j;
+          // prefetch tile it+1 into the other buffer while computing on this one
+          uint8_t* cur = smem + (j & 1) * L::kStageAligned;
+          uint8_t* nxt = smem + ((j + 1) & 1) * L::kStageAligned;
+          if (it + 1 < ntiles) dq_issue<D, HAS_MASK>(nxt, vbyte, p, b, kvh, it + 1, wave, lane, tid);
+          const int tile0 = it * L::kBN;
+          if (wave_live && !(CAUSAL && tile0 > wave_last) && !(DOCS && tile0 + L::kBN <= lo_wave)) {
+            const uint8_t* ks = cur + L::kOffK;
+            const uint8_t* vs = cur + L::kOffV;
+            const uint8_t* vb = cur + L::kOffValid;
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+              const int key0 = tile0 + half * 32;
+              if (CAUSAL && key0 > wave_last) break;
+              // visible iff key < n, and key <= t if causal
+              int lim = p.n - 1 - key0 - 4 * hh;
+              if (CAUSAL) lim = min(lim, t - key0 - 4 * hh);
+              // documents: key >= the row's bound (no-op above the last row's bound)
+              const int lo = (DOCS && tile0 < lo_last) ? lo_row - key0 - 4 * hh : -0x7fffffff;
+              dq_half<D, HAS_MASK, SPLIT, DOCS, MASKED, DLPASS>(ks, vs, vb, half, lim, lo, qf, df, lse2, dl, p.c, l32,
+                                                                hh, lane, dqa, dlacc);
+            }
+          }
+          if (HAS_MASK && it + 1 < ntiles && tid < L::kBN)
+            reinterpret_cast<float*>(nxt + L::kOffValid)[tid] = vbyte ? 0.f : -INFINITY;
+          wait_vmem();
+          __syncthreads();
+        }
+      };
+      if (!DOCS) steps(0, j_hi, std::false_type{});
+      steps(j_hi, nsteps, std::true_type{});
+      return dlacc;
     };
-    if (!DOCS) steps(0, j_hi, std::false_type{});
-    steps(j_hi, nsteps, std::true_type{});
+
+    if constexpr (SPLIT) {
+      // the two half-waves hold complementary keys of the same row
+      dl = halves_sum(sweep(std::true_type{}));
+      if (t < p.n && hh == 0) p.rowdot[(int64_t(b) * p.Hq + head) * p.n + t] = dl;
+    }
+    sweep(std::false_type{});
 
     if (t < p.n) {
       const int64_t base = ((int64_t(b) * p.n + t) * p.Hq + head) * D;
@@ -736,16 +771,19 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const BwdParams p) {
         }
     }
   };
-  if (pb * p.pw - lo_last < kSplitRows) run(std::true_type{});
+  // non-causal rows see all n positions
+  const bool few_keys = CAUSAL ? (pb * p.pw - lo_last < kSplitRows) : (p.n < kSplitRows);
+  if (few_keys) run(std::true_type{});
   else run(std::false_type{});
 }
 
 template <int D, bool HAS_MASK, bool CAUSAL, bool DOCS>
 hipError_t launch_grads(const BwdParams& p, int64_t kv_blocks, int64_t q_blocks, hipStream_t stream) {
-  hipLaunchKernelGGL((dkdv_kernel<D, HAS_MASK, CAUSAL, DOCS>), dim3(kv_blocks), dim3(kThreads), 0, stream, p);
+  // dq first: it rewrites Dl of the rows with few visible keys, which dkdv reads
+  hipLaunchKernelGGL((dq_kernel<D, HAS_MASK, CAUSAL, DOCS>), dim3(q_blocks), dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((dq_kernel<D, HAS_MASK, CAUSAL, DOCS>), dim3(q_blocks), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((dkdv_kernel<D, HAS_MASK, CAUSAL, DOCS>), dim3(kv_blocks), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
