@@ -47,8 +47,11 @@
  *    arguments may then be NULL.
  *  - Kernel faults, if any, surface at the caller's next synchronisation of
  *    `stream` as HIP errors; ULYSSES_ERR_HIP reports a failed launch.
- *  - The library holds no mutable global state: calls are thread-safe and
- *    may be issued concurrently on different streams.
+ *  - The library holds no mutable global state apart from a per-device
+ *    cache of one device address (ulysses_attn_bwd_noalloc's scratch,
+ *    filled under a lock): calls are thread-safe and may be issued
+ *    concurrently on different streams, except ulysses_attn_bwd_noalloc
+ *    calls that overlap on one GPU (they share its scratch).
  */
 #ifndef ULYSSES_H_
 #define ULYSSES_H_
@@ -70,7 +73,8 @@ typedef enum {
   ULYSSES_OK = 0,
   ULYSSES_ERR_INVALID_ARG = 1,  /* a null pointer, a bad size, a violated constraint, misalignment, aliasing */
   ULYSSES_ERR_UNSUPPORTED = 2,  /* valid in principle, not built: head dim, dtype combination, size limits */
-  ULYSSES_ERR_HIP = 3           /* a HIP launch failed */
+  ULYSSES_ERR_HIP = 3,          /* a HIP launch failed */
+  ULYSSES_ERR_SCRATCH_LIMIT = 4 /* too large for ulysses_attn_bwd_noalloc's fixed scratch */
 } ulysses_status_t;
 
 typedef enum {
@@ -217,6 +221,36 @@ ULYSSES_API ulysses_status_t ulysses_attn_bwd(const void* q, const void* k, cons
                                   float softmax_scale, int32_t causal,
                                   ulysses_dtype_t in_dtype, ulysses_dtype_t o_dtype,
                                   void* stream);
+
+/*
+ * ulysses_attn_bwd_noalloc -- ulysses_attn_bwd for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving or
+ * training loops, harnesses that forbid hipMalloc): the same computation
+ * and kernels, with the workspace taken from a fixed scratch array that
+ * the library's code object holds on each GPU it runs on (16 MiB, kept
+ * until the process ends).  The call itself allocates nothing and frees
+ * nothing; the caller passes every input and output as for
+ * ulysses_attn_bwd.
+ *
+ * Limit: 2 * B * Hq * n * 4 bytes <= 16 MiB, i.e. B * Hq * n <= 2^21 rows
+ * (the 64K workload's 8 query heads use 2^19).  Larger problems return
+ * ULYSSES_ERR_SCRATCH_LIMIT before anything is launched.
+ * Every call on a GPU uses that GPU's one scratch array, and nothing in it
+ * needs to start at zero (each call writes every value before reading
+ * it): calls that overlap in time on one GPU -- on different streams, or
+ * from different threads -- race on it and must be serialised by the
+ * caller.  The first call on a device looks the array's address up
+ * (hipGetSymbolAddress) and keeps it; ULYSSES_ERR_HIP if that fails.
+ * Arguments, built combinations and other errors: as ulysses_attn_bwd.
+ */
+ULYSSES_API ulysses_status_t ulysses_attn_bwd_noalloc(const void* q, const void* k, const void* v,
+                                          const uint8_t* key_valid,
+                                          const void* o, const float* lse, const void* dout,
+                                          float* dq, float* dk, float* dv,
+                                          int32_t B, int64_t n, int32_t Hq, int32_t Hkv, int32_t D,
+                                          float softmax_scale, int32_t causal,
+                                          ulysses_dtype_t in_dtype, ulysses_dtype_t o_dtype,
+                                          void* stream);
 
 /*
  * ulysses_attn_fwd_docs -- ulysses_attn_fwd over a packed sequence of

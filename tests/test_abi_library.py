@@ -207,3 +207,29 @@ def test_proj_validation(lib):
     assert g(FAKE, W, Y, 4, 1, 16, 30, 128, 4096, None) == INVALID                # Hq % P
     assert g(FAKE, W, Y, 4, 1, 16, 32, 128, 4098, None) == UNSUPPORTED           # hidden % 4
     assert g(FAKE, W, ctypes.c_void_p(0x10000 + 16), 4, 1, 16, 32, 128, 4096, None) == INVALID   # y overlaps o
+
+
+def _bwd_noalloc(lib, B=1, n=64, Hq=8, dq=None, it=BF16, D=128):
+    # buffers 2^36 bytes apart, so that even the largest sizes below do not overlap
+    a = [ctypes.c_void_p((i + 1) << 36) for i in range(10)]
+    if dq is not None:
+        a[7] = dq
+    return lib.ulysses_attn_bwd_noalloc(a[0], a[1], a[2], None, a[4], a[5], a[6], a[7], a[8], a[9],
+                                        B, n, Hq, 2, D, 0.1, 1, it, BF16, None)
+
+
+def test_bwd_noalloc_validation(lib):
+    """The no-allocation backward: its size limit (2 * B * Hq * n * 4 bytes
+    <= 16 MiB) is checked before anything touches a device, after the
+    ordinary argument checks."""
+    SCRATCH_LIMIT = 4
+    assert b"scratch" in lib.ulysses_status_string(SCRATCH_LIMIT)
+    assert _bwd_noalloc(lib, n=(1 << 21) // 8 + 1) == SCRATCH_LIMIT      # B*Hq*n just above 2^21
+    assert _bwd_noalloc(lib, B=2, n=1 << 20, Hq=2) == SCRATCH_LIMIT
+    assert _bwd_noalloc(lib, Hq=7) == INVALID                             # Hq % Hkv
+    assert _bwd_noalloc(lib, D=80) == UNSUPPORTED
+    assert _bwd_noalloc(lib, n=-1) == INVALID
+    assert _bwd_noalloc(lib, B=0) == OK                                   # empty: nothing to do, no device use
+    assert _bwd_noalloc(lib, dq=ctypes.c_void_p(0)) == INVALID             # null dq
+    assert _bwd_noalloc(lib, dq=ctypes.c_void_p((7 << 36) + 64)) == INVALID  # dq overlaps dout
+    assert _bwd_noalloc(lib, it=F32) == UNSUPPORTED

@@ -5,8 +5,8 @@ Argument marshalling only: every step runs in the library's HIP kernels.
 PyTorch supplies device memory and the current stream; outputs not passed
 in are allocated here with ``torch.empty``.  The functions carry the C
 names and follow ``include/ulysses.h``; status codes become exceptions:
-INVALID_ARG -> ValueError, UNSUPPORTED -> NotImplementedError,
-HIP -> RuntimeError.
+INVALID_ARG and SCRATCH_LIMIT -> ValueError, UNSUPPORTED ->
+NotImplementedError, HIP -> RuntimeError.
 
 There is no fallback: if ``libulysses.so`` is missing, importing the library
 raises ``ImportError`` (build it with ``python -m
@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(_HERE, "libulysses.so")
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
 
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_SCRATCH_LIMIT = 0, 1, 2, 3, 4
 
 _lib = None
 
@@ -55,6 +55,11 @@ _SIGS = {
                                         ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                         ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_int, ctypes.c_int,
                                         ctypes.c_void_p]),
+    "ulysses_attn_bwd_noalloc": (ctypes.c_int, [ctypes.c_void_p] * 10 + [ctypes.c_int32, ctypes.c_int64,
+                                                                          ctypes.c_int32, ctypes.c_int32,
+                                                                          ctypes.c_int32, ctypes.c_float,
+                                                                          ctypes.c_int32, ctypes.c_int, ctypes.c_int,
+                                                                          ctypes.c_void_p]),
     "ulysses_attn_bwd_docs": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -103,7 +108,7 @@ def _check(status: int, what: str) -> None:
     if status == OK:
         return
     msg = f"{what}: {load_library().ulysses_status_string(status).decode()}"
-    if status == ERR_INVALID_ARG:
+    if status in (ERR_INVALID_ARG, ERR_SCRATCH_LIMIT):
         raise ValueError(msg)
     if status == ERR_UNSUPPORTED:
         raise NotImplementedError(msg)
@@ -374,7 +379,19 @@ def ulysses_attn_bwd_docs(q, k, v, o, lse, dout, doc_start, key_valid=None, soft
     return _attn_bwd(q, k, v, o, lse, dout, key_valid, doc_start, softmax_scale, True, dq, dk, dv, workspace)
 
 
-def _attn_bwd(q, k, v, o, lse, dout, key_valid, doc_start, softmax_scale, causal, dq, dk, dv, workspace):
+def ulysses_attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, key_valid=None, softmax_scale=None, causal=True):
+    """:func:`ulysses_attn_bwd` without a workspace and without any
+    allocation: the caller passes the float32 outputs ``dq``, ``dk``, ``dv``;
+    the library uses its fixed per-GPU scratch (B * Hq * n <= 2^21).  Calls
+    that overlap on one GPU race on that scratch."""
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t is None:
+            raise ValueError(f"{name} is required: this call allocates nothing")
+    return _attn_bwd(q, k, v, o, lse, dout, key_valid, None, softmax_scale, causal, dq, dk, dv, None, noalloc=True)
+
+
+def _attn_bwd(q, k, v, o, lse, dout, key_valid, doc_start, softmax_scale, causal, dq, dk, dv, workspace,
+              noalloc=False):
     lib = load_library()
     _need_contig_cuda(q, k, v, o, lse, dout, key_valid, doc_start, dq, dk, dv, workspace)
     if q.dim() != 4 or k.dim() != 4:
@@ -397,6 +414,12 @@ def _attn_bwd(q, k, v, o, lse, dout, key_valid, doc_start, softmax_scale, causal
     _expect(dv, "dv", (B, n, Hkv, D), _F32, dev)
     if workspace is not None and workspace.device != dev:
         raise ValueError(f"workspace is on {workspace.device}, expected {dev}")
+    if noalloc:
+        _check(lib.ulysses_attn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(key_valid), _ptr(o), _ptr(lse),
+                                            _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), B, n, Hq, Hkv, D, scale,
+                                            int(bool(causal)), _dtype_code(q), _dtype_code(o), _stream(dev)),
+               "ulysses_attn_bwd_noalloc")
+        return dq, dk, dv
     dq = torch.empty((B, n, Hq, D), dtype=torch.float32, device=dev) if dq is None else dq
     dk = torch.empty((B, n, Hkv, D), dtype=torch.float32, device=dev) if dk is None else dk
     dv = torch.empty((B, n, Hkv, D), dtype=torch.float32, device=dev) if dv is None else dv
@@ -421,6 +444,6 @@ def _attn_bwd(q, k, v, o, lse, dout, key_valid, doc_start, softmax_scale, causal
 __all__ = [
     "load_library", "EXPORTED", "LIB_PATH", "ulysses_abi_version", "ulysses_repack_seq2head",
     "ulysses_repack_head2seq", "ulysses_attn_fwd", "ulysses_attn_bwd", "ulysses_attn_bwd_workspace_bytes",
-    "ulysses_attn_fwd_docs", "ulysses_attn_bwd_docs", "ulysses_repack_seq2head_rope", "ulysses_loss_aggregate",
+    "ulysses_attn_fwd_docs", "ulysses_attn_bwd_docs", "ulysses_attn_bwd_noalloc", "ulysses_repack_seq2head_rope", "ulysses_loss_aggregate",
     "ulysses_attn_fwd_block", "ulysses_qkv_proj_seq2head", "ulysses_head2seq_out_proj",
 ]

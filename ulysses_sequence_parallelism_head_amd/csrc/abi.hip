@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/ulysses.h"
 #include "internal.h"
 
@@ -98,31 +100,33 @@ ulysses_status_t attn_fwd(const void* q, const void* k, const void* v, const uin
                                                static_cast<float*>(o), lse, s, hs));
 }
 
-// Backward with an optional per-row document bound (doc_start, causal only).
-ulysses_status_t attn_bwd(const void* q, const void* k, const void* v, const uint8_t* key_valid,
-                          const int32_t* doc_start, const void* o, const float* lse, const void* dout, float* dq,
-                          float* dk, float* dv, void* workspace, size_t workspace_bytes, int32_t B, int64_t n,
-                          int32_t Hq, int32_t Hkv, int32_t D, float softmax_scale, int32_t causal,
-                          ulysses_dtype_t in_dtype, ulysses_dtype_t o_dtype, void* stream) {
-  bool empty = false;
-  ulysses_status_t st = check_attn_shape(B, n, Hq, Hkv, D, softmax_scale, causal, in_dtype, o_dtype, &empty);
-  if (st != ULYSSES_OK || empty) return st;
+// Checks of the backward's arguments.  With workspace == nullptr the caller
+// supplies none (the no-allocation call, whose scratch is the library's own):
+// only the other buffers are checked.  Sets *empty for zero-sized problems.
+ulysses_status_t check_bwd(const void* q, const void* k, const void* v, const uint8_t* key_valid,
+                           const int32_t* doc_start, const void* o, const float* lse, const void* dout,
+                           const float* dq, const float* dk, const float* dv, const void* workspace,
+                           size_t workspace_bytes, bool own_workspace, int32_t B, int64_t n, int32_t Hq,
+                           int32_t Hkv, int32_t D, float softmax_scale, int32_t causal, ulysses_dtype_t in_dtype,
+                           ulysses_dtype_t o_dtype, bool* empty) {
+  ulysses_status_t st = check_attn_shape(B, n, Hq, Hkv, D, softmax_scale, causal, in_dtype, o_dtype, empty);
+  if (st != ULYSSES_OK || *empty) return st;
   if (in_dtype != ULYSSES_DTYPE_BF16) return ULYSSES_ERR_UNSUPPORTED;
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || lse == nullptr || dout == nullptr ||
-      dq == nullptr || dk == nullptr || dv == nullptr || workspace == nullptr)
+      dq == nullptr || dk == nullptr || dv == nullptr || (own_workspace && workspace == nullptr))
     return ULYSSES_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
       !aligned(lse, 4) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(workspace, 256) ||
       !aligned(doc_start, 4))
     return ULYSSES_ERR_INVALID_ARG;
   const size_t need = ulysses::attn_bwd_workspace_bytes(B, n, Hq);
-  if (workspace_bytes < need) return ULYSSES_ERR_INVALID_ARG;
+  if (own_workspace && workspace_bytes < need) return ULYSSES_ERR_INVALID_ARG;
   const uint64_t nq = uint64_t(B) * n * Hq * D, nkv = uint64_t(B) * n * Hkv * D;
   const void* ins[8] = {q, k, v, key_valid, o, lse, dout, doc_start};
   const uint64_t inb[8] = {nq * 2, nkv * 2, nkv * 2, key_valid ? uint64_t(B) * n : 0,
                            nq * elem_size(o_dtype), uint64_t(B) * Hq * n * 4, nq * 2,
                            doc_start ? uint64_t(B) * n * 4 : 0};
-  const void* outs[4] = {dq, dk, dv, workspace};
+  const void* outs[4] = {dq, dk, dv, own_workspace ? workspace : nullptr};
   const uint64_t outb[4] = {nq * 4, nkv * 4, nkv * 4, need};
   for (int a = 0; a < 4; ++a) {
     for (int i = 0; i < 8; ++i)
@@ -130,10 +134,58 @@ ulysses_status_t attn_bwd(const void* q, const void* k, const void* v, const uin
     for (int c = a + 1; c < 4; ++c)
       if (overlap(outs[a], outb[a], outs[c], outb[c])) return ULYSSES_ERR_INVALID_ARG;
   }
+  return ULYSSES_OK;
+}
+
+// Backward with an optional per-row document bound (doc_start, causal only).
+ulysses_status_t attn_bwd(const void* q, const void* k, const void* v, const uint8_t* key_valid,
+                          const int32_t* doc_start, const void* o, const float* lse, const void* dout, float* dq,
+                          float* dk, float* dv, void* workspace, size_t workspace_bytes, int32_t B, int64_t n,
+                          int32_t Hq, int32_t Hkv, int32_t D, float softmax_scale, int32_t causal,
+                          ulysses_dtype_t in_dtype, ulysses_dtype_t o_dtype, void* stream) {
+  bool empty = false;
+  ulysses_status_t st = check_bwd(q, k, v, key_valid, doc_start, o, lse, dout, dq, dk, dv, workspace,
+                                  workspace_bytes, true, B, n, Hq, Hkv, D, softmax_scale, causal, in_dtype, o_dtype,
+                                  &empty);
+  if (st != ULYSSES_OK || empty) return st;
   AttnShape s{B, n, Hq, Hkv, D, softmax_scale, causal};
   return from_hip(ulysses::launch_attn_bwd_bf16(q, k, v, key_valid, doc_start, o, lse, dout, dq, dk, dv,
                                                 static_cast<float*>(workspace), s, o_dtype == ULYSSES_DTYPE_F32,
                                                 static_cast<hipStream_t>(stream)));
+}
+
+// ---- the no-allocation backward
+//
+// Its scratch (the two float32 [B][Hq][n] row arrays of the backward) is a
+// file-scope device array: the code object holds one copy on every GPU the
+// library runs on, until the process ends.  In host code `scratch` names a
+// host-side stand-in, not device memory, so host code never passes it to a
+// kernel: the device address comes from hipGetSymbolAddress, taken once per
+// device (with that device current) and kept below.
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this GPU's `scratch`, or null with *err set.
+void* scratch_on_current_device(hipError_t* err) {
+  int dev = -1;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    *err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (*err != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
 }
 
 }  // namespace
@@ -148,6 +200,8 @@ const char* ulysses_status_string(ulysses_status_t status) {
     case ULYSSES_ERR_INVALID_ARG: return "invalid argument";
     case ULYSSES_ERR_UNSUPPORTED: return "unsupported configuration";
     case ULYSSES_ERR_HIP: return "HIP launch failed";
+    case ULYSSES_ERR_SCRATCH_LIMIT:
+      return "problem exceeds the fixed scratch of the no-allocation call (2 * B * Hq * n * 4 bytes > 16 MiB)";
     default: return "unknown status";
   }
 }
@@ -193,6 +247,25 @@ ulysses_status_t ulysses_attn_bwd(const void* q, const void* k, const void* v, c
                                   ulysses_dtype_t in_dtype, ulysses_dtype_t o_dtype, void* stream) {
   return attn_bwd(q, k, v, key_valid, nullptr, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, n, Hq, Hkv,
                   D, softmax_scale, causal, in_dtype, o_dtype, stream);
+}
+
+ulysses_status_t ulysses_attn_bwd_noalloc(const void* q, const void* k, const void* v, const uint8_t* key_valid,
+                                          const void* o, const float* lse, const void* dout, float* dq, float* dk,
+                                          float* dv, int32_t B, int64_t n, int32_t Hq, int32_t Hkv, int32_t D,
+                                          float softmax_scale, int32_t causal, ulysses_dtype_t in_dtype,
+                                          ulysses_dtype_t o_dtype, void* stream) {
+  bool empty = false;
+  ulysses_status_t st = check_bwd(q, k, v, key_valid, nullptr, o, lse, dout, dq, dk, dv, nullptr, 0, false, B, n,
+                                  Hq, Hkv, D, softmax_scale, causal, in_dtype, o_dtype, &empty);
+  if (st != ULYSSES_OK || empty) return st;
+  if (ulysses::attn_bwd_workspace_bytes(B, n, Hq) > kNoAllocScratchBytes) return ULYSSES_ERR_SCRATCH_LIMIT;
+  hipError_t e = hipSuccess;
+  void* ws = scratch_on_current_device(&e);
+  if (ws == nullptr) return ULYSSES_ERR_HIP;
+  AttnShape s{B, n, Hq, Hkv, D, softmax_scale, causal};
+  return from_hip(ulysses::launch_attn_bwd_bf16(q, k, v, key_valid, nullptr, o, lse, dout, dq, dk, dv,
+                                                static_cast<float*>(ws), s, o_dtype == ULYSSES_DTYPE_F32,
+                                                static_cast<hipStream_t>(stream)));
 }
 
 ulysses_status_t ulysses_attn_bwd_docs(const void* q, const void* k, const void* v, const uint8_t* key_valid,
