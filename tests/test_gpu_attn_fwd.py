@@ -151,6 +151,27 @@ def test_fwd_64k_workload_sampled():
     assert np.array_equal(l16, l32)
 
 
+@pytest.mark.parametrize("masked", [False, True])
+def test_fwd_wide_workgroups_ragged(masked):
+    """A causal run long enough for the 8-wave workgroups (n = 16417: 514
+    of them, with a ragged last block): stratified rows and every row of
+    the last two blocks, against the oracle."""
+    n, Hq, Hkv, D = 16417, 8, 2, 128
+    say(f"fwd wide workgroups n={n} masked={masked}")
+    q, k, v, valid = _inputs(16417 + masked, n, Hq, Hkv, D, masked)
+    g = synth.streams(99)
+    rows = np.unique(np.concatenate([synth.stratified_rows(g[6], n, 24, None if valid is None else valid[0]),
+                                     np.arange(n - 100, n)]))
+    scale = D ** -0.5
+    O, L = oracle.attn_fwd(to_f64(q), to_f64(k), to_f64(v), scale, True, valid, rows=rows)
+    o32, l32 = _run(q, k, v, valid, scale, True, torch.float32)
+    assert_close("O(f32 out)", o32[:, rows], O, 1e-2)
+    assert_close("LSE", l32[:, :, rows], L, 1e-2)
+    o16, l16 = _run(q, k, v, valid, scale, True, torch.bfloat16)
+    assert_close("O(bf16 out)", o16[:, rows], O, 1e-2, bf16_out=True)
+    assert np.array_equal(l16, l32)
+
+
 def test_fwd_96k_docs_workload_sampled():
     """Workload 4 forward: n=98304 with packed documents (padding keys masked)."""
     say("fwd workload 4 (96K, documents) sampled rows")

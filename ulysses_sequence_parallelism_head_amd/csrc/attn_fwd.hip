@@ -57,13 +57,12 @@ namespace ulysses {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
 constexpr int kBN = 64;                 // keys per tile
 constexpr int kSplitRows = 512;         // rows using the hi/lo split of P
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;   // log2 units
+constexpr int kWide8Blocks = 512;       // 8-wave workgroups from this grid size on (plain causal, D = 128)
 
 template <int D>
 struct FwdLayout {
@@ -101,7 +100,7 @@ struct FwdParams {
 // tiles of `stage` (keys past n read as zero), and load the tile's key-valid
 // bytes into a register of the first 64 threads (stored by the caller once
 // the buffer is free).
-template <int D, bool HAS_MASK>
+template <int NW, int D, bool HAS_MASK>
 __device__ __forceinline__ void fwd_issue(uint8_t* stage, uint32_t& vbyte, const FwdParams& p, int b, int kvh,
                                           int tile, int wave, int lane, int tid) {
   using L = FwdLayout<D>;
@@ -109,16 +108,16 @@ __device__ __forceinline__ void fwd_issue(uint8_t* stage, uint32_t& vbyte, const
   const int rows_ok = min(kBN, p.nk - key0);
   const int64_t off = ((int64_t(b) * p.nk + key0) * p.Hkv + kvh) * D;
   const int stride = p.Hkv * D * 2;
-  dma_tile<D, kBN, kWaves>(stage, p.k + off, stride, rows_ok, wave, lane);
-  dma_tile<D, kBN, kWaves>(stage + L::kBytesK, p.v + off, stride, rows_ok, wave, lane);
+  dma_tile<D, kBN, NW>(stage, p.k + off, stride, rows_ok, wave, lane);
+  dma_tile<D, kBN, NW>(stage + L::kBytesK, p.v + off, stride, rows_ok, wave, lane);
   if (HAS_MASK && tid < kBN) {
     const int key = key0 + tid;
     vbyte = (key < p.nk) ? (p.valid[int64_t(b) * p.nk + key] != 0 ? 1u : 0u) : 0u;
   }
 }
 
-template <int D, bool HAS_MASK, bool O_F32, bool CAUSAL, bool DOCS>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const FwdParams p) {
+template <int NW, int D, bool HAS_MASK, bool O_F32, bool CAUSAL, bool DOCS>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(const FwdParams p) {
   static_assert(CAUSAL || !DOCS, "documents are causal");
   using L = FwdLayout<D>;
   constexpr int KK = D / 16;     // contraction slices of the score product
@@ -188,7 +187,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const FwdPar
     float lsum = 0.f;          // this half-wave's share of the row sum
 
     uint32_t vbyte = 0;
-    fwd_issue<D, HAS_MASK>(smem, vbyte, p, b, kvh, it_first, wave, lane, tid);
+    fwd_issue<NW, D, HAS_MASK>(smem, vbyte, p, b, kvh, it_first, wave, lane, tid);
     if (HAS_MASK && tid < kBN) reinterpret_cast<float*>(smem + L::kBytesK + L::kBytesV)[tid] = vbyte ? 0.f : -INFINITY;
     wait_vmem();
     __syncthreads();
@@ -198,7 +197,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const FwdPar
     // statically and every LDS address folds the buffer into the
     // instruction's immediate offset.
     auto tile = [&](int it, uint8_t* cur, uint8_t* nxt) {
-      if (it + 1 < ntiles) fwd_issue<D, HAS_MASK>(nxt, vbyte, p, b, kvh, it + 1, wave, lane, tid);
+      if (it + 1 < ntiles) fwd_issue<NW, D, HAS_MASK>(nxt, vbyte, p, b, kvh, it + 1, wave, lane, tid);
 
       const int tile0 = it * kBN;
       if (wave_live && !(CAUSAL && tile0 > wave_last + p.delta) && !(DOCS && tile0 + kBN <= lo_wave)) {
@@ -384,24 +383,48 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const FwdPar
   else run(std::false_type{});
 }
 
-template <int D, bool HAS_MASK, bool O_F32, bool CAUSAL, bool DOCS>
+template <int NW, int D, bool HAS_MASK, bool O_F32, bool CAUSAL, bool DOCS>
 hipError_t launch_fwd_t(const FwdParams& p, int blocks, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, HAS_MASK, O_F32, CAUSAL, DOCS>), dim3(blocks), dim3(kThreads), 0,
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<NW, D, HAS_MASK, O_F32, CAUSAL, DOCS>), dim3(blocks), dim3(NW * 64), 0,
                      stream, p);
   return hipGetLastError();
 }
 
+// Long plain causal runs use 8-wave workgroups (one per CU, two waves per
+// SIMD as with two 4-wave workgroups): each staged K/V tile then feeds 8
+// waves, which halves the DMA writes into LDS and the L2 reads per flop
+// (measured 4 % faster at n = 64K, 10 % on 128K single-head runs, identical
+// output).  Short grids keep 4-wave workgroups, whose finer granularity
+// balances the causal triangle better.
 template <int D, bool HAS_MASK, bool O_F32>
-hipError_t dispatch_causal(const FwdParams& p, int blocks, hipStream_t stream) {
-  if (p.doc_start != nullptr) return launch_fwd_t<D, HAS_MASK, O_F32, true, true>(p, blocks, stream);
-  return p.causal ? launch_fwd_t<D, HAS_MASK, O_F32, true, false>(p, blocks, stream)
-                  : launch_fwd_t<D, HAS_MASK, O_F32, false, false>(p, blocks, stream);
+hipError_t dispatch_causal(const FwdParams& p4, const FwdParams& p8, int blocks4, int blocks8, hipStream_t stream) {
+  if (p4.doc_start != nullptr) return launch_fwd_t<4, D, HAS_MASK, O_F32, true, true>(p4, blocks4, stream);
+  if (!p4.causal) return launch_fwd_t<4, D, HAS_MASK, O_F32, false, false>(p4, blocks4, stream);
+  if constexpr (D == 128)
+    if (blocks8 >= kWide8Blocks) return launch_fwd_t<8, D, HAS_MASK, O_F32, true, false>(p8, blocks8, stream);
+  return launch_fwd_t<4, D, HAS_MASK, O_F32, true, false>(p4, blocks4, stream);
 }
 
 template <int D>
-hipError_t dispatch_fwd(const FwdParams& p, int blocks, bool has_mask, bool o_f32, hipStream_t stream) {
-  if (has_mask) return o_f32 ? dispatch_causal<D, true, true>(p, blocks, stream) : dispatch_causal<D, true, false>(p, blocks, stream);
-  return o_f32 ? dispatch_causal<D, false, true>(p, blocks, stream) : dispatch_causal<D, false, false>(p, blocks, stream);
+hipError_t dispatch_fwd(const FwdParams& p4, const FwdParams& p8, int blocks4, int blocks8, bool has_mask, bool o_f32,
+                        hipStream_t stream) {
+  if (has_mask)
+    return o_f32 ? dispatch_causal<D, true, true>(p4, p8, blocks4, blocks8, stream)
+                 : dispatch_causal<D, true, false>(p4, p8, blocks4, blocks8, stream);
+  return o_f32 ? dispatch_causal<D, false, true>(p4, p8, blocks4, blocks8, stream)
+               : dispatch_causal<D, false, false>(p4, p8, blocks4, blocks8, stream);
+}
+
+// workgroup shape for NW waves: query heads per workgroup (the largest
+// divisor of g that divides NW) and positions per workgroup
+void set_shape(FwdParams& p, int nw, int64_t n) {
+  int gh = 1;
+  for (int c = nw; c >= 1; --c)
+    if (p.g % c == 0 && nw % c == 0) { gh = c; break; }
+  p.gh = gh;
+  p.pw = 32 * (nw / gh);
+  p.n_pblocks = int32_t((n + p.pw - 1) / p.pw);
+  p.n_hsub = p.g / gh;
 }
 
 }  // namespace
@@ -425,22 +448,18 @@ hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, con
   p.Hq = s.Hq;
   p.Hkv = s.Hkv;
   p.g = s.Hq / s.Hkv;
-  // query heads per workgroup: the largest divisor of g that is <= 4 (the wave count)
-  int gh = 1;
-  for (int c = kWaves; c >= 1; --c)
-    if (p.g % c == 0 && kWaves % c == 0) { gh = c; break; }
-  p.gh = gh;
-  p.pw = 32 * (kWaves / gh);
-  p.n_pblocks = int32_t((s.n + p.pw - 1) / p.pw);
-  p.n_hsub = p.g / gh;
   p.c = s.scale * kLog2e;
   p.causal = s.causal;
+  FwdParams p8 = p;
+  set_shape(p, 4, s.n);
+  set_shape(p8, 8, s.n);
   const int64_t blocks = int64_t(p.n_pblocks) * p.n_hsub * p.Hkv * p.B;
+  const int64_t blocks8 = int64_t(p8.n_pblocks) * p8.n_hsub * p8.Hkv * p8.B;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   const bool has_mask = valid != nullptr;
-  if (s.D == 128) return dispatch_fwd<128>(p, int(blocks), has_mask, o_f32 != 0, stream);
-  return dispatch_fwd<64>(p, int(blocks), has_mask, o_f32 != 0, stream);
+  if (s.D == 128) return dispatch_fwd<128>(p, p8, int(blocks), int(blocks8), has_mask, o_f32 != 0, stream);
+  return dispatch_fwd<64>(p, p8, int(blocks), int(blocks8), has_mask, o_f32 != 0, stream);
 }
 
 }  // namespace ulysses

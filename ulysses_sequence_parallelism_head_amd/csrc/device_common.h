@@ -177,6 +177,36 @@ __device__ __forceinline__ void pipeline_reads_mfma() {
   __builtin_amdgcn_sched_group_barrier(kMaskMfma, AHEAD, 0);
 }
 
+// The same for LDS reads that each feed two MFMAs (an operand shared by two
+// accumulators): AHEAD reads first, then two MFMAs and one read at a time,
+// then the last 2 * AHEAD MFMAs (N reads, 2N MFMAs).
+template <int AHEAD, int N>
+__device__ __forceinline__ void pipeline_reads_mfma2() {
+  constexpr int kMaskMfma = 0x008, kMaskDsRead = 0x100;
+  __builtin_amdgcn_sched_group_barrier(kMaskDsRead, AHEAD, 0);
+#pragma unroll
+  for (int i = 0; i < N - AHEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kMaskMfma, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(kMaskDsRead, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kMaskMfma, 2 * AHEAD, 0);
+}
+
+// Transposed operands (two LDS reads each) that each feed two MFMAs: reads
+// for AHEAD operands first, then two MFMAs and one operand's two reads at a
+// time, then the last 2 * AHEAD MFMAs (2N reads, 2N MFMAs).
+template <int AHEAD, int N>
+__device__ __forceinline__ void pipeline_tr_reads_mfma2() {
+  constexpr int kMaskMfma = 0x008, kMaskDsRead = 0x100;
+  __builtin_amdgcn_sched_group_barrier(kMaskDsRead, 2 * AHEAD, 0);
+#pragma unroll
+  for (int i = 0; i < N - AHEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kMaskMfma, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(kMaskDsRead, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kMaskMfma, 2 * AHEAD, 0);
+}
+
 // The same for MFMAs whose A operand takes two LDS reads (the transposing
 // reads): reads for AHEAD MFMAs first, then one MFMA and its two reads at a
 // time, then the last AHEAD MFMAs (2N reads, N MFMAs).
@@ -263,6 +293,20 @@ __device__ __forceinline__ void dma4(const i32x4 rsrc, uint8_t* lds, int voffset
 // own in the loop that follows (one that would also stall on the prefetch).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// One 16-byte-per-lane load: rsrc + vo[0] into LDS m0[0] + 16 * lane.
+__device__ __forceinline__ void dma16x1(const i32x4 rsrc, const uint32_t (&m0)[1], const int (&vo)[1]) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(m0[0]), "v"(vo[0]), "s"(uniform_rsrc(rsrc))
+      : "memory");
+}
+
 // Two or four 16-byte-per-lane loads in one asm statement (one M0 save and
 // restore): load u reads rsrc + vo[u] into LDS m0[u] + 16 * lane.
 __device__ __forceinline__ void dma16x2(const i32x4 rsrc, const uint32_t (&m0)[2], const int (&vo)[2]) {
@@ -317,7 +361,7 @@ __device__ __forceinline__ void dma_tile(uint8_t* lds_tile, const uint16_t* row0
   constexpr int ROW_BYTES = 2 * D;
   constexpr int PER_WAVE = ROWS * NC / (64 * NWAVES);
   static_assert(ROWS * NC % (64 * NWAVES) == 0, "tile must split evenly across the waves");
-  static_assert(PER_WAVE == 2 || PER_WAVE == 4, "two or four loads per wave");
+  static_assert(PER_WAVE == 1 || PER_WAVE == 2 || PER_WAVE == 4, "one, two or four loads per wave");
   const i32x4 rsrc = buffer_rsrc(row0, uint32_t(rows_ok > 0 ? rows_ok : 0) * uint32_t(row_stride_bytes));
   const uint32_t base = lds_addr(lds_tile);
   uint32_t m0[PER_WAVE];
@@ -332,7 +376,8 @@ __device__ __forceinline__ void dma_tile(uint8_t* lds_tile, const uint16_t* row0
     vo[u] = r * row_stride_bytes + c * 16;
   }
   if constexpr (PER_WAVE == 4) dma16x4(rsrc, m0, vo);
-  else dma16x2(rsrc, m0, vo);
+  else if constexpr (PER_WAVE == 2) dma16x2(rsrc, m0, vo);
+  else dma16x1(rsrc, m0, vo);
 }
 
 }  // namespace ulysses
