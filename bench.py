@@ -120,7 +120,7 @@ def cpu_baseline(workload, docs: bool, budget_s: float = 12.0):
     ds = d.get("doc_start") if docs else None
     seen = visible_keys(w.n, None if valid is None else valid[0], None if ds is None else ds[0])
     gen = np.random.Generator(np.random.PCG64(12345))
-    workers = oracle.attention._workers(None)
+    workers = host_cores()
     done_rows, flops, spent = 0, 0.0, 0.0
     batch = 64
     while spent < budget_s:
@@ -132,8 +132,45 @@ def cpu_baseline(workload, docs: bool, budget_s: float = 12.0):
         done_rows += batch
     kind = "document-masked causal" if docs else "causal"
     return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{done_rows} seeded query rows x {w.hq} heads of the n={w.n} {kind} forward "
-                      f"(fp64 NumPy, {spent:.1f} s)"}
+                      f"(fp64 NumPy, {workers} worker threads with one BLAS thread each, {spent:.1f} s)"}
+
+
+def host_cores() -> int:
+    """Cores this process may run on (its affinity set)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except Exception:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def measure_sclk(U, torch, fn, call_ms: float, window_ms: float = 40.0):
+    """Median engine clock (MHz) while `fn` (one launch of a kernel) runs back
+    to back for about window_ms, sampled by the library's clock probe on a
+    second stream (default priority).  None if the probe reads nothing."""
+    reps = max(2, int(np.ceil((window_ms + 10.0) / max(call_ms, 1e-3))))
+    samples, interval_us = 20, int(window_ms * 1000 / 20)
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        out, khz = U.ulysses_clock_probe(samples, interval_us, stream=side)
+    for _ in range(reps):
+        fn()
+    torch.cuda.synchronize()
+    mhz = U.clock_probe_mhz(out, khz)[2:]        # the first intervals may precede the kernels
+    return float(np.median(mhz)) if mhz else None
 
 
 def bench_ring(args, w):
@@ -498,6 +535,28 @@ def main():
         step_ms.append(e[0].elapsed_time(e[nev - 1]))
     ms_step = wall * 1e3 / args.steps
     avg = {k: float(np.mean(v)) for k, v in per.items()}
+    med = {k: float(np.median(v)) for k, v in per.items()}
+    mins = {k: float(np.min(v)) for k, v in per.items()}
+
+    # engine clock under each attention call (outside the timed steps)
+    log("[bench] engine clock under the attention calls")
+
+    def fwd_call():
+        if ds_t is None:
+            U.ulysses_attn_fwd(q_h[0], k_h[0], v_h[0], valid_t, w.scale, True, out=o_h[0], lse=lse)
+        else:
+            U.ulysses_attn_fwd_docs(q_h[0], k_h[0], v_h[0], ds_t, valid_t, w.scale, out=o_h[0], lse=lse)
+
+    def bwd_call():
+        if ds_t is None:
+            U.ulysses_attn_bwd(q_h[0], k_h[0], v_h[0], o_h[0], lse, do_h[0], valid_t, w.scale, True,
+                               dq=dq_h[0], dk=dk_h[0], dv=dv_h[0], workspace=ws)
+        else:
+            U.ulysses_attn_bwd_docs(q_h[0], k_h[0], v_h[0], o_h[0], lse, do_h[0], ds_t, valid_t, w.scale,
+                                    dq=dq_h[0], dk=dk_h[0], dv=dv_h[0], workspace=ws)
+
+    sclk = {"attn_fwd": measure_sclk(U, torch, fwd_call, avg["attn_fwd"]),
+            "attn_bwd": measure_sclk(U, torch, bwd_call, avg["attn_bwd"])}
 
     # reference for the repacks, outside the timed steps: a plain 512 MiB device-to-device
     # copy on the same stream (HIP events, median of 5)
@@ -533,13 +592,26 @@ def main():
     }
     value = (fwd_flops + bwd_flops) / (ms_step * 1e-3) / 1e12
 
+    # roofline of each attention call: algorithmic flops over the average
+    # launch duration; also against the peak at the engine clock measured
+    # under that call (the peak scales with the clock; 2.4 GHz is its maximum)
+    def roof(call, flops):
+        achieved = flops / (avg[call] * 1e-3) / 1e12
+        r = {"bound": "mfma", "kernel": call, "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+             "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+             "traffic": measured_traffic(call, w.name + ("+document-mask" if args.docs else ""))}
+        if sclk[call]:
+            peak_at = MFMA_BF16_PEAK_TFLOPS * sclk[call] / 2400.0
+            r["sclk_MHz"] = round(sclk[call], 1)
+            r["peak_at_sclk"] = round(peak_at, 1)
+            r["frac_at_sclk"] = round(achieved / peak_at, 4)
+        return r
+
     # dominant launch: the call with the largest share of the step
     dom = max(("attn_fwd", "attn_bwd"), key=lambda k: avg[k])
-    dom_flops = fwd_flops if dom == "attn_fwd" else bwd_flops
-    achieved = dom_flops / (avg[dom] * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                "traffic": measured_traffic(dom, w.name + ("+document-mask" if args.docs else ""))}
+    roofline = roof(dom, fwd_flops if dom == "attn_fwd" else bwd_flops)
+    other = "attn_bwd" if dom == "attn_fwd" else "attn_fwd"
+    roofline_other = roof(other, bwd_flops if other == "attn_bwd" else fwd_flops)
 
     metric = "causal attn TFLOP/s @64K, 8q/2kv heads d128 bf16; % MFMA peak; repack GB/s"
     if args.docs:
@@ -568,6 +640,10 @@ def main():
                    "visible_pairs_per_head": pairs,
                    "step": "seq2head(q,k,v) > attn_fwd > seq2head(dO) > attn_bwd > head2seq(o) > head2seq(dq,dk,dv)"},
         "breakdown_ms": {k: round(v, 4) for k, v in avg.items()},
+        "per_call_ms": {k: {"mean": round(avg[k], 4), "median": round(med[k], 4), "min": round(mins[k], 4)}
+                        for k in names},
+        "attn_fwd_tflops_median": round(fwd_flops / (med["attn_fwd"] * 1e-3) / 1e12, 2),
+        "attn_bwd_tflops_median": round(bwd_flops / (med["attn_bwd"] * 1e-3) / 1e12, 2),
         "attn_fwd_tflops": round(fwd_tf, 2),
         "attn_fwd_frac_mfma_peak": round(fwd_tf / MFMA_BF16_PEAK_TFLOPS, 4),
         "attn_bwd_tflops": round(bwd_tf, 2),
@@ -577,6 +653,7 @@ def main():
         "device_copy_512MiB_GBs": round(copy_gbs, 1),
         "repack_frac_device_copy": {k: round(v / copy_gbs, 4) for k, v in rep.items()},
         "roofline": roofline,
+        f"roofline_{other}": roofline_other,
     }
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle sample)")

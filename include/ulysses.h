@@ -471,6 +471,31 @@ ULYSSES_API ulysses_status_t ulysses_loss_aggregate(const float* token_loss, con
                                         double* rank_sum, int64_t* rank_count, float* loss,
                                         void* stream);
 
+/*
+ * ulysses_clock_probe -- a measurement aid, not a step of the path: samples
+ * the engine (shader) clock while another kernel runs.
+ *
+ * The matrix-core peak scales with the engine clock, which under sustained
+ * matrix work runs below its maximum; a rate measured against the nominal
+ * peak is also reported against the peak at the clock actually sustained.
+ * One wave, launched on `stream` (a second stream beside the measured
+ * kernel's), records every interval_us microseconds the pair
+ *   out[2s]     real-time counter stamp (constant rate, *wall_khz kHz)
+ *   out[2s + 1] shader cycles elapsed since the previous sample
+ * for s = 0 .. samples-1, so the clock over sample s is
+ *   out[2s+1] / ((out[2s] - out[2s-2]) / (*wall_khz * 1e3))   Hz.
+ * The wave needs a few registers and no LDS, so it runs beside the attention
+ * kernels' waves.  It ends after samples * interval_us microseconds (each
+ * wait is also bounded by a fixed number of polls).
+ *
+ *   out       [2 * samples] uint64, device, 8-byte aligned (output)
+ *   wall_khz  host int32 (output): the real-time counter's rate, kHz
+ * Errors: INVALID_ARG for a null or misaligned out, a null wall_khz,
+ * samples outside [1, 65536] or interval_us outside [1, 10^6].
+ */
+ULYSSES_API ulysses_status_t ulysses_clock_probe(uint64_t* out, int32_t samples, int32_t interval_us,
+                                     int32_t* wall_khz, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -99,10 +99,13 @@ def _doc(doc_start, b):
 
 
 def _workers(workers):
+    """Worker threads: every core of the process's affinity set by default
+    (NumPy's matrix and elementwise kernels release the interpreter lock,
+    and each worker runs one BLAS thread)."""
     if workers is not None:
         return max(1, int(workers))
     try:
-        return max(1, min(16, len(os.sched_getaffinity(0))))
+        return max(1, len(os.sched_getaffinity(0)))
     except Exception:  # pragma: no cover
         return 1
 

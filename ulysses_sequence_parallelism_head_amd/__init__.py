@@ -81,6 +81,8 @@ _SIGS = {
     "ulysses_repack_seq2head_rope": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                                     ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_double,
                                                     ctypes.c_double, ctypes.c_int, ctypes.c_void_p]),
+    "ulysses_clock_probe": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.POINTER(ctypes.c_int32), ctypes.c_void_p]),
     "ulysses_loss_aggregate": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
                                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
 }
@@ -305,6 +307,29 @@ def ulysses_loss_aggregate(token_loss: torch.Tensor, valid: torch.Tensor | None 
     return rank_sum, rank_count, loss
 
 
+def ulysses_clock_probe(samples: int, interval_us: int, stream=None):
+    """Launch the clock sampler on ``stream`` (a torch.cuda.Stream; the
+    current stream if None).  Returns ``(out, wall_khz)``: ``out`` is the
+    uint64 device buffer of (stamp, cycles) pairs as an int64 tensor
+    ``[samples][2]`` (valid once the stream has finished), ``wall_khz`` the
+    real-time counter's rate."""
+    lib = load_library()
+    dev = torch.device("cuda", torch.cuda.current_device())
+    out = torch.zeros((samples, 2), dtype=torch.int64, device=dev)
+    khz = ctypes.c_int32(0)
+    st = ctypes.c_void_p((stream if stream is not None else torch.cuda.current_stream(dev)).cuda_stream)
+    _check(lib.ulysses_clock_probe(_ptr(out), int(samples), int(interval_us), ctypes.byref(khz), st),
+           "ulysses_clock_probe")
+    return out, int(khz.value)
+
+
+def clock_probe_mhz(out: torch.Tensor, wall_khz: int):
+    """Engine clock (MHz) over each interval of a finished probe."""
+    o = out.cpu().numpy()
+    ticks = o[1:, 0] - o[:-1, 0]
+    return [float(c) / (float(t) / (wall_khz * 1e3)) / 1e6 for c, t in zip(o[1:, 1], ticks) if t > 0]
+
+
 def _check_docs(doc_start, B, n):
     if doc_start is not None and (doc_start.dtype != torch.int32 or tuple(doc_start.shape) != (B, n)):
         raise ValueError("doc_start must be int32 [B][n]")
@@ -445,5 +470,6 @@ __all__ = [
     "load_library", "EXPORTED", "LIB_PATH", "ulysses_abi_version", "ulysses_repack_seq2head",
     "ulysses_repack_head2seq", "ulysses_attn_fwd", "ulysses_attn_bwd", "ulysses_attn_bwd_workspace_bytes",
     "ulysses_attn_fwd_docs", "ulysses_attn_bwd_docs", "ulysses_attn_bwd_noalloc", "ulysses_repack_seq2head_rope", "ulysses_loss_aggregate",
-    "ulysses_attn_fwd_block", "ulysses_qkv_proj_seq2head", "ulysses_head2seq_out_proj",
+    "ulysses_attn_fwd_block", "ulysses_qkv_proj_seq2head", "ulysses_head2seq_out_proj", "ulysses_clock_probe",
+    "clock_probe_mhz",
 ]

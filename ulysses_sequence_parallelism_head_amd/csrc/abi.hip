@@ -378,6 +378,16 @@ ulysses_status_t ulysses_head2seq_out_proj(const void* o, const void* w_o, void*
                                                     static_cast<hipStream_t>(stream)));
 }
 
+ulysses_status_t ulysses_clock_probe(uint64_t* out, int32_t samples, int32_t interval_us, int32_t* wall_khz,
+                                     void* stream) {
+  if (out == nullptr || wall_khz == nullptr || samples < 1 || samples > 65536 || interval_us < 1 ||
+      interval_us > 1000000)
+    return ULYSSES_ERR_INVALID_ARG;
+  if (!aligned(out, 8)) return ULYSSES_ERR_INVALID_ARG;
+  return from_hip(ulysses::launch_clock_probe(out, samples, uint32_t(interval_us), wall_khz,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 ulysses_status_t ulysses_loss_aggregate(const float* token_loss, const uint8_t* valid, int32_t P, int64_t per_rank,
                                         double* rank_sum, int64_t* rank_count, float* loss, void* stream) {
   if (P < 1 || P > 65535 || per_rank < 0) return ULYSSES_ERR_INVALID_ARG;

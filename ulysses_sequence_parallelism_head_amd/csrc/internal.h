@@ -66,6 +66,11 @@ hipError_t launch_qkv_proj_seq2head(const void* x, const void* w, void* q, void*
 hipError_t launch_head2seq_out_proj(const void* o, const void* w_o, void* y, int32_t P, int32_t B, int32_t n_local,
                                     int32_t Hq, int32_t D, int32_t hidden, hipStream_t stream);
 
+// one wave sampling (real-time stamp, shader cycles) pairs every interval_us;
+// *wall_khz receives the real-time counter's rate
+hipError_t launch_clock_probe(uint64_t* out, int32_t samples, uint32_t interval_us, int32_t* wall_khz,
+                              hipStream_t stream);
+
 // per-rank sums and counts of the valid tokens' losses, and their ratio
 hipError_t launch_loss_aggregate(const float* token_loss, const uint8_t* valid, int32_t P, int64_t per_rank,
                                  double* rank_sum, int64_t* rank_count, float* loss, hipStream_t stream);
