@@ -181,7 +181,9 @@ ULYSSES_API ulysses_status_t ulysses_attn_fwd(const void* q, const void* k, cons
 /*
  * Bytes of device workspace ulysses_attn_bwd needs for this problem: two
  * float32 [B][Hq][n] arrays (the per-row dot products dO.O, and the
- * logsumexp in base 2), each rounded up to 256 B.
+ * logsumexp in base 2), each rounded up to 256 B, and on short sequences
+ * the partial dK and dV of the workgroups that share a key block
+ * (2 * S * B * n * Hkv * D float32, S <= 8 chosen from B, n and Hkv).
  */
 ULYSSES_API size_t ulysses_attn_bwd_workspace_bytes(int32_t B, int64_t n, int32_t Hq, int32_t Hkv, int32_t D);
 
@@ -206,6 +208,11 @@ ULYSSES_API size_t ulysses_attn_bwd_workspace_bytes(int32_t B, int64_t n, int32_
  *   workspace  device scratch of at least
  *              ulysses_attn_bwd_workspace_bytes(...) bytes, 256-byte
  *              aligned; contents on entry are ignored, on exit undefined.
+ *
+ * On short sequences (fewer than 384 pairs of 128-key blocks over B and
+ * Hkv) each key block's query rows are spread over up to 8 workgroups,
+ * which write partial dK/dV into the workspace; a second pass adds them in
+ * a fixed order, so the result is still the same on every run.
  *
  * Built combinations: in_dtype BF16 with o_dtype BF16 or F32; D 64 or 128.
  * Errors: as ulysses_attn_fwd, plus INVALID_ARG for a null or too small
@@ -234,7 +241,12 @@ ULYSSES_API ulysses_status_t ulysses_attn_bwd(const void* q, const void* k, cons
  *
  * Limit: 2 * B * Hq * n * 4 bytes <= 16 MiB, i.e. B * Hq * n <= 2^21 rows
  * (the 64K workload's 8 query heads use 2^19).  Larger problems return
- * ULYSSES_ERR_SCRATCH_LIMIT before anything is launched.
+ * ULYSSES_ERR_SCRATCH_LIMIT before anything is launched.  The scratch holds
+ * only the two row arrays: this call never spreads a key block's query
+ * rows over several workgroups (ulysses_attn_bwd does on short sequences,
+ * adding partial sums from its workspace), so on short sequences its dK
+ * and dV may differ from ulysses_attn_bwd's in float32 rounding; dQ is
+ * identical.
  * Every call on a GPU uses that GPU's one scratch array, and nothing in it
  * needs to start at zero (each call writes every value before reading
  * it): calls that overlap in time on one GPU -- on different streams, or

@@ -105,7 +105,7 @@ def test_fwd_validation(lib):
     assert _fwd(lib, n=0, q=None, k=None, v=None, o=None, lse=None) == OK
 
 
-def _bwd(lib, ws=ctypes.c_void_p(0x9000000), wsb=1 << 20, dq=ctypes.c_void_p(0x6000000), it=BF16, D=128, n=64):
+def _bwd(lib, ws=ctypes.c_void_p(0x9000000), wsb=1 << 21, dq=ctypes.c_void_p(0x6000000), it=BF16, D=128, n=64):
     return lib.ulysses_attn_bwd(FAKE, ctypes.c_void_p(0x1000000), ctypes.c_void_p(0x2000000), None,
                                 ctypes.c_void_p(0x3000000), ctypes.c_void_p(0x4000000), ctypes.c_void_p(0x5000000),
                                 dq, ctypes.c_void_p(0x7000000), ctypes.c_void_p(0x8000000), ws, wsb,
@@ -114,8 +114,13 @@ def _bwd(lib, ws=ctypes.c_void_p(0x9000000), wsb=1 << 20, dq=ctypes.c_void_p(0x6
 
 def test_bwd_validation(lib):
     need = lib.ulysses_attn_bwd_workspace_bytes(1, 64, 8, 2, 128)
-    assert need == 2 * 64 * 8 * 4 and need % 256 == 0
+    # two float32 row arrays, plus (short sequences) 8 splits' partial dK and dV
+    assert need == 2 * 64 * 8 * 4 + 2 * 8 * 64 * 2 * 128 * 4 and need % 256 == 0
     assert lib.ulysses_attn_bwd_workspace_bytes(0, 64, 8, 2, 128) == 0
+    # long sequences: no splits, the row arrays only (n = 65536, 2 KV heads: 512 key-block pairs)
+    assert lib.ulysses_attn_bwd_workspace_bytes(1, 65536, 8, 2, 128) == 2 * 65536 * 8 * 4
+    # 8192 tokens, 2 KV heads: 64 pairs -> 8 splits
+    assert lib.ulysses_attn_bwd_workspace_bytes(1, 8192, 8, 2, 128) == 2 * 8192 * 8 * 4 + 2 * 8 * 8192 * 2 * 128 * 4
     assert _bwd(lib, wsb=need - 1) == INVALID
     assert _bwd(lib, ws=None) == INVALID
     assert _bwd(lib, ws=ctypes.c_void_p(0x9000000 + 16)) == INVALID        # workspace not 256-byte aligned

@@ -1,10 +1,18 @@
 """The no-allocation backward, ulysses_attn_bwd_noalloc, through the C ABI:
-its gradients must equal ulysses_attn_bwd's (same kernels, the workspace
-taken from the library's fixed per-GPU scratch) bit for bit, on calls in a
-row whose sizes shrink (nothing left in the shared scratch by one call may
-leak into the next), at the scratch limit, and it must refuse a problem
-one row-block beyond the limit.  The call itself allocates nothing: torch's
-allocator counts no allocation across it."""
+its gradients must match ulysses_attn_bwd's (same kernels, the workspace
+taken from the library's fixed per-GPU scratch) on calls in a row whose
+sizes shrink (nothing left in the shared scratch by one call may leak into
+the next) and at the scratch limit, and it must refuse a problem one
+row-block beyond the limit.  The call itself allocates nothing: torch's
+allocator counts no allocation across it.
+
+dQ must be bit-identical.  dK and dV too where the workspace call runs its
+key blocks unsplit (long sequences); on short sequences the workspace call
+spreads each key block's query units over several workgroups and adds
+their partial sums (its workspace holds them), which the no-allocation
+call, whose scratch holds only the row arrays, does not: there the two
+agree to float32 summation order (relative 1e-5), and both meet the
+oracle's 1e-2."""
 import numpy as np
 import pytest
 import torch
@@ -47,10 +55,20 @@ def _both(q, k, v, do, valid, scale, causal, o_dtype):
     return [to_host_f64(r) for r in ref], [to_host_f64(g) for g in got]
 
 
-def _same(ref, got):
+def _same(ref, got, split):
     for name, r, g in zip(("dq", "dk", "dv"), ref, got):
         assert not np.any(np.isnan(g)), f"{name}: element not written"
-        assert np.array_equal(r, g), f"{name}: differs from the workspace call"
+        if name == "dq" or not split:
+            assert np.array_equal(r, g), f"{name}: differs from the workspace call"
+        else:
+            tol = 1e-5 * max(1.0, float(np.abs(r).max()))
+            assert float(np.abs(r - g).max()) <= tol, f"{name}: differs from the workspace call beyond {tol}"
+
+
+def _splits(n, Hq, Hkv, D):
+    """Whether the workspace call splits its key blocks: its workspace then
+    holds more than the two row arrays."""
+    return U.ulysses_attn_bwd_workspace_bytes(1, n, Hq, Hkv, D) > 2 * n * Hq * 4 + 512
 
 
 def test_noalloc_equals_workspace_call_shrinking_sizes():
@@ -64,7 +82,7 @@ def test_noalloc_equals_workspace_call_shrinking_sizes():
         q, k, v, do, valid = _inputs(4040 + i, n, Hq, Hkv, D, masked)
         scale = D ** -0.5
         ref, got = _both(q, k, v, do, valid, scale, causal, o_dtype)
-        _same(ref, got)
+        _same(ref, got, _splits(n, Hq, Hkv, D))
         dQ, dK, dV, _, _ = oracle.attn_bwd(to_f64(q), to_f64(k), to_f64(v), to_f64(do), scale, causal, valid)
         assert_close("dQ", got[0], dQ, 1e-2)
         assert_close("dK", got[1], dK, 1e-2)
@@ -79,7 +97,8 @@ def test_noalloc_at_the_limit_and_beyond():
     say(f"noalloc at the limit: n={n} Hq={Hq} Hkv={Hkv}")
     q, k, v, do, _ = _inputs(4050, n, Hq, Hkv, D, False)
     ref, got = _both(q, k, v, do, None, D ** -0.5, True, torch.bfloat16)
-    _same(ref, got)
+    assert not _splits(n, Hq, Hkv, D)
+    _same(ref, got, False)
     del ref, got
     say("noalloc beyond the limit")
     n2 = n + 64

@@ -119,7 +119,8 @@ ulysses_status_t check_bwd(const void* q, const void* k, const void* v, const ui
       !aligned(lse, 4) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(workspace, 256) ||
       !aligned(doc_start, 4))
     return ULYSSES_ERR_INVALID_ARG;
-  const size_t need = ulysses::attn_bwd_workspace_bytes(B, n, Hq);
+  const size_t need =
+      ulysses::attn_bwd_workspace_bytes(B, n, Hq, Hkv, D, own_workspace ? ulysses::attn_bwd_nsplit(B, n, Hkv) : 1);
   if (own_workspace && workspace_bytes < need) return ULYSSES_ERR_INVALID_ARG;
   const uint64_t nq = uint64_t(B) * n * Hq * D, nkv = uint64_t(B) * n * Hkv * D;
   const void* ins[8] = {q, k, v, key_valid, o, lse, dout, doc_start};
@@ -151,7 +152,7 @@ ulysses_status_t attn_bwd(const void* q, const void* k, const void* v, const uin
   AttnShape s{B, n, Hq, Hkv, D, softmax_scale, causal};
   return from_hip(ulysses::launch_attn_bwd_bf16(q, k, v, key_valid, doc_start, o, lse, dout, dq, dk, dv,
                                                 static_cast<float*>(workspace), s, o_dtype == ULYSSES_DTYPE_F32,
-                                                static_cast<hipStream_t>(stream)));
+                                                ulysses::attn_bwd_nsplit(B, n, Hkv), static_cast<hipStream_t>(stream)));
 }
 
 // ---- the no-allocation backward
@@ -234,10 +235,8 @@ ulysses_status_t ulysses_attn_fwd_docs(const void* q, const void* k, const void*
 }
 
 size_t ulysses_attn_bwd_workspace_bytes(int32_t B, int64_t n, int32_t Hq, int32_t Hkv, int32_t D) {
-  (void)Hkv;
-  (void)D;
-  if (B <= 0 || n <= 0 || Hq <= 0) return 0;
-  return ulysses::attn_bwd_workspace_bytes(B, n, Hq);
+  if (B <= 0 || n <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0) return 0;
+  return ulysses::attn_bwd_workspace_bytes(B, n, Hq, Hkv, D, ulysses::attn_bwd_nsplit(B, n, Hkv));
 }
 
 ulysses_status_t ulysses_attn_bwd(const void* q, const void* k, const void* v, const uint8_t* key_valid,
@@ -258,13 +257,13 @@ ulysses_status_t ulysses_attn_bwd_noalloc(const void* q, const void* k, const vo
   ulysses_status_t st = check_bwd(q, k, v, key_valid, nullptr, o, lse, dout, dq, dk, dv, nullptr, 0, false, B, n,
                                   Hq, Hkv, D, softmax_scale, causal, in_dtype, o_dtype, &empty);
   if (st != ULYSSES_OK || empty) return st;
-  if (ulysses::attn_bwd_workspace_bytes(B, n, Hq) > kNoAllocScratchBytes) return ULYSSES_ERR_SCRATCH_LIMIT;
+  if (ulysses::attn_bwd_workspace_bytes(B, n, Hq, Hkv, D, 1) > kNoAllocScratchBytes) return ULYSSES_ERR_SCRATCH_LIMIT;
   hipError_t e = hipSuccess;
   void* ws = scratch_on_current_device(&e);
   if (ws == nullptr) return ULYSSES_ERR_HIP;
   AttnShape s{B, n, Hq, Hkv, D, softmax_scale, causal};
   return from_hip(ulysses::launch_attn_bwd_bf16(q, k, v, key_valid, nullptr, o, lse, dout, dq, dk, dv,
-                                                static_cast<float*>(ws), s, o_dtype == ULYSSES_DTYPE_F32,
+                                                static_cast<float*>(ws), s, o_dtype == ULYSSES_DTYPE_F32, 1,
                                                 static_cast<hipStream_t>(stream)));
 }
 

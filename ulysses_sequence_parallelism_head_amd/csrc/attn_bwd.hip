@@ -43,6 +43,7 @@
 // last document its keys belong to (a 64-lane search over the bounds) and
 // visits only the query tiles up to it, sweeping down from there so that the
 // workgroups of one document read the same tiles at the same time.
+#include <algorithm>
 #include <type_traits>
 
 #include "device_common.h"
@@ -71,6 +72,10 @@ struct BwdParams {
   float* dv;
   float* rowdot;      // [B][Hq][n] dO . O (workspace)
   float* lse2;        // [B][Hq][n] lse * log2(e), +inf for empty rows (workspace)
+  float* dk_part;     // [nsplit][B][n][Hkv][D] partial dK of each split (workspace; nsplit > 1)
+  float* dv_part;     // [nsplit][B][n][Hkv][D] partial dV
+  int32_t nsplit;     // workgroups sharing one key block's query units (a power of two)
+  int32_t lsplit;     // log2(nsplit)
   int32_t B, n, Hq, Hkv, g;
   float scale;
   float c;            // scale * log2(e)
@@ -321,10 +326,12 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdParams p) {
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
-  // block -> (work item, kv head, batch); kv head varies fastest
+  // block -> (split, work item, kv head, batch); split fastest, then kv head
+  const int sp = int(blockIdx.x) & (p.nsplit - 1);
+  const int bid = int(blockIdx.x) >> p.lsplit;
   const int per_w = p.Hkv * p.B;
-  const int w = int(blockIdx.x) / per_w;
-  const int rem = int(blockIdx.x) % per_w;
+  const int w = bid / per_w;
+  const int rem = bid % per_w;
   const int b = rem / p.Hkv;
   const int kvh = rem % p.Hkv;
   const int ntq = (p.n + L::kRows - 1) / L::kRows;   // query tiles per head
@@ -386,8 +393,14 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdParams p) {
     const int niter = (tend - tfirst) * p.g;
     // unit it -> (tile, head of the group)
     auto tile_of = [&](int it) { return down ? tend - 1 - it / p.g : tfirst + it / p.g; };
+    // this split's units [u0, u1): the block's units cut into nsplit equal
+    // runs (wave-uniform scalars: they bound the loops around the MFMAs)
+    const int u0 = __builtin_amdgcn_readfirstlane((niter * sp) >> p.lsplit);
+    const int u1 = __builtin_amdgcn_readfirstlane((niter * (sp + 1)) >> p.lsplit);
 
-    if (niter > 0) dkdv_issue<D, DOCS>(smem, p, b, kvh * p.g, tile_of(0) * L::kRows, wave, lane);
+    if (u0 < u1)
+      dkdv_issue<D, DOCS>(smem + (u0 & 1) * L::kStageAligned, p, b, kvh * p.g + u0 % p.g, tile_of(u0) * L::kRows,
+                          wave, lane);
     wait_vmem();
     __syncthreads();
 
@@ -404,7 +417,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdParams p) {
       for (int it = it0; it < it1; ++it) {
         // prefetch unit it+1 into the other buffer while computing on this one
         uint8_t* cur = smem + (it & 1) * L::kStageAligned;
-        if (it + 1 < niter)
+        if (it + 1 < u1)
           dkdv_issue<D, DOCS>(smem + ((it + 1) & 1) * L::kStageAligned, p, b, kvh * p.g + (it + 1) % p.g,
                               tile_of(it + 1) * L::kRows, wave, lane);
         const int t0 = tile_of(it) * L::kRows;
@@ -459,10 +472,12 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdParams p) {
       using F = std::false_type;
       const int n1 = min(nsplit, ndiag), n2 = max(nsplit, ndiag);
       // runs by distance from the diagonal end: [0, n1) both, [n1, n2) one, [n2, niter) neither
+      // units [x0, x1) of the run, cut to this split's [u0, u1)
       auto seg = [&](int a, int z, auto split_tag, auto diag_tag) __attribute__((always_inline)) {
-        if (a >= z) return;
-        if (down) run(niter - z, niter - a, split_tag, diag_tag, lower_tag);
-        else run(a, z, split_tag, diag_tag, lower_tag);
+        const int x0 = max(down ? niter - z : a, u0);
+        const int x1 = min(down ? niter - a : z, u1);
+        if (x0 >= x1) return;
+        run(x0, x1, split_tag, diag_tag, lower_tag);
       };
       if (down) {                       // the diagonal end comes last
         seg(n2, niter, F{}, F{});
@@ -486,7 +501,15 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdParams p) {
 
     // write dK = scale * dK^T^T and dV: lane = key u, dims 32j + 8*(i/4) + 4hh + i%4;
     // a padding key's gradients are zero (selected, not multiplied: its
-    // unmasked column may hold any value, inf or NaN included)
+    // unmasked column may hold any value, inf or NaN included).  With
+    // several splits each writes its partial sums, added by dkdv_reduce.
+    float* dk_out = p.dk;
+    float* dv_out = p.dv;
+    if (p.nsplit > 1) {
+      const int64_t part = int64_t(p.B) * p.n * p.Hkv * D;
+      dk_out = p.dk_part + sp * part;
+      dv_out = p.dv_part + sp * part;
+    }
     if (u < p.n) {
       const int64_t base = ((int64_t(b) * p.n + u) * p.Hkv + kvh) * D;
 #pragma unroll
@@ -498,11 +521,24 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdParams p) {
                             dka[j][i4 * 4 + 3] * p.scale};
           f32x4 vv4 = f32x4{dva[j][i4 * 4], dva[j][i4 * 4 + 1], dva[j][i4 * 4 + 2], dva[j][i4 * 4 + 3]};
           if (!key_ok) kv4 = vv4 = f32x4{0.f, 0.f, 0.f, 0.f};
-          *reinterpret_cast<f32x4*>(p.dk + base + d0) = kv4;
-          *reinterpret_cast<f32x4*>(p.dv + base + d0) = vv4;
+          *reinterpret_cast<f32x4*>(dk_out + base + d0) = kv4;
+          *reinterpret_cast<f32x4*>(dv_out + base + d0) = vv4;
         }
     }
   }
+}
+
+// Sum of the splits' partial dK (or dV) in split order: out[i] = sum_s part[s][i]
+// (a fixed order, so the result does not depend on scheduling).
+__global__ __launch_bounds__(256) void dkdv_reduce_kernel(const float* part, float* out, int64_t count, int32_t nsplit) {
+  const int64_t i = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (i >= count) return;
+  f32x4 acc = *reinterpret_cast<const f32x4*>(part + i);
+  for (int32_t sp = 1; sp < nsplit; ++sp) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(part + sp * count + i);
+    acc = f32x4{acc[0] + x[0], acc[1] + x[1], acc[2] + x[2], acc[3] + x[3]};
+  }
+  *reinterpret_cast<f32x4*>(out + i) = acc;
 }
 
 // --------------------------------------------------------------------- dq
@@ -784,6 +820,14 @@ hipError_t launch_grads(const BwdParams& p, int64_t kv_blocks, int64_t q_blocks,
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((dkdv_kernel<D, HAS_MASK, CAUSAL, DOCS>), dim3(kv_blocks), dim3(kThreads), 0, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess || p.nsplit == 1) return e;
+  const int64_t count = int64_t(p.B) * p.n * p.Hkv * D;   // a multiple of 4 (D is)
+  const int64_t rblocks = (count / 4 + 255) / 256;
+  hipLaunchKernelGGL(dkdv_reduce_kernel, dim3(rblocks), dim3(256), 0, stream, p.dk_part, p.dk, count, p.nsplit);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(dkdv_reduce_kernel, dim3(rblocks), dim3(256), 0, stream, p.dv_part, p.dv, count, p.nsplit);
   return hipGetLastError();
 }
 
@@ -807,7 +851,7 @@ hipError_t launch_bwd_d(const BwdParams& p, bool has_mask, bool o_f32, hipStream
   // causal: one workgroup per pair of key blocks (nkb-1-w, w); documents:
   // one per key block
   const int64_t kv_work = (p.causal && p.doc_start == nullptr) ? (int64_t(p.n_kblocks) + 1) / 2 : p.n_kblocks;
-  const int64_t kv_blocks = kv_work * p.Hkv * p.B;
+  const int64_t kv_blocks = kv_work * p.Hkv * p.B * p.nsplit;
   const int64_t q_blocks = int64_t(p.n_pblocks) * p.n_hsub * p.Hkv * p.B;
   if (kv_blocks > 0x7fffffff || q_blocks > 0x7fffffff) return hipErrorInvalidValue;
   return has_mask ? dispatch_grads<D, true>(p, kv_blocks, q_blocks, stream)
@@ -824,13 +868,29 @@ size_t row_array_bytes(int32_t B, int64_t n, int32_t Hq) {
 }
 }  // namespace
 
-// Dl = dO . O, then the base-2 logsumexp
-size_t attn_bwd_workspace_bytes(int32_t B, int64_t n, int32_t Hq) { return 2 * row_array_bytes(B, n, Hq); }
+// Workgroups per key-block pair of the dK/dV pass: enough that short
+// sequences still give the 256 CUs about two workgroups each (one resident
+// per CU).  A function of the shape only, so the result of a call does not
+// depend on the device or the workspace handed in.
+int attn_bwd_nsplit(int32_t B, int64_t n, int32_t Hkv) {
+  const int64_t pairs = ((n + 127) / 128 + 1) / 2 * int64_t(Hkv) * B;
+  int s = 1;
+  while (s < 8 && pairs * s < 384) s *= 2;   // a power of two, at most 8
+  return s;
+}
+
+// Dl = dO . O, then the base-2 logsumexp; with several splits, their
+// partial dK and dV
+size_t attn_bwd_workspace_bytes(int32_t B, int64_t n, int32_t Hq, int32_t Hkv, int32_t D, int nsplit) {
+  size_t bytes = 2 * row_array_bytes(B, n, Hq);
+  if (nsplit > 1) bytes += 2 * size_t(nsplit) * size_t(B) * size_t(n) * size_t(Hkv) * size_t(D) * sizeof(float);
+  return bytes;
+}
 
 hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const uint8_t* valid,
                                 const int32_t* doc_start, const void* o, const float* lse, const void* dout,
                                 float* dq, float* dk, float* dv, float* workspace, const AttnShape& s, int o_f32,
-                                hipStream_t stream) {
+                                int nsplit, hipStream_t stream) {
   BwdParams p;
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
@@ -845,6 +905,11 @@ hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, con
   p.dv = dv;
   p.rowdot = workspace;
   p.lse2 = workspace + row_array_bytes(s.B, s.n, s.Hq) / sizeof(float);
+  p.nsplit = nsplit < 1 ? 1 : nsplit;
+  p.lsplit = 0;
+  while ((1 << p.lsplit) < p.nsplit) ++p.lsplit;
+  p.dk_part = p.lse2 + row_array_bytes(s.B, s.n, s.Hq) / sizeof(float);
+  p.dv_part = p.dk_part + size_t(p.nsplit) * size_t(s.B) * size_t(s.n) * size_t(s.Hkv) * size_t(s.D);
   p.B = s.B;
   p.n = int32_t(s.n);
   p.Hq = s.Hq;

@@ -45,13 +45,16 @@ hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, c
                                hipStream_t stream);
 
 // bf16 inputs; o is bf16 or float32 (o_f32); gradients are float32.
-// workspace holds the per-row dO.O values and the base-2 logsumexp.
+// workspace holds the per-row dO.O values and the base-2 logsumexp, and with
+// nsplit > 1 the splits' partial dK/dV (attn_bwd_workspace_bytes(..., nsplit)).
 hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const uint8_t* valid,
                                 const int32_t* doc_start, const void* o, const float* lse, const void* dout,
                                 float* dq, float* dk, float* dv, float* workspace, const AttnShape& s, int o_f32,
-                                hipStream_t stream);
+                                int nsplit, hipStream_t stream);
 
-size_t attn_bwd_workspace_bytes(int32_t B, int64_t n, int32_t Hq);
+// workgroups per key-block pair of the dK/dV pass for this shape
+int attn_bwd_nsplit(int32_t B, int64_t n, int32_t Hkv);
+size_t attn_bwd_workspace_bytes(int32_t B, int64_t n, int32_t Hq, int32_t Hkv, int32_t D, int nsplit);
 
 // seq2head fused with the rotary embedding at global positions; elem_bytes
 // 2 (bf16) or 4 (fp32), D 64 or 128, H % P == 0.
