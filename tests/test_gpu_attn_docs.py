@@ -177,9 +177,13 @@ def test_single_document_matches_causal_bitwise():
     kernels must give the causal kernels' O, LSE and dQ bit for bit.  dK and
     dV sum the same terms, but the document kernel visits every key block's
     query tiles from the last down while the causal kernel visits half of
-    them upwards, so those agree to float32 rounding of the sums."""
+    them upwards, so those agree to float32 rounding of the sums.
+    (n = 16400: long enough for the plain causal forward's shared-tile
+    workgroups, whose arithmetic is the 4-wave kernel's; short plain causal
+    runs split each block's keys between two wave groups and merge them,
+    which rounds differently.)"""
     say("docs: one document == causal, bitwise")
-    n, Hq, Hkv, D = 1500, 8, 2, 128
+    n, Hq, Hkv, D = 16400, 8, 2, 128
     q, k, v, do, ds, valid = _inputs(99, n, Hq, Hkv, D, True, ("one",))
     scale = D ** -0.5
     got = _gpu(q, k, v, do, ds, valid, scale, torch.bfloat16)

@@ -103,6 +103,7 @@ struct FwdParams {
 template <int NW, int D, bool HAS_MASK>
 __device__ __forceinline__ void fwd_issue(uint8_t* stage, uint32_t& vbyte, const FwdParams& p, int b, int kvh,
                                           int tile, int wave, int lane, int tid) {
+  // (wave, tid: indices within the NW waves that stage this tile)
   using L = FwdLayout<D>;
   const int key0 = tile * kBN;
   const int rows_ok = min(kBN, p.nk - key0);
@@ -116,18 +117,33 @@ __device__ __forceinline__ void fwd_issue(uint8_t* stage, uint32_t& vbyte, const
   }
 }
 
-template <int NW, int D, bool HAS_MASK, bool O_F32, bool CAUSAL, bool DOCS>
+// KS (key split, 8 waves): two groups of 4 waves take the same rows, the
+// first group the first half of their key tiles and the second the rest,
+// each with its own staging buffers and online softmax; at the end the
+// second group hands its (O, max, row sum) to the first through LDS, which
+// merges them exactly (the same combination as for disjoint key blocks) and
+// writes the output.  Every workgroup then lasts about half as long as its
+// block's keys, which evens out the causal triangle on short grids, where
+// all blocks are resident at once and the longest one sets the time.
+template <int NW, int D, bool HAS_MASK, bool O_F32, bool CAUSAL, bool DOCS, bool KS>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(const FwdParams p) {
   static_assert(CAUSAL || !DOCS, "documents are causal");
+  static_assert(!KS || (NW == 8 && !DOCS), "the key split pairs two 4-wave groups");
   using L = FwdLayout<D>;
   constexpr int KK = D / 16;     // contraction slices of the score product
   constexpr int DJ = D / 32;     // 32-row blocks of O^T
-  __shared__ __attribute__((aligned(128))) uint8_t smem[2 * L::kStageAligned];
+  constexpr int NG = KS ? 2 : 1;         // wave groups
+  constexpr int GW = NW / NG;            // waves per group
+  __shared__ __attribute__((aligned(128))) uint8_t smem[NG * 2 * L::kStageAligned];
 
-  const int tid = threadIdx.x;
+  const int tid_all = threadIdx.x;
   // wave index as a scalar: every branch that guards a matrix-core instruction
   // must be wave-uniform to the compiler (MFMA does not honour EXEC)
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_all = __builtin_amdgcn_readfirstlane(tid_all >> 6);
+  const int grp = KS ? wave_all / GW : 0;
+  const int wave = wave_all % GW;        // wave within its group
+  const int tid = tid_all % (GW * 64);   // thread within its group
+  uint8_t* const gsmem = smem + grp * 2 * L::kStageAligned;   // the group's two staging buffers
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
@@ -186,9 +202,15 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(const Fw
     float m_ref = -INFINITY;   // running reference max (log2 units), identical in both half-waves
     float lsum = 0.f;          // this half-wave's share of the row sum
 
+    // this group's tiles [it_beg, it_end), in nsteps steps of one barrier each
+    // (with the key split the first group takes the first half, rounded up)
+    const int nsteps = KS ? (max(ntiles - it_first, 0) + 1) / 2 : 0;
+    const int it_beg = KS ? it_first + (grp == 1 ? nsteps : 0) : it_first;
+    const int it_end = KS && grp == 0 ? it_first + nsteps : ntiles;
+
     uint32_t vbyte = 0;
-    fwd_issue<NW, D, HAS_MASK>(smem, vbyte, p, b, kvh, it_first, wave, lane, tid);
-    if (HAS_MASK && tid < kBN) reinterpret_cast<float*>(smem + L::kBytesK + L::kBytesV)[tid] = vbyte ? 0.f : -INFINITY;
+    if (!KS || it_beg < it_end) fwd_issue<GW, D, HAS_MASK>(gsmem, vbyte, p, b, kvh, it_beg, wave, lane, tid);
+    if (HAS_MASK && tid < kBN) reinterpret_cast<float*>(gsmem + L::kBytesK + L::kBytesV)[tid] = vbyte ? 0.f : -INFINITY;
     wait_vmem();
     __syncthreads();
 
@@ -197,10 +219,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(const Fw
     // statically and every LDS address folds the buffer into the
     // instruction's immediate offset.
     auto tile = [&](int it, uint8_t* cur, uint8_t* nxt) {
-      if (it + 1 < ntiles) fwd_issue<NW, D, HAS_MASK>(nxt, vbyte, p, b, kvh, it + 1, wave, lane, tid);
+      if (it + 1 < it_end) fwd_issue<GW, D, HAS_MASK>(nxt, vbyte, p, b, kvh, it + 1, wave, lane, tid);
 
       const int tile0 = it * kBN;
-      if (wave_live && !(CAUSAL && tile0 > wave_last + p.delta) && !(DOCS && tile0 + kBN <= lo_wave)) {
+      // (with the key split the second group may have one step fewer than the first)
+      if ((!KS || it < it_end) && wave_live && !(CAUSAL && tile0 > wave_last + p.delta) &&
+          !(DOCS && tile0 + kBN <= lo_wave)) {
         const uint8_t* ks = cur;
         const uint8_t* vs = cur + L::kBytesK;
 
@@ -317,17 +341,56 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(const Fw
         if (!SPLIT) pipeline_tr_reads_mfma<4, 4 * DJ>();
       }
 
-      if (HAS_MASK && it + 1 < ntiles && tid < kBN)
+      if (HAS_MASK && it + 1 < it_end && tid < kBN)
         reinterpret_cast<float*>(nxt + L::kBytesK + L::kBytesV)[tid] = vbyte ? 0.f : -INFINITY;
       wait_vmem();
       __syncthreads();
     };
-    int it = it_first;
-    for (; it + 1 < ntiles; it += 2) {
-      tile(it, smem, smem + L::kStageAligned);
-      tile(it + 1, smem + L::kStageAligned, smem);
+    if constexpr (KS) {
+      int st = 0;
+      for (; st + 1 < nsteps; st += 2) {
+        tile(it_beg + st, gsmem, gsmem + L::kStageAligned);
+        tile(it_beg + st + 1, gsmem + L::kStageAligned, gsmem);
+      }
+      if (st < nsteps) tile(it_beg + st, gsmem, gsmem + L::kStageAligned);
+    } else {
+      int it = it_first;
+      for (; it + 1 < ntiles; it += 2) {
+        tile(it, smem, smem + L::kStageAligned);
+        tile(it + 1, smem + L::kStageAligned, smem);
+      }
+      if (it < ntiles) tile(it, smem, smem + L::kStageAligned);
     }
-    if (it < ntiles) tile(it, smem, smem + L::kStageAligned);
+
+    if constexpr (KS) {
+      // the second group's (row max, row-sum share, O accumulators) to LDS,
+      // lane-contiguous per value; the first group merges them into its own.
+      // Every tile read is behind the last step's barrier, so the staging
+      // buffers are free.
+      constexpr int NV = 2 + 16 * DJ;
+      float* xch = reinterpret_cast<float*>(smem) + wave * NV * 64 + lane;
+      if (grp == 1) {
+        xch[0] = m_ref;
+        xch[64] = lsum;
+#pragma unroll
+        for (int j = 0; j < DJ; ++j)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) xch[(2 + 16 * j + i) * 64] = oacc[j][i];
+      }
+      __syncthreads();
+      if (grp == 1) return;
+      // weights 2^(m_g - m) of each group's terms (0 for a group that saw no key)
+      const float m_b = xch[0];
+      const float m = fmaxf(m_ref, m_b);
+      const float wa = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - m);
+      const float wb = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_b - m);
+      lsum = lsum * wa + xch[64] * wb;
+#pragma unroll
+      for (int j = 0; j < DJ; ++j)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[j][i] = oacc[j][i] * wa + xch[(2 + 16 * j + i) * 64] * wb;
+      m_ref = m;
+    }
 
     // ---- epilogue: normalise, write O (row t, dims 32j + 8*(i/4) + 4hh + i%4) and LSE
     if (t < p.n) {
@@ -383,9 +446,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(const Fw
   else run(std::false_type{});
 }
 
-template <int NW, int D, bool HAS_MASK, bool O_F32, bool CAUSAL, bool DOCS>
+template <int NW, int D, bool HAS_MASK, bool O_F32, bool CAUSAL, bool DOCS, bool KS = false>
 hipError_t launch_fwd_t(const FwdParams& p, int blocks, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<NW, D, HAS_MASK, O_F32, CAUSAL, DOCS>), dim3(blocks), dim3(NW * 64), 0,
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<NW, D, HAS_MASK, O_F32, CAUSAL, DOCS, KS>), dim3(blocks), dim3(NW * 64), 0,
                      stream, p);
   return hipGetLastError();
 }
@@ -394,14 +457,17 @@ hipError_t launch_fwd_t(const FwdParams& p, int blocks, hipStream_t stream) {
 // SIMD as with two 4-wave workgroups): each staged K/V tile then feeds 8
 // waves, which halves the DMA writes into LDS and the L2 reads per flop
 // (measured 4 % faster at n = 64K, 10 % on 128K single-head runs, identical
-// output).  Short grids keep 4-wave workgroups, whose finer granularity
-// balances the causal triangle better.
+// output).  Short plain causal grids, where every block is resident at once
+// and the longest sets the time, use the key split: 8-wave workgroups over
+// the 4-wave blocks, each block's keys halved between two groups.
 template <int D, bool HAS_MASK, bool O_F32>
 hipError_t dispatch_causal(const FwdParams& p4, const FwdParams& p8, int blocks4, int blocks8, hipStream_t stream) {
   if (p4.doc_start != nullptr) return launch_fwd_t<4, D, HAS_MASK, O_F32, true, true>(p4, blocks4, stream);
   if (!p4.causal) return launch_fwd_t<4, D, HAS_MASK, O_F32, false, false>(p4, blocks4, stream);
-  if constexpr (D == 128)
+  if constexpr (D == 128) {
     if (blocks8 >= kWide8Blocks) return launch_fwd_t<8, D, HAS_MASK, O_F32, true, false>(p8, blocks8, stream);
+    return launch_fwd_t<8, D, HAS_MASK, O_F32, true, false, true>(p4, blocks4, stream);
+  }
   return launch_fwd_t<4, D, HAS_MASK, O_F32, true, false>(p4, blocks4, stream);
 }
 
