@@ -74,12 +74,17 @@ typedef enum {
   ULYSSES_ERR_INVALID_ARG = 1,  /* a null pointer, a bad size, a violated constraint, misalignment, aliasing */
   ULYSSES_ERR_UNSUPPORTED = 2,  /* valid in principle, not built: head dim, dtype combination, size limits */
   ULYSSES_ERR_HIP = 3,          /* a HIP launch failed */
-  ULYSSES_ERR_SCRATCH_LIMIT = 4 /* too large for ulysses_attn_bwd_noalloc's fixed scratch */
+  ULYSSES_ERR_SCRATCH_LIMIT = 4, /* too large for ulysses_attn_bwd_noalloc's fixed scratch */
+  ULYSSES_STATUS_MAX_ENUM = 0x7fffffff
 } ulysses_status_t;
 
+/* The *_MAX_ENUM values are not codes: they keep each type 32 bits wide, so
+   that any non-negative int a C caller passes is a value of the type (the
+   library then rejects unknown ones as INVALID_ARG). */
 typedef enum {
   ULYSSES_DTYPE_F32 = 0,
-  ULYSSES_DTYPE_BF16 = 1
+  ULYSSES_DTYPE_BF16 = 1,
+  ULYSSES_DTYPE_MAX_ENUM = 0x7fffffff
 } ulysses_dtype_t;
 
 /* Version of this ABI (incremented on any incompatible change). */

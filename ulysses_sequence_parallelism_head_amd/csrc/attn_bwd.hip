@@ -860,33 +860,6 @@ hipError_t launch_bwd_d(const BwdParams& p, bool has_mask, bool o_f32, hipStream
 
 }  // namespace
 
-namespace {
-// one float32 [B][Hq][n] array, rounded up to 256 bytes
-size_t row_array_bytes(int32_t B, int64_t n, int32_t Hq) {
-  const size_t bytes = size_t(B) * size_t(n) * size_t(Hq) * sizeof(float);
-  return (bytes + 255) / 256 * 256;
-}
-}  // namespace
-
-// Workgroups per key-block pair of the dK/dV pass: enough that short
-// sequences still give the 256 CUs about two workgroups each (one resident
-// per CU).  A function of the shape only, so the result of a call does not
-// depend on the device or the workspace handed in.
-int attn_bwd_nsplit(int32_t B, int64_t n, int32_t Hkv) {
-  const int64_t pairs = ((n + 127) / 128 + 1) / 2 * int64_t(Hkv) * B;
-  int s = 1;
-  while (s < 8 && pairs * s < 384) s *= 2;   // a power of two, at most 8
-  return s;
-}
-
-// Dl = dO . O, then the base-2 logsumexp; with several splits, their
-// partial dK and dV
-size_t attn_bwd_workspace_bytes(int32_t B, int64_t n, int32_t Hq, int32_t Hkv, int32_t D, int nsplit) {
-  size_t bytes = 2 * row_array_bytes(B, n, Hq);
-  if (nsplit > 1) bytes += 2 * size_t(nsplit) * size_t(B) * size_t(n) * size_t(Hkv) * size_t(D) * sizeof(float);
-  return bytes;
-}
-
 hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const uint8_t* valid,
                                 const int32_t* doc_start, const void* o, const float* lse, const void* dout,
                                 float* dq, float* dk, float* dv, float* workspace, const AttnShape& s, int o_f32,
@@ -903,13 +876,14 @@ hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, con
   p.dq = dq;
   p.dk = dk;
   p.dv = dv;
-  p.rowdot = workspace;
-  p.lse2 = workspace + row_array_bytes(s.B, s.n, s.Hq) / sizeof(float);
   p.nsplit = nsplit < 1 ? 1 : nsplit;
   p.lsplit = 0;
   while ((1 << p.lsplit) < p.nsplit) ++p.lsplit;
-  p.dk_part = p.lse2 + row_array_bytes(s.B, s.n, s.Hq) / sizeof(float);
-  p.dv_part = p.dk_part + size_t(p.nsplit) * size_t(s.B) * size_t(s.n) * size_t(s.Hkv) * size_t(s.D);
+  const BwdWorkspace ws = attn_bwd_workspace(s.B, s.n, s.Hq, s.Hkv, s.D, p.nsplit);
+  p.rowdot = workspace + ws.rowdot;
+  p.lse2 = workspace + ws.lse2;
+  p.dk_part = workspace + ws.dk_part;
+  p.dv_part = workspace + ws.dv_part;
   p.B = s.B;
   p.n = int32_t(s.n);
   p.Hq = s.Hq;

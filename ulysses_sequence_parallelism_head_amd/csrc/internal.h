@@ -54,6 +54,12 @@ hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, con
 
 // workgroups per key-block pair of the dK/dV pass for this shape
 int attn_bwd_nsplit(int32_t B, int64_t n, int32_t Hkv);
+// where each array of the backward's workspace lives (offsets in floats)
+struct BwdWorkspace {
+  size_t rowdot, lse2, dk_part, dv_part;
+  size_t bytes;   // total
+};
+BwdWorkspace attn_bwd_workspace(int32_t B, int64_t n, int32_t Hq, int32_t Hkv, int32_t D, int nsplit);
 size_t attn_bwd_workspace_bytes(int32_t B, int64_t n, int32_t Hq, int32_t Hkv, int32_t D, int nsplit);
 
 // seq2head fused with the rotary embedding at global positions; elem_bytes
