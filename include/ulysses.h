@@ -161,7 +161,11 @@ ULYSSES_API ulysses_status_t ulysses_repack_head2seq(const void* src, void* dst,
  *
  *   q          [B][n][Hq][D]   in_dtype
  *   k, v       [B][n][Hkv][D]  in_dtype
- *   key_valid  [B][n] uint8 (nonzero = valid key) or NULL (all valid)
+ *   key_valid  [B][n] uint8 (nonzero = valid key) or NULL (all valid).
+ *              A padding key takes no part in any softmax, but its K and V
+ *              rows still enter the matrix products (with weight zero), so
+ *              they must hold finite values (0 * Inf is NaN): zeros, or any
+ *              finite data, are fine.
  *   o          [B][n][Hq][D]   o_dtype             (output)
  *   lse        [B][Hq][n]      float32             (output)
  *

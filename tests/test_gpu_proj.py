@@ -83,8 +83,11 @@ def test_out_proj(P, B, nl, Hq, D, hidden):
 
 def test_proj_64k_sampled():
     """The 64K workload's shapes: x [4][1][16384][4096], W_qkv [6144][4096],
-    W_o [4096][4096]; Q/K/V and the output projection of the projected Q
-    (as a stand-in attention output) on sampled tokens."""
+    W_o [4096][4096]; Q, K, V and the output projection of the projected Q
+    (as a stand-in attention output) at sampled local positions of every
+    shard, against the oracle run on those positions (the same local
+    positions of each shard, so the oracle's exchange places them exactly
+    as the full one would)."""
     say("projections at the 64K workload, sampled tokens")
     w3 = synth.WORKLOADS[3]
     P, nl, D, Hq, Hkv = w3.P, w3.n_local, w3.D, w3.Hq_global, w3.Hkv_global
@@ -96,21 +99,19 @@ def test_proj_64k_sampled():
     q, k, v = U.ulysses_qkv_proj_seq2head(bits_to_device(x), bits_to_device(w), Hq, Hkv, D)
     y = U.ulysses_head2seq_out_proj(q, bits_to_device(w_o))
     torch.cuda.synchronize()
-    tok = synth.sample_rows(g[synth.STREAM_ROWS], P * nl, 24, extra=(0, nl - 1, nl, P * nl - 1))
-    i, s = tok // nl, tok % nl
-    xf, wf = to_f64(x[i, 0, s]), to_f64(w)                  # [R][hidden]
-    ref = xf @ wf.T
-    ab = np.abs(xf) @ np.abs(wf).T
-    qg = to_host_f64(q)                                     # [P][1][n][Hq/P][D]
-    hp = Hq // P
-    got_q = qg[:, 0, tok].transpose(1, 0, 2, 3).reshape(len(tok), Hq * D)
-    _check("Q rows", got_q, ref[:, :Hq * D], ab[:, :Hq * D], hidden)
-    kg = to_host_f64(k)
-    got_k = kg[:, 0, tok].transpose(1, 0, 2, 3).reshape(len(tok), Hkv * D)
-    _check("K rows", got_k, ref[:, Hq * D:(Hq + Hkv) * D], ab[:, Hq * D:(Hq + Hkv) * D], hidden)
-    # output projection of the (bf16) projected Q at the same tokens
-    qrow = got_q                                            # the GPU's bf16 Q, exactly
-    yref = qrow @ to_f64(w_o).T
-    yab = np.abs(qrow) @ np.abs(to_f64(w_o)).T
-    _check("Y rows", to_host_f64(y)[i, 0, s], yref, yab, Hq * D)
-    assert hp * P == Hq
+    loc = synth.sample_rows(g[synth.STREAM_ROWS], nl, 6, extra=(0, 1, 255, 256, nl - 1))   # local positions
+    R = loc.size
+    xs = x[:, :, loc]                                        # [P][1][R][hidden]: the same positions of every shard
+    xf, wf = to_f64(xs), to_f64(w)
+    rq, rk, rv = oracle.proj.qkv_proj_seq2head(xf, wf, Hq, Hkv, D)      # [P][1][P*R][H/P][D]
+    aq, ak, av = oracle.proj.qkv_proj_seq2head(np.abs(xf), np.abs(wf), Hq, Hkv, D)
+    glob = (np.arange(P)[:, None] * nl + loc[None, :]).reshape(-1)     # shard-major, as the exchange orders them
+    gi = torch.from_numpy(glob).to(q.device)
+    for name, got_t, ref, ab in (("Q", q, rq, aq), ("K", k, rk, ak), ("V", v, rv, av)):
+        _check(f"{name} rows", to_host_f64(got_t[:, :, gi]), ref, ab, hidden)
+    # output projection of the GPU's (bf16) projected Q at the same tokens
+    o_s = to_host_f64(q[:, :, gi])                            # [P][1][P*R][Hq/P][D]
+    yref = oracle.proj.head2seq_out_proj(o_s, to_f64(w_o))    # [P][1][R][hidden]
+    yab = oracle.proj.head2seq_out_proj(np.abs(o_s), np.abs(to_f64(w_o)))
+    _check("Y rows", to_host_f64(y[:, :, torch.from_numpy(loc).to(y.device)]), yref, yab, Hq * D)
+    assert R >= 8

@@ -26,6 +26,37 @@ def test_scanner_flags_unskipped_mfma():
     assert len(bad) == 1 and bad[0][1] == 4
 
 
+def test_scanner_follows_fall_through_and_scalar_branches():
+    """An MFMA reached through a labelled fall-through block, a branch on
+    SCC, an unconditional branch, or the taken side of s_cbranch_execz is
+    flagged; one behind s_cbranch_execz's fall-through or after the EXEC
+    restore is not."""
+    asm = "\n".join([
+        "kern:",
+        "\ts_and_saveexec_b64 s[0:1], vcc",               # 2
+        "\ts_cmp_eq_u32 s4, 0",
+        "\ts_cbranch_scc1 .LBB0_3",                        # 4: both ways
+        ".LBB0_1:",                                        # fall-through into a label
+        "\tv_mfma_f32_32x32x16_bf16 v[0:15], v[16:19], v[20:23], v[0:15]",   # 6: flagged
+        "\ts_branch .LBB0_4",
+        ".LBB0_3:",
+        "\tv_mfma_f32_32x32x16_bf16 v[0:15], v[16:19], v[20:23], v[0:15]",   # 9: flagged (SCC taken)
+        ".LBB0_4:",
+        "\ts_or_b64 exec, exec, s[0:1]",
+        "\tv_mfma_f32_32x32x16_bf16 v[0:15], v[16:19], v[20:23], v[0:15]",   # 12: EXEC restored
+        "\ts_and_saveexec_b64 s[2:3], vcc",
+        "\ts_cbranch_execz .LBB0_6",
+        "\tv_mfma_f32_32x32x16_bf16 v[0:15], v[16:19], v[20:23], v[0:15]",   # 15: EXEC non-empty here
+        "\ts_or_b64 exec, exec, s[2:3]",
+        "\ts_endpgm",
+        ".LBB0_6:",
+        "\tv_mfma_f32_32x32x16_bf16 v[0:15], v[16:19], v[20:23], v[0:15]",   # 19: flagged (EXEC empty)
+        "\ts_or_b64 exec, exec, s[2:3]",
+        "\ts_endpgm",
+    ])
+    assert [b[1] for b in isa_check.scan(asm)] == [6, 9, 19]
+
+
 def test_scratch_parser():
     asm = "\n".join([
         "\t.amdhsa_kernel kern_a",
