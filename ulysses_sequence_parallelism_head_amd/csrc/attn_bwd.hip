@@ -13,17 +13,19 @@
 //
 // Three kernels:
 //  1. rowdot: Dl[b][h][t] = dO . O per query row (float32 workspace).
-//  2. dkdv (KV-stationary): a workgroup of 4 waves owns 128 keys of one KV
-//     head (32 per wave, K and V held in registers) and streams the 64-row
+//  2. dkdv (KV-stationary): a workgroup of 8 waves owns 128 keys of one KV
+//     head (4 groups of 32 keys, two waves per group) and streams the 64-row
 //     query tiles of every query head of the group that can see them (for
 //     causal attention, two key blocks in turn, ordered so that resident
-//     workgroups read the same tiles at the same time).  It
-//     computes S = Q K^T and dP = dO V^T with the key on the lane (so P and dS
-//     come out as MFMA B operands) and accumulates dV^T += dO^T P and
-//     dK^T += Q^T dS.  Q and dO are staged once, row-major with swizzled
+//     workgroups read the same tiles at the same time).  In each group one
+//     wave holds the K rows and computes S = Q K^T, P and dV^T += dO^T P, the
+//     other holds the V rows and computes dP = dO V^T, dS and dK^T += Q^T dS,
+//     receiving P through LDS; the key is on the lane, so P and dS come out
+//     as MFMA B operands.  Q and dO are staged once, row-major with swizzled
 //     chunks; the Q^T and dO^T operands come from transposing LDS reads
-//     (ds_read_b64_tr_b16).  One wave per SIMD: 512 registers hold the K/V
-//     rows, both accumulators and two 32-row blocks in flight without spills.
+//     (ds_read_b64_tr_b16).  Splitting a group's work over two waves halves
+//     each wave's registers, so two waves share a SIMD and one's
+//     exponentials and waits overlap the other's matrix work.
 //  3. dq (Q-stationary, laid out like the forward): recomputes S^T = K Q^T and
 //     dP^T = V dO^T with the query on the lane and accumulates
 //     dQ^T += K^T dS^T, the K^T operand read transposed from the row-major K
@@ -127,40 +129,6 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const BwdParams p) {
 }
 
 // ------------------------------------------------------------------- dkdv
-template <int D, bool DOCS>
-struct DkdvLayout {
-  static constexpr int kRows = 64;                        // query rows per tile
-  static constexpr int kRowBytes = 2 * D;
-  static constexpr int kChunks = D / 8;
-  static constexpr int kBytesRM = kRows * kRowBytes;
-  static constexpr int kOffQ = 0;
-  static constexpr int kOffDO = kOffQ + kBytesRM;
-  static constexpr int kOffLSE = kOffDO + kBytesRM;
-  static constexpr int kOffDL = kOffLSE + kRows * 4;
-  static constexpr int kOffLO = kOffDL + kRows * 4;       // document bounds of the rows (DOCS)
-  static constexpr int kStage = kOffLO + (DOCS ? kRows * 4 : 0);
-  static constexpr int kStageAligned = (kStage + 127) / 128 * 128;
-};
-
-// DMA the query tile t0 .. t0+63 of query head `head`: Q and dO rows into the
-// swizzled row-major tiles, the base-2 logsumexp and Dl values (and with
-// documents the rows' bounds) into arrays of 64 (rows past n read as zero).
-template <int D, bool DOCS>
-__device__ __forceinline__ void dkdv_issue(uint8_t* stage, const BwdParams& p, int b, int head, int t0, int wave,
-                                           int lane) {
-  using L = DkdvLayout<D, DOCS>;
-  const int rows_ok = min(L::kRows, p.n - t0);
-  const int64_t off = ((int64_t(b) * p.n + t0) * p.Hq + head) * D;
-  const int stride = p.Hq * D * 2;
-  dma_tile<D, L::kRows, kWaves>(stage + L::kOffQ, p.q + off, stride, rows_ok, wave, lane);
-  dma_tile<D, L::kRows, kWaves>(stage + L::kOffDO, p.dout + off, stride, rows_ok, wave, lane);
-  const int64_t roff = (int64_t(b) * p.Hq + head) * p.n + t0;
-  if (wave == 0) dma4(buffer_rsrc(p.lse2 + roff, uint32_t(rows_ok) * 4u), stage + L::kOffLSE, lane * 4);
-  if (wave == 1) dma4(buffer_rsrc(p.rowdot + roff, uint32_t(rows_ok) * 4u), stage + L::kOffDL, lane * 4);
-  if (DOCS && wave == 2)
-    dma4(buffer_rsrc(p.doc_start + int64_t(b) * p.n + t0, uint32_t(rows_ok) * 4u), stage + L::kOffLO, lane * 4);
-}
-
 // Pack 8 floats (x[0..7]) as the bf16 B operand of one MFMA, and optionally
 // the bf16 residual x - bf16(x) as a second operand.
 __device__ __forceinline__ u32x4 pack8(const float* x) {
@@ -175,74 +143,6 @@ __device__ __forceinline__ u32x4 pack8_residual(const float* x, const u32x4 hi) 
     r[2 * e + 1] = x[2 * e + 1] - bf16hi_to_f32(hi[e]);
   }
   return pack8(r);
-}
-
-// One 32-row block of a staged query tile against this wave's 32 keys, after
-// S and dP are in registers: P, dS, then dV^T += dO^T P and dK^T += Q^T dS.
-// SPLIT adds the bf16 residuals of P and dS as second MFMAs.  DIAG applies
-// the causal mask (only tiles that reach above the block's last key need
-// it).  LOWER applies the rows' document bounds (key u is visible to row t
-// only if u >= bound).
-template <int D, bool DOCS, bool CAUSAL, bool SPLIT, bool DIAG, bool LOWER>
-__device__ __forceinline__ void dkdv_rows(const uint8_t* qs, const uint8_t* dos, const float* lses, const float* dls,
-                                          const int32_t* los, const f32x16& s, const f32x16& dp, int rb, int t0, int u,
-                                          int hh, int lane, float c, f32x16 (&dka)[D / 32],
-                                          f32x16 (&dva)[D / 32]) {
-  using L = DkdvLayout<D, DOCS>;
-  constexpr int DJ = D / 32;
-  float pr[16], ds[16];
-  // element i is query row t0 + 4hh + C_i (C_i = rb*32 + (i/4)*8 + i%4, a
-  // compile-time constant); the key is visible iff u <= row, i.e. C_i >= lim
-  const int lim = (CAUSAL && DIAG) ? u - t0 - 4 * hh : -0x7fffffff;
-#pragma unroll
-  for (int g4 = 0; g4 < 4; ++g4) {
-    const int rr = rb * 32 + g4 * 8 + hh * 4;
-    const f32x4 l4 = *reinterpret_cast<const f32x4*>(lses + rr);
-    const f32x4 d4 = *reinterpret_cast<const f32x4*>(dls + rr);
-    i32x4 b4 = i32x4{0, 0, 0, 0};
-    if (LOWER) b4 = *reinterpret_cast<const i32x4*>(los + rr);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = g4 * 4 + e;
-      const int ci = rb * 32 + g4 * 8 + e;
-      const bool ok = (!(CAUSAL && DIAG) || ci >= lim) && (!LOWER || b4[e] <= u);
-      // invisible keys, and rows with no visible key (base-2 LSE = +inf), get
-      // exponent -inf: exp2(-inf) = 0 exactly.  A key that is padding or past
-      // n is not masked here: its P and dS reach only its own column of dV^T
-      // and dK^T (the lane's key), which the epilogue writes as zero.
-      const float x = ok ? fmaf(s[i], c, -l4[e]) : -INFINITY;
-      const float pv = __builtin_amdgcn_exp2f(x);
-      pr[i] = pv;
-      ds[i] = pv * (dp[i] - d4[e]);
-    }
-  }
-  u32x4 ph[2], pl[2], dh[2], dl[2];
-#pragma unroll
-  for (int f = 0; f < 2; ++f) {
-    ph[f] = pack8(pr + 8 * f);
-    dh[f] = pack8(ds + 8 * f);
-    if (SPLIT) {
-      pl[f] = pack8_residual(pr + 8 * f, ph[f]);
-      dl[f] = pack8_residual(ds + 8 * f, dh[f]);
-    }
-  }
-  // dV^T += dO^T P,  dK^T += Q^T dS   (A operands read transposed from the row-major tiles)
-#pragma unroll
-  for (int f = 0; f < 2; ++f) {
-#pragma unroll
-    for (int j = 0; j < DJ; ++j) {
-      // (the document variants take the folded row offset: with their extra
-      // live values the row-wise form spills)
-      const u32x4 adt = DOCS ? tr_operand<L::kRowBytes>(dos, rb * 32 + 16 * f, 32 * j, lane)
-                             : tr_operand_rows<L::kRowBytes>(dos, rb * 32 + 16 * f, 32 * j, lane);
-      dva[j] = mfma32x32x16(adt, ph[f], dva[j]);
-      if (SPLIT) dva[j] = mfma32x32x16(adt, pl[f], dva[j]);
-      const u32x4 aqt = DOCS ? tr_operand<L::kRowBytes>(qs, rb * 32 + 16 * f, 32 * j, lane)
-                             : tr_operand_rows<L::kRowBytes>(qs, rb * 32 + 16 * f, 32 * j, lane);
-      dka[j] = mfma32x32x16(aqt, dh[f], dka[j]);
-      if (SPLIT) dka[j] = mfma32x32x16(aqt, dl[f], dka[j]);
-    }
-  }
 }
 
 // End (exclusive) of the rows that can see key `klast`: the first row t >
@@ -294,6 +194,135 @@ __device__ __forceinline__ int docs_partner(const int32_t* rs, int kb, int n, in
   return (q0 == r0 && q1 == r1) ? partner : kb;
 }
 
+// Sum of the splits' partial dK (or dV) in split order: out[i] = sum_s part[s][i]
+// (a fixed order, so the result does not depend on scheduling).
+__global__ __launch_bounds__(256) void dkdv_reduce_kernel(const float* part, float* out, int64_t count, int32_t nsplit) {
+  const int64_t i = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (i >= count) return;
+  f32x4 acc = *reinterpret_cast<const f32x4*>(part + i);
+  for (int32_t sp = 1; sp < nsplit; ++sp) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(part + sp * count + i);
+    acc = f32x4{acc[0] + x[0], acc[1] + x[1], acc[2] + x[2], acc[3] + x[3]};
+  }
+  *reinterpret_cast<f32x4*>(out + i) = acc;
+}
+
+// dkdv (KV-stationary): a workgroup of 8 waves owns 128 keys of one KV head
+// as 4 groups of 32, two waves per group on one SIMD.  The P wave holds the
+// group's K rows and computes S = Q K^T, P and dV^T += dO^T P; the dS wave
+// holds the V rows and computes dP = dO V^T, dS = P (dP - Dl) and
+// dK^T += Q^T dS.  Both have the key on the lane, so P and dS come out as
+// MFMA B operands, and P passes from one wave to the other through LDS, lane
+// to the same lane, in float32.  Each wave keeps one accumulator set and one
+// operand set, so two waves fit on a SIMD (256 registers each), and one
+// wave's exponentials, operand reads and waits overlap the other wave's
+// matrix work.  Q and dO are staged once per unit, row-major with swizzled
+// chunks; the Q^T and dO^T operands come from transposing LDS reads.
+constexpr int kPairWaves = 8;
+constexpr int kPairThreads = kPairWaves * 64;
+constexpr int kRowAhead = 6;  // row-major operands read ahead of their MFMAs
+constexpr int kTrAhead = 3;   // transposed operands read ahead of their MFMAs
+
+template <int D, bool DOCS>
+struct DkdvPairLayout {
+  static constexpr int kRows = 64;                         // query rows per unit
+  static constexpr int kRowBytes = 2 * D;
+  static constexpr int kTile = kRows * kRowBytes;          // one bf16 row-major tile
+  // a stage: Q, dO, the base-2 logsumexp, Dl and (documents) the rows' bounds
+  static constexpr int kSQ = 0;
+  static constexpr int kSDO = kTile;
+  static constexpr int kSLSE = 2 * kTile;
+  static constexpr int kSDL = kSLSE + kRows * 4;
+  static constexpr int kSLO = kSDL + kRows * 4;
+  static constexpr int kStage = (kSLO + (DOCS ? kRows * 4 : 0) + 127) / 128 * 128;
+  // two stages, then P of the 4 key groups: 64 lanes x 32 floats (two 32-row blocks) each
+  static constexpr int kOffX = 2 * kStage;
+  static constexpr int kXGroup = 64 * 32 * 4;
+  static constexpr int kBytes = kOffX + 4 * kXGroup;
+};
+
+// DMA unit tile t0 .. t0+63 of query head `head` for the two-wave kernel: Q,
+// dO, the base-2 logsumexp, Dl (and the rows' bounds) into stage `st` (rows
+// past n read as zero).  All eight waves take part.
+template <int D, bool DOCS>
+__device__ __forceinline__ void dkdv_pair_issue(uint8_t* st, const BwdParams& p, int b, int head, int t0, int wave,
+                                                int lane) {
+  using X = DkdvPairLayout<D, DOCS>;
+  const int rows_ok = min(X::kRows, p.n - t0);
+  const int64_t off = ((int64_t(b) * p.n + t0) * p.Hq + head) * D;
+  const int stride = p.Hq * D * 2;
+  dma_tile<D, X::kRows, kPairWaves>(st + X::kSQ, p.q + off, stride, rows_ok, wave, lane);
+  dma_tile<D, X::kRows, kPairWaves>(st + X::kSDO, p.dout + off, stride, rows_ok, wave, lane);
+  const int64_t roff = (int64_t(b) * p.Hq + head) * p.n + t0;
+  if (wave == 0) dma4(buffer_rsrc(p.lse2 + roff, uint32_t(rows_ok) * 4u), st + X::kSLSE, lane * 4);
+  if (wave == 1) dma4(buffer_rsrc(p.rowdot + roff, uint32_t(rows_ok) * 4u), st + X::kSDL, lane * 4);
+  if (DOCS && wave == 2)
+    dma4(buffer_rsrc(p.doc_start + int64_t(b) * p.n + t0, uint32_t(rows_ok) * 4u), st + X::kSLO, lane * 4);
+}
+
+// Software pipeline of N matrix-core steps that each take one A operand
+// from LDS: the operands of the first AH steps are read first, then step t
+// issues its MFMAs together with the read for step t + AH, and a scheduling
+// fence after every step keeps that order (the compiler's latency model
+// takes LDS reads as short and would otherwise read each operand just
+// before its MFMA).  `before` runs between the first reads and the first
+// step.
+template <int AH, int N, typename Load, typename Before, typename Step>
+__device__ __forceinline__ void lds_pipeline(Load&& load, Before&& before, Step&& step) {
+  static_assert(AH >= 1 && AH <= N, "read-ahead within the steps");
+  u32x4 win[AH];
+#pragma unroll
+  for (int t = 0; t < AH; ++t) win[t] = load(t);
+  __builtin_amdgcn_sched_barrier(0);
+  before();
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int t = 0; t < N; ++t) {
+    const u32x4 a = win[t % AH];
+    if (t + AH < N) win[t % AH] = load(t + AH);
+    step(t, a);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// The lane index from an instruction the compiler cannot merge or move:
+// values derived from it are computed where they are used, not hoisted
+// above branches and loops where they would hold registers throughout.
+__device__ __forceinline__ int opaque_lane_id() {
+  int lane;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+  return lane;
+}
+
+// P of one 32-row block of the staged tile (rows rb*32 + (i/4)*8 + 4hh + i%4,
+// key u on the lane) from the scores s.  DIAG applies the causal mask (only
+// tiles that reach above the block's last key need it), LOWER the rows'
+// document bounds (key u is visible to row t only if u >= bound).  Invisible
+// keys, and rows with no visible key (base-2 LSE = +inf), get exponent -inf:
+// exp2(-inf) = 0 exactly.  A key that is padding or past n is not masked
+// here: its P and dS reach only its own column of dV^T and dK^T (the lane's
+// key), which the epilogue writes as zero.
+template <bool CAUSAL, bool DIAG, bool LOWER>
+__device__ __forceinline__ void dkdv_probs(const float* lses, const int32_t* los, const f32x16& s, int rb, int t0,
+                                           int u, int hh, float c, float (&pr)[16]) {
+  const int lim = (CAUSAL && DIAG) ? u - t0 - 4 * hh : -0x7fffffff;
+#pragma unroll
+  for (int g4 = 0; g4 < 4; ++g4) {
+    const int rr = rb * 32 + g4 * 8 + hh * 4;
+    const f32x4 l4 = *reinterpret_cast<const f32x4*>(lses + rr);
+    i32x4 b4 = i32x4{0, 0, 0, 0};
+    if (LOWER) b4 = *reinterpret_cast<const i32x4*>(los + rr);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = g4 * 4 + e;
+      const int ci = rb * 32 + g4 * 8 + e;
+      const bool ok = (!(CAUSAL && DIAG) || ci >= lim) && (!LOWER || b4[e] <= u);
+      const float x = ok ? fmaf(s[i], c, -l4[e]) : -INFINITY;
+      pr[i] = __builtin_amdgcn_exp2f(x);
+    }
+  }
+}
+
 // Work items and tile order.  A work item is one key block (non-causal) or,
 // for causal attention, the pair of key blocks (nkb-1-w, w): the first one
 // sweeps the query tiles from the last down to its diagonal, the second from
@@ -310,21 +339,20 @@ __device__ __forceinline__ int docs_partner(const int32_t* rs, int kb, int n, in
 // of the earlier block does the pair; the later block's exits at once.
 // Which blocks form a run is read from the bounds (see docs_partner below).
 template <int D, bool HAS_MASK, bool CAUSAL, bool DOCS>
-__global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdParams p) {
+__global__ __launch_bounds__(kPairThreads, 1) void dkdv_pair_kernel(const BwdParams p) {
   static_assert(CAUSAL || !DOCS, "documents are causal");
-  using L = DkdvLayout<D, DOCS>;
+  using X = DkdvPairLayout<D, DOCS>;
   constexpr int KK = D / 16;
   constexpr int DJ = D / 32;
-  constexpr int kKeys = 128;                      // keys per workgroup (4 waves x 32)
-  __shared__ __attribute__((aligned(128))) uint8_t smem[2 * L::kStageAligned];
+  constexpr int kKeys = 128;                      // keys per workgroup (4 groups x 32)
+  __shared__ __attribute__((aligned(128))) uint8_t smem[X::kBytes];
 
   const int tid = threadIdx.x;
-  // wave index as a scalar: every branch that guards a matrix-core instruction
-  // must be wave-uniform to the compiler (MFMA does not honour EXEC)
+  // scalar wave index: every branch around a matrix-core instruction is wave-uniform
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-  const int l32 = lane & 31;
-  const int hh = lane >> 5;
+  const int kw = wave & 3;                        // key group; waves kw and kw + 4 share it
+  const int lane0 = tid & 63;
+  float* xp = reinterpret_cast<float*>(smem + X::kOffX + kw * X::kXGroup);
 
   // block -> (split, work item, kv head, batch); split fastest, then kv head
   const int sp = int(blockIdx.x) & (p.nsplit - 1);
@@ -334,211 +362,247 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdParams p) {
   const int rem = bid % per_w;
   const int b = rem / p.Hkv;
   const int kvh = rem % p.Hkv;
-  const int ntq = (p.n + L::kRows - 1) / L::kRows;   // query tiles per head
+  const int ntq = (p.n + X::kRows - 1) / X::kRows;
   int nph = (CAUSAL && p.n_kblocks - 1 - w != w) ? 2 : 1;
-  int kb_first = p.n_kblocks - 1 - w;   // the block of the first phase (the pair's later block)
+  int kb_first = p.n_kblocks - 1 - w;
   if (DOCS) {
-    kb_first = docs_partner(p.doc_start + int64_t(b) * p.n, w, p.n, p.n_kblocks, lane);
-    if (kb_first < w) return;           // the partner's workgroup does this pair (uniform: no barrier passed yet)
+    kb_first = docs_partner(p.doc_start + int64_t(b) * p.n, w, p.n, p.n_kblocks, lane0);
+    if (kb_first < w) return;           // uniform across the workgroup: no barrier passed yet
     nph = kb_first == w ? 1 : 2;
   }
 
-  for (int ph = 0; ph < nph; ++ph) {
-    // causal: the first phase (the later block, or a block alone) sweeps down, the second up
-    const bool down = CAUSAL && ph == 0;
-    const int kb = down ? kb_first : w;
-    const int k0w = kb * kKeys + wave * 32;        // first key of this wave
-    const int u = k0w + l32;                       // this lane's key
-    const bool wave_live = k0w < p.n;
+  // the whole sweep of one role; the two roles run the same units and meet
+  // at the same barriers
+  auto go = [&](auto role_tag) __attribute__((always_inline)) {
+    constexpr bool PW = decltype(role_tag)::value;   // P wave (else dS wave)
+    // (per role: derived values are not kept live through the other role's loops)
+    const int lane = opaque_lane_id();
+    const int l32 = lane & 31;
+    const int hh = lane >> 5;
+    for (int ph = 0; ph < nph; ++ph) {
+      const bool down = CAUSAL && ph == 0;
+      const int kb = down ? kb_first : w;
+      const int k0w = kb * kKeys + kw * 32;
+      const int u = k0w + l32;
+      const bool wave_live = k0w < p.n;
 
-    // K and V rows of this lane's key as the B operands of S = Q K^T, dP = dO V^T
-    u32x4 kf[KK], vf[KK];
-    bool key_ok = u < p.n;
-    {
-      const int64_t off = ((int64_t(b) * p.n + (key_ok ? u : 0)) * p.Hkv + kvh) * D + 8 * hh;
+      // K rows (P wave) or V rows (dS wave) of this lane's key as B operands
+      u32x4 kv[KK];
+      bool key_ok = u < p.n;
+      {
+        const uint16_t* src = PW ? p.k : p.v;
+        const int64_t off = ((int64_t(b) * p.n + (key_ok ? u : 0)) * p.Hkv + kvh) * D + 8 * hh;
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        kf[kk] = key_ok ? *reinterpret_cast<const u32x4*>(p.k + off + 16 * kk) : u32x4{0, 0, 0, 0};
-        vf[kk] = key_ok ? *reinterpret_cast<const u32x4*>(p.v + off + 16 * kk) : u32x4{0, 0, 0, 0};
+        for (int kk = 0; kk < KK; ++kk)
+          kv[kk] = key_ok ? *reinterpret_cast<const u32x4*>(src + off + 16 * kk) : u32x4{0, 0, 0, 0};
+        if (HAS_MASK && key_ok) key_ok = p.valid[int64_t(b) * p.n + u] != 0;
       }
-      if (HAS_MASK && key_ok) key_ok = p.valid[int64_t(b) * p.n + u] != 0;
-    }
-
-    f32x16 dka[DJ], dva[DJ];
+      f32x16 acc[DJ];                    // dV^T (P wave) or dK^T (dS wave)
 #pragma unroll
-    for (int j = 0; j < DJ; ++j) {
-      dka[j] = f32x16{};
-      dva[j] = f32x16{};
-    }
+      for (int j = 0; j < DJ; ++j) acc[j] = f32x16{};
 
-    // query tiles tfirst .. tend-1 hold every row that can see the block's
-    // keys.  Rows from split_end on see at least kSplitRows keys.  With
-    // documents, the rows that see the keys end at rend (the end of the last
-    // document holding one of them), and the per-row lower mask is needed if
-    // any visited row -- up to the end of the last tile, past rend -- has its
-    // bound above the block's first key.
-    const int tfirst = CAUSAL ? (kb * kKeys) / L::kRows : 0;
-    int tend = ntq;
-    int split_end = kSplitRows;
-    bool lower = false;
-    if (DOCS) {
-      const int32_t* rs = p.doc_start + int64_t(b) * p.n;
-      const int kfirst = kb * kKeys;
-      const int klast = min(kfirst + kKeys, p.n) - 1;
-      const int rend = doc_rows_end(rs, klast, p.n, lane);
-      tend = (rend + L::kRows - 1) / L::kRows;
-      split_end = doc_lower(rs, rend - 1) + kSplitRows;
-      lower = doc_lower(rs, min(tend * L::kRows, p.n) - 1) > kfirst;
-    }
-    const int niter = (tend - tfirst) * p.g;
-    // unit it -> (tile, head of the group)
-    auto tile_of = [&](int it) { return down ? tend - 1 - it / p.g : tfirst + it / p.g; };
-    // this split's units [u0, u1): the block's units cut into nsplit equal
-    // runs (wave-uniform scalars: they bound the loops around the MFMAs)
-    const int u0 = __builtin_amdgcn_readfirstlane((niter * sp) >> p.lsplit);
-    const int u1 = __builtin_amdgcn_readfirstlane((niter * (sp + 1)) >> p.lsplit);
+      const int tfirst = CAUSAL ? (kb * kKeys) / X::kRows : 0;
+      int tend = ntq;
+      int split_end = kSplitRows;
+      bool lower = false;
+      if (DOCS) {
+        const int32_t* rs = p.doc_start + int64_t(b) * p.n;
+        const int kfirst = kb * kKeys;
+        const int klast = min(kfirst + kKeys, p.n) - 1;
+        const int rend = doc_rows_end(rs, klast, p.n, lane);
+        tend = (rend + X::kRows - 1) / X::kRows;
+        split_end = doc_lower(rs, rend - 1) + kSplitRows;
+        lower = doc_lower(rs, min(tend * X::kRows, p.n) - 1) > kfirst;
+      }
+      const int niter = (tend - tfirst) * p.g;
+      auto tile_of = [&](int it) { return down ? tend - 1 - it / p.g : tfirst + it / p.g; };
+      const int u0 = __builtin_amdgcn_readfirstlane((niter * sp) >> p.lsplit);
+      const int u1 = __builtin_amdgcn_readfirstlane((niter * (sp + 1)) >> p.lsplit);
 
-    if (u0 < u1)
-      dkdv_issue<D, DOCS>(smem + (u0 & 1) * L::kStageAligned, p, b, kvh * p.g + u0 % p.g, tile_of(u0) * L::kRows,
-                          wave, lane);
-    wait_vmem();
-    __syncthreads();
+      // unit it's stage: it % 2.  The byte offset passes through an opaque
+      // scalar: the compiler then forms each address where it is used (base
+      // + lane offset + immediate) instead of precomputing one register per
+      // stage and operand ahead of the loops.
+      auto sbuf = [&](int it) {
+        int off = (it & 1) * X::kStage;
+        asm volatile("" : "+s"(off));
+        return smem + off;
+      };
+      if (u0 < u1) dkdv_pair_issue<D, DOCS>(sbuf(u0), p, b, kvh * p.g + u0 % p.g, tile_of(u0) * X::kRows, wave, lane);
+      wait_vmem();
+      __syncthreads();
 
-    // units [it0, it1), all on tiles of one kind: rows below split_end (hi/lo
-    // split) or not, lower mask or not.  Keeping the choice out of the loop
-    // body matters: a branch inside it makes the two sides allocate the 128
-    // dK/dV accumulator registers differently and copy all of them at every
-    // merge.
-    // (forced inline: as a call the wave index would arrive in a vector register)
-    auto run = [&](int it0, int it1, auto split_tag, auto diag_tag, auto lower_tag) __attribute__((always_inline)) {
-      constexpr bool SPLIT = decltype(split_tag)::value;
-      constexpr bool DIAG = decltype(diag_tag)::value;
-      constexpr bool LOWER = decltype(lower_tag)::value;
-      for (int it = it0; it < it1; ++it) {
-        // prefetch unit it+1 into the other buffer while computing on this one
-        uint8_t* cur = smem + (it & 1) * L::kStageAligned;
-        if (it + 1 < u1)
-          dkdv_issue<D, DOCS>(smem + ((it + 1) & 1) * L::kStageAligned, p, b, kvh * p.g + (it + 1) % p.g,
-                              tile_of(it + 1) * L::kRows, wave, lane);
-        const int t0 = tile_of(it) * L::kRows;
-        if (wave_live) {
-          const uint8_t* qs = cur + L::kOffQ;
-          const uint8_t* dos = cur + L::kOffDO;
-          const float* lses = reinterpret_cast<const float*>(cur + L::kOffLSE);
-          const float* dls = reinterpret_cast<const float*>(cur + L::kOffDL);
-          const int32_t* los = reinterpret_cast<const int32_t*>(cur + L::kOffLO);
-          // S[q][key] and dP[q][key] for both 32-row blocks (lane = key, rows
-          // q = rb*32 + (i/4)*8 + 4hh + i%4), then P, dS and the dV/dK products
-          // block by block, all in one basic block so that one block's
-          // exponentials overlap the other block's matrix work.  On a causal
-          // diagonal tile a block may hold no row that sees these keys; it is
-          // computed anyway and masked to exact zeros.
-          f32x16 s[2], dp[2];
+      // Unit it, in two halves separated by a barrier:
+      //   P wave:  S = Q K^T, P, store P | dV^T += dO^T P
+      //   dS wave: dP = dO V^T           | load P, dS, dK^T += Q^T dS
+      // then a barrier before the other stage is refilled and the P slot
+      // rewritten.
+      auto run = [&](int it0, int it1, auto split_tag, auto diag_tag, auto lower_tag) __attribute__((always_inline)) {
+        constexpr bool SPLIT = decltype(split_tag)::value;
+        constexpr bool DIAG = decltype(diag_tag)::value;
+        constexpr bool LOWER = decltype(lower_tag)::value;
+        // P (P wave) or dS (dS wave) as bf16 B operands: hi, and the
+        // residual lo with SPLIT
+        u32x4 bh[2][2], bl[2][2];
+        // the products with transposed A operands from tile `ts` for 32-row
+        // blocks RB0 .. RB0+NRB-1, step t = (rb, f, j) = (RB0 + t / 2DJ,
+        // t / DJ % 2, t % DJ)
+        auto tr_products = [&](const uint8_t* ts, auto rb0_tag, auto nrb_tag) __attribute__((always_inline)) {
+          constexpr int RB0 = decltype(rb0_tag)::value;
+          constexpr int NRB = decltype(nrb_tag)::value;
+          lds_pipeline<SPLIT ? kTrAhead - 1 : kTrAhead, NRB * 2 * DJ>(
+              [&](int t) {
+                return tr_operand<X::kRowBytes>(ts, (RB0 + t / (2 * DJ)) * 32 + 16 * (t / DJ % 2), 32 * (t % DJ),
+                                                lane);
+              },
+              [] {},
+              [&](int t, const u32x4 a) {
+                acc[t % DJ] = mfma32x32x16(a, bh[RB0 + t / (2 * DJ)][t / DJ % 2], acc[t % DJ]);
+                if (SPLIT) acc[t % DJ] = mfma32x32x16(a, bl[RB0 + t / (2 * DJ)][t / DJ % 2], acc[t % DJ]);
+              });
+        };
+        // unit it's tile, and the next unit's tile and head, advanced by
+        // additions (wave-uniform scalars)
+        int tile = tile_of(it0);
+        int ntile = tile_of(it0 + 1), nhead = (it0 + 1) % p.g;
+        const int tstep = down ? -1 : 1;
+        for (int it = it0; it < it1; ++it) {
+          if (it + 1 < u1)
+            dkdv_pair_issue<D, DOCS>(sbuf(it + 1), p, b, kvh * p.g + nhead, ntile * X::kRows, wave, lane);
+          const int t0 = tile * X::kRows;
+          const uint8_t* st = sbuf(it);
+          const uint8_t* qs = st + X::kSQ;
+          const uint8_t* dos = st + X::kSDO;
+          f32x16 sc[2];                  // S (P wave) or dP (dS wave)
+          if (wave_live) {
+            // S = Q K^T (P wave) or dP = dO V^T (dS wave); step t = (kk, rb) =
+            // (t / 2, t % 2), A operand row-major from the tile
+            const uint8_t* as = PW ? qs : dos;
 #pragma unroll
-          for (int rb = 0; rb < 2; ++rb) {
-            s[rb] = f32x16{};
-            dp[rb] = f32x16{};
-          }
+            for (int rb = 0; rb < 2; ++rb) sc[rb] = f32x16{};
+            lds_pipeline<DOCS ? kRowAhead - 2 : kRowAhead, 2 * KK>(   // (documents: registers)
+                [&](int t) {
+                  return *reinterpret_cast<const u32x4*>(as + rm_off<X::kRowBytes>((t % 2) * 32 + l32, t + hh - t % 2));
+                },
+                [] {},
+                [&](int t, const u32x4 a) { sc[t % 2] = mfma32x32x16(a, kv[t / 2], sc[t % 2]); });
+            if constexpr (PW) {
+              const float* lses = reinterpret_cast<const float*>(st + X::kSLSE);
+              const int32_t* los = reinterpret_cast<const int32_t*>(st + X::kSLO);
 #pragma unroll
-          for (int kk = 0; kk < KK; ++kk) {
+              for (int rb = 0; rb < 2; ++rb) {
+                float pr[16];
+                dkdv_probs<CAUSAL, DIAG, LOWER>(lses, los, sc[rb], rb, t0, u, hh, p.c, pr);
+                // P to the dS wave: float4 c of block rb at xp[(rb*4 + c)*64 + lane]
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
-              const int off = rm_off<L::kRowBytes>(rb * 32 + l32, 2 * kk + hh);
-              s[rb] = mfma32x32x16(*reinterpret_cast<const u32x4*>(qs + off), kf[kk], s[rb]);
-              dp[rb] = mfma32x32x16(*reinterpret_cast<const u32x4*>(dos + off), vf[kk], dp[rb]);
+                for (int c4 = 0; c4 < 4; ++c4)
+                  *reinterpret_cast<f32x4*>(xp + ((rb * 4 + c4) * 64 + lane) * 4) =
+                      f32x4{pr[4 * c4], pr[4 * c4 + 1], pr[4 * c4 + 2], pr[4 * c4 + 3]};
+#pragma unroll
+                for (int f = 0; f < 2; ++f) {
+                  bh[rb][f] = pack8(pr + 8 * f);
+                  if (SPLIT) bl[rb][f] = pack8_residual(pr + 8 * f, bh[rb][f]);
+                }
+              }
             }
           }
-          // keep three k-steps of operands in flight: LDS latency is several
-          // times one MFMA pair, and this wave is alone on its SIMD
-          pipeline_reads_mfma<6, 4 * KK>();
+          __syncthreads();               // P is in LDS
+          if (wave_live) {
+            if constexpr (PW) {
+              tr_products(dos, std::integral_constant<int, 0>{}, std::integral_constant<int, 2>{});   // dV^T += dO^T P
+            } else {
+              // each block's dS just before its products dK^T += Q^T dS
+              const float* dls = reinterpret_cast<const float*>(st + X::kSDL);
+              auto block = [&](auto rb_tag) __attribute__((always_inline)) {
+                constexpr int rb = decltype(rb_tag)::value;
+                float ds[16];
 #pragma unroll
-          for (int rb = 0; rb < 2; ++rb)
-            dkdv_rows<D, DOCS, CAUSAL, SPLIT, DIAG, LOWER>(qs, dos, lses, dls, los, s[rb], dp[rb], rb, t0, u, hh,
-                                                           lane, p.c, dka, dva);
+                for (int c4 = 0; c4 < 4; ++c4) {
+                  const f32x4 p4 = *reinterpret_cast<const f32x4*>(xp + ((rb * 4 + c4) * 64 + lane) * 4);
+                  const f32x4 d4 = *reinterpret_cast<const f32x4*>(dls + rb * 32 + c4 * 8 + hh * 4);
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) ds[4 * c4 + e] = p4[e] * (sc[rb][4 * c4 + e] - d4[e]);
+                }
+#pragma unroll
+                for (int f = 0; f < 2; ++f) {
+                  bh[rb][f] = pack8(ds + 8 * f);
+                  if (SPLIT) bl[rb][f] = pack8_residual(ds + 8 * f, bh[rb][f]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                tr_products(qs, rb_tag, std::integral_constant<int, 1>{});
+              };
+              block(std::integral_constant<int, 0>{});
+              block(std::integral_constant<int, 1>{});
+            }
+          }
+          wait_vmem();
+          __syncthreads();               // the stage and the P slot are free again
+          tile = ntile;
+          if (++nhead == p.g) {          // unit it+2 starts the next tile
+            nhead = 0;
+            ntile += tstep;
+          }
         }
-        wait_vmem();
-        __syncthreads();
-      }
-    };
-    // tiles below split_end need the split: tfirst .. min(ceil(split_end / kRows), tend) - 1.
-    // The causal mask is needed on the tiles whose first row lies below the
-    // block's last key: tfirst and tfirst + 1 (the block starts a tile and
-    // spans two).  Both ranges sit at the diagonal end of the sweep, so the
-    // units split into at most three runs: both kinds, one kind, neither.
-    const int nsplit = max(0, min((split_end + L::kRows - 1) / L::kRows, tend) - tfirst) * p.g;
-    const int ndiag = CAUSAL ? min(kKeys / L::kRows, tend - tfirst) * p.g : 0;
-    auto sweep = [&](auto lower_tag) __attribute__((always_inline)) {
-      using T = std::true_type;
-      using F = std::false_type;
-      const int n1 = min(nsplit, ndiag), n2 = max(nsplit, ndiag);
-      // runs by distance from the diagonal end: [0, n1) both, [n1, n2) one, [n2, niter) neither
-      // units [x0, x1) of the run, cut to this split's [u0, u1)
-      auto seg = [&](int a, int z, auto split_tag, auto diag_tag) __attribute__((always_inline)) {
-        const int x0 = max(down ? niter - z : a, u0);
-        const int x1 = min(down ? niter - a : z, u1);
-        if (x0 >= x1) return;
-        run(x0, x1, split_tag, diag_tag, lower_tag);
       };
-      if (down) {                       // the diagonal end comes last
-        seg(n2, niter, F{}, F{});
-        if (nsplit > ndiag) seg(n1, n2, T{}, F{});
-        else seg(n1, n2, F{}, T{});
-        seg(0, n1, T{}, T{});
-      } else {                          // the diagonal end comes first
-        seg(0, n1, T{}, T{});
-        if (nsplit > ndiag) seg(n1, n2, T{}, F{});
-        else seg(n1, n2, F{}, T{});
-        seg(n2, niter, F{}, F{});
-      }
-    };
-    if constexpr (DOCS) {
-      if (lower) sweep(std::true_type{});
-      else sweep(std::false_type{});
-    } else {
-      (void)lower;
-      sweep(std::false_type{});
-    }
-
-    // write dK = scale * dK^T^T and dV: lane = key u, dims 32j + 8*(i/4) + 4hh + i%4;
-    // a padding key's gradients are zero (selected, not multiplied: its
-    // unmasked column may hold any value, inf or NaN included).  With
-    // several splits each writes its partial sums, added by dkdv_reduce.
-    float* dk_out = p.dk;
-    float* dv_out = p.dv;
-    if (p.nsplit > 1) {
-      const int64_t part = int64_t(p.B) * p.n * p.Hkv * D;
-      dk_out = p.dk_part + sp * part;
-      dv_out = p.dv_part + sp * part;
-    }
-    if (u < p.n) {
-      const int64_t base = ((int64_t(b) * p.n + u) * p.Hkv + kvh) * D;
-#pragma unroll
-      for (int j = 0; j < DJ; ++j)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int d0 = j * 32 + i4 * 8 + hh * 4;
-          f32x4 kv4 = f32x4{dka[j][i4 * 4] * p.scale, dka[j][i4 * 4 + 1] * p.scale, dka[j][i4 * 4 + 2] * p.scale,
-                            dka[j][i4 * 4 + 3] * p.scale};
-          f32x4 vv4 = f32x4{dva[j][i4 * 4], dva[j][i4 * 4 + 1], dva[j][i4 * 4 + 2], dva[j][i4 * 4 + 3]};
-          if (!key_ok) kv4 = vv4 = f32x4{0.f, 0.f, 0.f, 0.f};
-          *reinterpret_cast<f32x4*>(dk_out + base + d0) = kv4;
-          *reinterpret_cast<f32x4*>(dv_out + base + d0) = vv4;
+      const int nsplit_u = max(0, min((split_end + X::kRows - 1) / X::kRows, tend) - tfirst) * p.g;
+      const int ndiag = CAUSAL ? min(kKeys / X::kRows, tend - tfirst) * p.g : 0;
+      auto sweep = [&](auto lower_tag) __attribute__((always_inline)) {
+        using T = std::true_type;
+        using F = std::false_type;
+        const int n1 = min(nsplit_u, ndiag), n2 = max(nsplit_u, ndiag);
+        auto seg = [&](int a, int z, auto split_tag, auto diag_tag) __attribute__((always_inline)) {
+          const int x0 = max(down ? niter - z : a, u0);
+          const int x1 = min(down ? niter - a : z, u1);
+          if (x0 >= x1) return;
+          run(x0, x1, split_tag, diag_tag, lower_tag);
+        };
+        if (down) {
+          seg(n2, niter, F{}, F{});
+          if (nsplit_u > ndiag) seg(n1, n2, T{}, F{});
+          else seg(n1, n2, F{}, T{});
+          seg(0, n1, T{}, T{});
+        } else {
+          seg(0, n1, T{}, T{});
+          if (nsplit_u > ndiag) seg(n1, n2, T{}, F{});
+          else seg(n1, n2, F{}, T{});
+          seg(n2, niter, F{}, F{});
         }
-    }
-  }
-}
+      };
+      if constexpr (DOCS) {
+        if (lower) sweep(std::true_type{});
+        else sweep(std::false_type{});
+      } else {
+        (void)lower;
+        sweep(std::false_type{});
+      }
 
-// Sum of the splits' partial dK (or dV) in split order: out[i] = sum_s part[s][i]
-// (a fixed order, so the result does not depend on scheduling).
-__global__ __launch_bounds__(256) void dkdv_reduce_kernel(const float* part, float* out, int64_t count, int32_t nsplit) {
-  const int64_t i = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
-  if (i >= count) return;
-  f32x4 acc = *reinterpret_cast<const f32x4*>(part + i);
-  for (int32_t sp = 1; sp < nsplit; ++sp) {
-    const f32x4 x = *reinterpret_cast<const f32x4*>(part + sp * count + i);
-    acc = f32x4{acc[0] + x[0], acc[1] + x[1], acc[2] + x[2], acc[3] + x[3]};
-  }
-  *reinterpret_cast<f32x4*>(out + i) = acc;
+      // dV (P wave) or dK = scale * dK^T^T (dS wave); lane = key u, dims
+      // 32j + 8*(i/4) + 4hh + i%4; a padding key's gradients are zero
+      float* out = PW ? p.dv : p.dk;
+      if (p.nsplit > 1) out = (PW ? p.dv_part : p.dk_part) + sp * (int64_t(p.B) * p.n * p.Hkv * D);
+      const int le = opaque_lane_id();   // (not hoisted out of the phase loop)
+      const int ue = k0w + (le & 31);
+      if (ue < p.n) {
+        const int64_t base = ((int64_t(b) * p.n + ue) * p.Hkv + kvh) * D;
+#pragma unroll
+        for (int j = 0; j < DJ; ++j)
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const int d0 = j * 32 + i4 * 8 + (le >> 5) * 4;
+            f32x4 o4;
+            if constexpr (PW)
+              o4 = f32x4{acc[j][i4 * 4], acc[j][i4 * 4 + 1], acc[j][i4 * 4 + 2], acc[j][i4 * 4 + 3]};
+            else
+              o4 = f32x4{acc[j][i4 * 4] * p.scale, acc[j][i4 * 4 + 1] * p.scale, acc[j][i4 * 4 + 2] * p.scale,
+                         acc[j][i4 * 4 + 3] * p.scale};
+            if (!key_ok) o4 = f32x4{0.f, 0.f, 0.f, 0.f};
+            *reinterpret_cast<f32x4*>(out + base + d0) = o4;
+          }
+      }
+    }
+  };
+  if (wave < 4) go(std::true_type{});
+  else go(std::false_type{});
 }
 
 // --------------------------------------------------------------------- dq
@@ -819,7 +883,7 @@ hipError_t launch_grads(const BwdParams& p, int64_t kv_blocks, int64_t q_blocks,
   hipLaunchKernelGGL((dq_kernel<D, HAS_MASK, CAUSAL, DOCS>), dim3(q_blocks), dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((dkdv_kernel<D, HAS_MASK, CAUSAL, DOCS>), dim3(kv_blocks), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((dkdv_pair_kernel<D, HAS_MASK, CAUSAL, DOCS>), dim3(kv_blocks), dim3(kPairThreads), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess || p.nsplit == 1) return e;
   const int64_t count = int64_t(p.B) * p.n * p.Hkv * D;   // a multiple of 4 (D is)
