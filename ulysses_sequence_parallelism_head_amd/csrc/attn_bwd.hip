@@ -58,6 +58,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kSplitRows = 512;   // a multiple of both query tile heights (64)
+constexpr int kDqSplitBlocks = 512;   // dq grids up to this size take the key split
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct BwdParams {
@@ -716,18 +717,32 @@ __device__ __forceinline__ void dq_half(const uint8_t* ks, const uint8_t* vs, co
   if (!SPLIT) pipeline_tr_reads_mfma<3, 2 * DJ>();
 }
 
-template <int D, bool HAS_MASK, bool CAUSAL, bool DOCS>
-__global__ __launch_bounds__(kThreads, 2) void dq_kernel(const BwdParams p) {
+// KS (key split, 8 waves, plain causal): two groups of 4 waves take the same
+// rows, the first group the first half of their key tiles (rounded up) and
+// the second the rest, each with its own staging buffers; at the end the
+// second group hands its dQ^T accumulators to the first through LDS, which
+// adds them and writes dQ.  On short grids, where every workgroup is
+// resident at once and the longest block (the last rows, which see every
+// key) sets the kernel's time, each block then lasts about half as long.
+// Blocks whose rows see fewer than kSplitRows keys (the hi/lo split and the
+// exact-Dl sweep) stay whole in the first group: they are short anyway.
+template <int D, bool HAS_MASK, bool CAUSAL, bool DOCS, bool KS = false>
+__global__ __launch_bounds__(KS ? 2 * kThreads : kThreads, KS ? 1 : 2) void dq_kernel(const BwdParams p) {
   static_assert(CAUSAL || !DOCS, "documents are causal");
+  static_assert(!KS || (CAUSAL && !DOCS), "the key split is for plain causal attention");
   using L = DqLayout<D>;
   constexpr int KK = D / 16;
   constexpr int DJ = D / 32;
-  __shared__ __attribute__((aligned(128))) uint8_t smem[2 * L::kStageAligned];
+  constexpr int NG = KS ? 2 : 1;                  // wave groups
+  __shared__ __attribute__((aligned(128))) uint8_t smem[NG * 2 * L::kStageAligned];
 
-  const int tid = threadIdx.x;
   // wave index as a scalar: every branch that guards a matrix-core instruction
   // must be wave-uniform to the compiler (MFMA does not honour EXEC)
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_all = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
+  const int grp = KS ? wave_all / kWaves : 0;      // wave group
+  const int wave = wave_all - grp * kWaves;       // wave within its group
+  const int tid = int(threadIdx.x) - grp * kThreads;
+  uint8_t* const gsmem = smem + grp * 2 * L::kStageAligned;   // the group's staging buffers
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
@@ -797,11 +812,23 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const BwdParams p) {
     // The steps split into a run without and a run with them, decided
     // outside the loop.  With documents every tile takes the masks (measured:
     // the split gained nothing there).
-    const int nsteps = ntiles - it_first;
+    const int nsteps_all = ntiles - it_first;
     const int first_row = pb * p.pw;
     int mask_from = CAUSAL ? max(first_row - L::kBN + 1, 0) : p.n - L::kBN + 1;   // first key0 of a masked tile
     mask_from = min(mask_from, p.n - L::kBN + 1);
-    const int j_hi = DOCS ? 0 : min(max((mask_from + L::kBN - 1) / L::kBN - it_first, 0), nsteps);   // steps >= j_hi masked
+    // tiles it_first .. ntiles-1 from mask_tile on take the masks
+    const int mask_tile = (mask_from + L::kBN - 1) / L::kBN;
+    // this group's tiles g_first .. g_first+g_steps-1; both groups run
+    // `nsteps` loop steps (the same barriers), the second group one fewer
+    // real step when the count is odd, or none on the split workgroups
+    int g_first = it_first, g_steps = nsteps_all, nsteps = nsteps_all;
+    if (KS) {
+      const int h = SPLIT ? nsteps_all : (nsteps_all + 1) / 2;
+      g_first = it_first + (grp == 1 ? h : 0);
+      g_steps = grp == 0 ? h : nsteps_all - h;
+      nsteps = h;
+    }
+    const int j_hi = DOCS ? 0 : min(max(mask_tile - g_first, 0), nsteps);   // steps >= j_hi masked
 
     // one sweep over the tiles: the dQ products, or (DLPASS) only the row sums of P dP
     auto sweep = [&](auto dlpass_tag) __attribute__((always_inline)) {
@@ -810,20 +837,23 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const BwdParams p) {
       // step j works on tile it_first + j, staged in buffer j & 1 (the LDS
       // addresses depend on the step counter only)
       uint32_t vbyte = 0;
-      dq_issue<D, HAS_MASK>(smem, vbyte, p, b, kvh, it_first, wave, lane, tid);
-      if (HAS_MASK && tid < L::kBN) reinterpret_cast<float*>(smem + L::kOffValid)[tid] = vbyte ? 0.f : -INFINITY;
+      if (g_steps > 0) {
+        dq_issue<D, HAS_MASK>(gsmem, vbyte, p, b, kvh, g_first, wave, lane, tid);
+        if (HAS_MASK && tid < L::kBN) reinterpret_cast<float*>(gsmem + L::kOffValid)[tid] = vbyte ? 0.f : -INFINITY;
+      }
       wait_vmem();
       __syncthreads();
       auto steps = [&](int j0, int j1, auto masked_tag) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(masked_tag)::value;
         for (int j = j0; j < j1; ++j) {
-          const int it = it_first + j;
+          const int it = g_first + j;
           // prefetch tile it+1 into the other buffer while computing on this one
-          uint8_t* cur = smem + (j & 1) * L::kStageAligned;
-          uint8_t* nxt = smem + ((j + 1) & 1) * L::kStageAligned;
-          if (it + 1 < ntiles) dq_issue<D, HAS_MASK>(nxt, vbyte, p, b, kvh, it + 1, wave, lane, tid);
+          uint8_t* cur = gsmem + (j & 1) * L::kStageAligned;
+          uint8_t* nxt = gsmem + ((j + 1) & 1) * L::kStageAligned;
+          if (j + 1 < g_steps) dq_issue<D, HAS_MASK>(nxt, vbyte, p, b, kvh, it + 1, wave, lane, tid);
           const int tile0 = it * L::kBN;
-          if (wave_live && !(CAUSAL && tile0 > wave_last) && !(DOCS && tile0 + L::kBN <= lo_wave)) {
+          if ((!KS || j < g_steps) && wave_live && !(CAUSAL && tile0 > wave_last) &&
+              !(DOCS && tile0 + L::kBN <= lo_wave)) {
             const uint8_t* ks = cur + L::kOffK;
             const uint8_t* vs = cur + L::kOffV;
             const uint8_t* vb = cur + L::kOffValid;
@@ -840,7 +870,7 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const BwdParams p) {
                                                                 hh, lane, dqa, dlacc);
             }
           }
-          if (HAS_MASK && it + 1 < ntiles && tid < L::kBN)
+          if (HAS_MASK && j + 1 < g_steps && tid < L::kBN)
             reinterpret_cast<float*>(nxt + L::kOffValid)[tid] = vbyte ? 0.f : -INFINITY;
           wait_vmem();
           __syncthreads();
@@ -852,11 +882,36 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const BwdParams p) {
     };
 
     if constexpr (SPLIT) {
-      // the two half-waves hold complementary keys of the same row
+      // the two half-waves hold complementary keys of the same row (with the
+      // key split, the first group holds all of them)
       dl = halves_sum(sweep(std::true_type{}));
-      if (t < p.n && hh == 0) p.rowdot[(int64_t(b) * p.Hq + head) * p.n + t] = dl;
+      if (t < p.n && hh == 0 && grp == 0) p.rowdot[(int64_t(b) * p.Hq + head) * p.n + t] = dl;
     }
     sweep(std::false_type{});
+
+    if constexpr (KS) {
+      // the second group's dQ^T to the first, through the second group's
+      // staging buffers (free: both groups are past their last barrier):
+      // float4 (j, i4) of wave w at xch[((w * DJ + j) * 4 + i4) * 64 + lane]
+      f32x4* xch = reinterpret_cast<f32x4*>(smem + 2 * L::kStageAligned);
+      if (grp == 1)
+#pragma unroll
+        for (int j = 0; j < DJ; ++j)
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4)
+            xch[((wave * DJ + j) * 4 + i4) * 64 + lane] =
+                f32x4{dqa[j][i4 * 4], dqa[j][i4 * 4 + 1], dqa[j][i4 * 4 + 2], dqa[j][i4 * 4 + 3]};
+      __syncthreads();
+      if (grp == 1) return;
+#pragma unroll
+      for (int j = 0; j < DJ; ++j)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const f32x4 x = xch[((wave * DJ + j) * 4 + i4) * 64 + lane];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dqa[j][i4 * 4 + e] += x[e];
+        }
+    }
 
     if (t < p.n) {
       const int64_t base = ((int64_t(b) * p.n + t) * p.Hq + head) * D;
@@ -880,7 +935,16 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const BwdParams p) {
 template <int D, bool HAS_MASK, bool CAUSAL, bool DOCS>
 hipError_t launch_grads(const BwdParams& p, int64_t kv_blocks, int64_t q_blocks, hipStream_t stream) {
   // dq first: it rewrites Dl of the rows with few visible keys, which dkdv reads
-  hipLaunchKernelGGL((dq_kernel<D, HAS_MASK, CAUSAL, DOCS>), dim3(q_blocks), dim3(kThreads), 0, stream, p);
+  // short plain causal grids (every 4-wave block resident at once, two per
+  // CU) take the key split: one 8-wave workgroup per block
+  if constexpr (CAUSAL && !DOCS) {
+    if (q_blocks <= kDqSplitBlocks)
+      hipLaunchKernelGGL((dq_kernel<D, HAS_MASK, true, false, true>), dim3(q_blocks), dim3(2 * kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((dq_kernel<D, HAS_MASK, true, false>), dim3(q_blocks), dim3(kThreads), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((dq_kernel<D, HAS_MASK, CAUSAL, DOCS>), dim3(q_blocks), dim3(kThreads), 0, stream, p);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((dkdv_pair_kernel<D, HAS_MASK, CAUSAL, DOCS>), dim3(kv_blocks), dim3(kPairThreads), 0, stream, p);
