@@ -662,6 +662,8 @@ __device__ __forceinline__ void dq_half(const uint8_t* ks, const uint8_t* vs, co
       for (int e = 0; e < 4; ++e) s[g4 * 4 + e] = b4[e];
     }
   }
+  // (matrix blocks at raised wave priority, as in the forward)
+  __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
     const int off = rm_off<L::kRowBytes>(half * 32 + l32, 2 * kk + hh);
@@ -669,6 +671,7 @@ __device__ __forceinline__ void dq_half(const uint8_t* ks, const uint8_t* vs, co
     dp = mfma32x32x16(*reinterpret_cast<const u32x4*>(vs + off), df[kk], dp);
   }
   pipeline_reads_mfma<6, 2 * KK>();   // three k-steps of K/V rows in flight
+  __builtin_amdgcn_s_setprio(0);
   if constexpr (DLPASS) {
     // Dl = sum over the visible keys of P dP, in float32 from the scores
 #pragma unroll
@@ -705,6 +708,7 @@ __device__ __forceinline__ void dq_half(const uint8_t* ks, const uint8_t* vs, co
     if (SPLIT) dlo[f] = pack8_residual(ds + 8 * f, dh[f]);
   }
   // dQ^T += K^T dS^T  (K^T read transposed from the row-major K tile)
+  __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int f = 0; f < 2; ++f) {
 #pragma unroll
@@ -715,6 +719,7 @@ __device__ __forceinline__ void dq_half(const uint8_t* ks, const uint8_t* vs, co
     }
   }
   if (!SPLIT) pipeline_tr_reads_mfma<3, 2 * DJ>();
+  __builtin_amdgcn_s_setprio(0);
 }
 
 // KS (key split, 8 waves, plain causal): two groups of 4 waves take the same

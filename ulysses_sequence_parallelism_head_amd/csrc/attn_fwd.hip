@@ -248,6 +248,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(const Fw
             }
           }
         }
+        // (the matrix blocks issue at raised wave priority: of the SIMD's two
+        // waves, the one with MFMAs to issue goes first and the other's
+        // softmax fills the gaps; measured 3-5 % on the masked kernels)
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
           const u32x4 a0 = *reinterpret_cast<const u32x4*>(ks + rm_off<L::kRowBytes>(l32, 2 * kk + hh));
@@ -256,6 +260,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(const Fw
           s1 = mfma32x32x16(a1, qf[kk], s1);
         }
         pipeline_reads_mfma<6, 2 * KK>();   // three k-steps of K rows in flight
+        __builtin_amdgcn_s_setprio(0);
 
         // ---- raw scores and masks (masked keys -> -inf)
         float x[32];
@@ -328,6 +333,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(const Fw
         }
 
         // ---- O^T += V^T P^T
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
 #pragma unroll
@@ -339,6 +345,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_bf16_kernel(const Fw
           }
         }
         if (!SPLIT) pipeline_tr_reads_mfma<4, 4 * DJ>();
+        __builtin_amdgcn_s_setprio(0);
       }
 
       if (HAS_MASK && it + 1 < it_end && tid < kBN)
