@@ -120,7 +120,7 @@ ulysses_status_t check_bwd(const void* q, const void* k, const void* v, const ui
       !aligned(doc_start, 4))
     return ULYSSES_ERR_INVALID_ARG;
   const size_t need =
-      ulysses::attn_bwd_workspace_bytes(B, n, Hq, Hkv, D, own_workspace ? ulysses::attn_bwd_nsplit(B, n, Hkv) : 1);
+      ulysses::attn_bwd_workspace_bytes(B, n, Hq, Hkv, D, own_workspace ? ulysses::attn_bwd_nsplit_max(B, n, Hkv) : 1);
   if (own_workspace && workspace_bytes < need) return ULYSSES_ERR_INVALID_ARG;
   const uint64_t nq = uint64_t(B) * n * Hq * D, nkv = uint64_t(B) * n * Hkv * D;
   const void* ins[8] = {q, k, v, key_valid, o, lse, dout, doc_start};
@@ -150,9 +150,12 @@ ulysses_status_t attn_bwd(const void* q, const void* k, const void* v, const uin
                                   &empty);
   if (st != ULYSSES_OK || empty) return st;
   AttnShape s{B, n, Hq, Hkv, D, softmax_scale, causal};
+  const ulysses::BwdKind kind = doc_start != nullptr ? ulysses::BwdKind::kDocs
+                                : causal             ? ulysses::BwdKind::kCausal
+                                                     : ulysses::BwdKind::kFull;
   return from_hip(ulysses::launch_attn_bwd_bf16(q, k, v, key_valid, doc_start, o, lse, dout, dq, dk, dv,
                                                 static_cast<float*>(workspace), s, o_dtype == ULYSSES_DTYPE_F32,
-                                                ulysses::attn_bwd_nsplit(B, n, Hkv), static_cast<hipStream_t>(stream)));
+                                                ulysses::attn_bwd_nsplit(B, n, Hkv, kind), static_cast<hipStream_t>(stream)));
 }
 
 // ---- the no-allocation backward
@@ -236,7 +239,7 @@ ulysses_status_t ulysses_attn_fwd_docs(const void* q, const void* k, const void*
 
 size_t ulysses_attn_bwd_workspace_bytes(int32_t B, int64_t n, int32_t Hq, int32_t Hkv, int32_t D) {
   if (B <= 0 || n <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0) return 0;
-  return ulysses::attn_bwd_workspace_bytes(B, n, Hq, Hkv, D, ulysses::attn_bwd_nsplit(B, n, Hkv));
+  return ulysses::attn_bwd_workspace_bytes(B, n, Hq, Hkv, D, ulysses::attn_bwd_nsplit_max(B, n, Hkv));
 }
 
 ulysses_status_t ulysses_attn_bwd(const void* q, const void* k, const void* v, const uint8_t* key_valid,

@@ -52,8 +52,11 @@ hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, con
                                 float* dq, float* dk, float* dv, float* workspace, const AttnShape& s, int o_f32,
                                 int nsplit, hipStream_t stream);
 
-// workgroups per key-block pair of the dK/dV pass for this shape
-int attn_bwd_nsplit(int32_t B, int64_t n, int32_t Hkv);
+// workgroups per work item of the dK/dV pass for this shape and kind of
+// call, and the largest over the kinds (what the workspace is sized for)
+enum class BwdKind { kCausal, kFull, kDocs };
+int attn_bwd_nsplit(int32_t B, int64_t n, int32_t Hkv, BwdKind kind);
+int attn_bwd_nsplit_max(int32_t B, int64_t n, int32_t Hkv);
 // where each array of the backward's workspace lives (offsets in floats)
 struct BwdWorkspace {
   size_t rowdot, lse2, dk_part, dv_part;
