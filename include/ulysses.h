@@ -192,7 +192,8 @@ ULYSSES_API ulysses_status_t ulysses_attn_fwd(const void* q, const void* k, cons
  * float32 [B][Hq][n] arrays (the per-row dot products dO.O, and the
  * logsumexp in base 2), each rounded up to 256 B, and on short sequences
  * the partial dK and dV of the workgroups that share a key block
- * (2 * S * B * n * Hkv * D float32, S <= 8 chosen from B, n and Hkv).
+ * (2 * S * B * n * Hkv * D float32, S <= 8 chosen from B, n and Hkv: the
+ * largest count any kind of backward call takes for the shape).
  */
 ULYSSES_API size_t ulysses_attn_bwd_workspace_bytes(int32_t B, int64_t n, int32_t Hq, int32_t Hkv, int32_t D);
 
@@ -218,10 +219,13 @@ ULYSSES_API size_t ulysses_attn_bwd_workspace_bytes(int32_t B, int64_t n, int32_
  *              ulysses_attn_bwd_workspace_bytes(...) bytes, 256-byte
  *              aligned; contents on entry are ignored, on exit undefined.
  *
- * On short sequences (fewer than 384 pairs of 128-key blocks over B and
- * Hkv) each key block's query rows are spread over up to 8 workgroups,
- * which write partial dK/dV into the workspace; a second pass adds them in
- * a fixed order, so the result is still the same on every run.
+ * On short sequences (fewer than 1024 work items of the dK/dV pass: pairs
+ * of 128-key blocks over B and Hkv when causal, single blocks otherwise)
+ * each key block's query rows may be spread over up to 8 workgroups, as many
+ * as minimise the pass's length on 256 CUs; they write partial dK/dV into
+ * the workspace and a second pass adds them in a fixed order, so the result
+ * is the same on every run.  The count depends on the shape and the kind of
+ * call (causal, non-causal, documents) only.
  *
  * Built combinations: in_dtype BF16 with o_dtype BF16 or F32; D 64 or 128.
  * Errors: as ulysses_attn_fwd, plus INVALID_ARG for a null or too small
