@@ -73,7 +73,7 @@ struct BwdParams {
   float* dq;
   float* dk;
   float* dv;
-  float* rowdot;      // [B][Hq][n] dO . O (workspace)
+  float* rowdot;      // [B][Hq][n] -(dO . O) (workspace)
   float* lse2;        // [B][Hq][n] lse * log2(e), +inf for empty rows (workspace)
   float* dk_part;     // [nsplit][B][n][Hkv][D] partial dK of each split (workspace; nsplit > 1)
   float* dv_part;     // [nsplit][B][n][Hkv][D] partial dV
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const BwdParams p) {
     const int64_t t = bt % p.n;
     const int64_t b = bt / p.n;
     const int64_t idx = (b * p.Hq + h) * p.n + t;
-    p.rowdot[idx] = acc;
+    p.rowdot[idx] = -acc;   // stored negated: the dK/dV pass starts its dP accumulators from it
     // base-2 logsumexp for the exponentials of the dK/dV pass; a row with no
     // visible key (lse = -inf) gets +inf so that every exponent is -inf
     const float l = p.lse[idx];
@@ -479,8 +479,22 @@ __global__ __launch_bounds__(kPairThreads, 1) void dkdv_pair_kernel(const BwdPar
             // S = Q K^T (P wave) or dP = dO V^T (dS wave); step t = (kk, rb) =
             // (t / 2, t % 2), A operand row-major from the tile
             const uint8_t* as = PW ? qs : dos;
+            if constexpr (PW) {
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) sc[rb] = f32x16{};
+              for (int rb = 0; rb < 2; ++rb) sc[rb] = f32x16{};
+            } else {
+              // dP accumulators start from -Dl of their rows: the products
+              // then leave dP - Dl, the factor of dS
+              const float* ndl = reinterpret_cast<const float*>(st + X::kSDL);
+#pragma unroll
+              for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int c4 = 0; c4 < 4; ++c4) {
+                  const f32x4 d4 = *reinterpret_cast<const f32x4*>(ndl + rb * 32 + c4 * 8 + hh * 4);
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) sc[rb][4 * c4 + e] = d4[e];
+                }
+            }
             lds_pipeline<DOCS ? kRowAhead - 2 : kRowAhead, 2 * KK>(   // (documents: registers)
                 [&](int t) {
                   return *reinterpret_cast<const u32x4*>(as + rm_off<X::kRowBytes>((t % 2) * 32 + l32, t + hh - t % 2));
@@ -512,17 +526,15 @@ __global__ __launch_bounds__(kPairThreads, 1) void dkdv_pair_kernel(const BwdPar
             if constexpr (PW) {
               tr_products(dos, std::integral_constant<int, 0>{}, std::integral_constant<int, 2>{});   // dV^T += dO^T P
             } else {
-              // each block's dS just before its products dK^T += Q^T dS
-              const float* dls = reinterpret_cast<const float*>(st + X::kSDL);
+              // each block's dS = P (dP - Dl) just before its products dK^T += Q^T dS
               auto block = [&](auto rb_tag) __attribute__((always_inline)) {
                 constexpr int rb = decltype(rb_tag)::value;
                 float ds[16];
 #pragma unroll
                 for (int c4 = 0; c4 < 4; ++c4) {
                   const f32x4 p4 = *reinterpret_cast<const f32x4*>(xp + ((rb * 4 + c4) * 64 + lane) * 4);
-                  const f32x4 d4 = *reinterpret_cast<const f32x4*>(dls + rb * 32 + c4 * 8 + hh * 4);
 #pragma unroll
-                  for (int e = 0; e < 4; ++e) ds[4 * c4 + e] = p4[e] * (sc[rb][4 * c4 + e] - d4[e]);
+                  for (int e = 0; e < 4; ++e) ds[4 * c4 + e] = p4[e] * sc[rb][4 * c4 + e];
                 }
 #pragma unroll
                 for (int f = 0; f < 2; ++f) {
@@ -793,7 +805,7 @@ __global__ __launch_bounds__(KS ? 2 * kThreads : kThreads, KS ? 1 : 2) void dq_k
     if (ok) {
       const float l = p.lse[(int64_t(b) * p.Hq + head) * p.n + t];
       lse2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
-      dl = p.rowdot[(int64_t(b) * p.Hq + head) * p.n + t];
+      dl = -p.rowdot[(int64_t(b) * p.Hq + head) * p.n + t];
     }
   }
 
@@ -890,7 +902,7 @@ __global__ __launch_bounds__(KS ? 2 * kThreads : kThreads, KS ? 1 : 2) void dq_k
       // the two half-waves hold complementary keys of the same row (with the
       // key split, the first group holds all of them)
       dl = halves_sum(sweep(std::true_type{}));
-      if (t < p.n && hh == 0 && grp == 0) p.rowdot[(int64_t(b) * p.Hq + head) * p.n + t] = dl;
+      if (t < p.n && hh == 0 && grp == 0) p.rowdot[(int64_t(b) * p.Hq + head) * p.n + t] = -dl;
     }
     sweep(std::false_type{});
 

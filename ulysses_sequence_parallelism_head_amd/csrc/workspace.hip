@@ -55,7 +55,7 @@ int attn_bwd_nsplit_max(int32_t B, int64_t n, int32_t Hkv) {
                    attn_bwd_nsplit(B, n, Hkv, BwdKind::kDocs)});
 }
 
-// Layout (offsets in floats): Dl = dO . O, then the base-2 logsumexp, then
+// Layout (offsets in floats): -Dl = -(dO . O), then the base-2 logsumexp, then
 // with several splits their partial dK and dV, [nsplit][B][n][Hkv][D] each.
 BwdWorkspace attn_bwd_workspace(int32_t B, int64_t n, int32_t Hq, int32_t Hkv, int32_t D, int nsplit) {
   BwdWorkspace w;
