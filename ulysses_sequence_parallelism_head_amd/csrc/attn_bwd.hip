@@ -544,8 +544,13 @@ __global__ __launch_bounds__(kPairThreads, 1) void dkdv_pair_kernel(const BwdPar
                 __builtin_amdgcn_sched_barrier(0);
                 tr_products(qs, rb_tag, std::integral_constant<int, 1>{});
               };
+              // the dS wave's products lead the unit's critical chain here (the
+              // P wave's dV has slack until the end barrier): its issue goes
+              // first on the SIMD
+              __builtin_amdgcn_s_setprio(1);
               block(std::integral_constant<int, 0>{});
               block(std::integral_constant<int, 1>{});
+              __builtin_amdgcn_s_setprio(0);
             }
           }
           wait_vmem();
