@@ -11,8 +11,15 @@
 //   P = exp(S - lse)      dV = P^T dO        dP = dO V^T
 //   Dl = rowsum(dO * O)   dS = P * (dP - Dl) dQ = scale dS K   dK = scale dS^T Q
 //
-// Three kernels:
-//  1. rowdot: Dl[b][h][t] = dO . O per query row (float32 workspace).
+// Two kernels (and a reduction of partial dK/dV when a key block's work is
+// split over several workgroups), dq first:
+//  1. dq (Q-stationary, laid out like the forward): each wave first forms
+//     Dl = dO . O and the base-2 logsumexp of its rows and stores them in the
+//     workspace for dkdv; then it recomputes S^T = K Q^T and dP^T = V dO^T
+//     with the query on the lane and accumulates dQ^T += K^T dS^T, the K^T
+//     operand read transposed from the row-major K tile.  Keeping dQ in its
+//     own pass avoids float32 atomics (whose traffic would grow as n^2 /
+//     block) and makes every gradient deterministic.
 //  2. dkdv (KV-stationary): a workgroup of 8 waves owns 128 keys of one KV
 //     head (4 groups of 32 keys, two waves per group) and streams the 64-row
 //     query tiles of every query head of the group that can see them (for
@@ -26,12 +33,6 @@
 //     (ds_read_b64_tr_b16).  Splitting a group's work over two waves halves
 //     each wave's registers, so two waves share a SIMD and one's
 //     exponentials and waits overlap the other's matrix work.
-//  3. dq (Q-stationary, laid out like the forward): recomputes S^T = K Q^T and
-//     dP^T = V dO^T with the query on the lane and accumulates
-//     dQ^T += K^T dS^T, the K^T operand read transposed from the row-major K
-//     tile.  Keeping dQ in its own pass
-//     avoids float32 atomics (whose traffic would grow as n^2 / block) and
-//     makes every gradient deterministic.
 // Masks run only on the tiles that need them, chosen per run of tiles
 // outside the loops: dkdv applies the causal compare on the two query tiles
 // at a key block's diagonal and no per-key mask at all (a padding key's P
@@ -83,51 +84,12 @@ struct BwdParams {
   float scale;
   float c;            // scale * log2(e)
   int32_t causal;
+  int32_t o_f32;       // O is float32 (else bf16)
   // dq grid (same as the forward)
   int32_t gh, pw, n_pblocks, n_hsub;
   // dkdv grid
   int32_t n_kblocks;
 };
-
-// ------------------------------------------------------------------ rowdot
-// Dl = dO . O per query row, and the base-2 logsumexp, into the workspace.
-template <int D, bool O_F32>
-__global__ __launch_bounds__(256) void rowdot_kernel(const BwdParams p) {
-  // 16 lanes per row, D/16 elements each
-  constexpr int PER = D / 16;
-  const int64_t rows = int64_t(p.B) * p.n * p.Hq;
-  const int64_t row = int64_t(blockIdx.x) * 16 + (threadIdx.x >> 4);
-  const int sub = threadIdx.x & 15;
-  float acc = 0.f;
-  if (row < rows) {
-    const uint16_t* dp = p.dout + row * D + sub * PER;
-    if (O_F32) {
-      const float* op = static_cast<const float*>(p.o) + row * D + sub * PER;
-#pragma unroll
-      for (int e = 0; e < PER; ++e) acc = fmaf(__uint_as_float(uint32_t(dp[e]) << 16), op[e], acc);
-    } else {
-      const uint16_t* op = static_cast<const uint16_t*>(p.o) + row * D + sub * PER;
-#pragma unroll
-      for (int e = 0; e < PER; ++e)
-        acc = fmaf(__uint_as_float(uint32_t(dp[e]) << 16), __uint_as_float(uint32_t(op[e]) << 16), acc);
-    }
-  }
-#pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
-  if (row < rows && sub == 0) {
-    // row = (b*n + t)*Hq + h  ->  rowdot[(b*Hq + h)*n + t]
-    const int64_t h = row % p.Hq;
-    const int64_t bt = row / p.Hq;
-    const int64_t t = bt % p.n;
-    const int64_t b = bt / p.n;
-    const int64_t idx = (b * p.Hq + h) * p.n + t;
-    p.rowdot[idx] = -acc;   // stored negated: the dK/dV pass starts its dP accumulators from it
-    // base-2 logsumexp for the exponentials of the dK/dV pass; a row with no
-    // visible key (lse = -inf) gets +inf so that every exponent is -inf
-    const float l = p.lse[idx];
-    p.lse2[idx] = (l == -INFINITY) ? INFINITY : l * kLog2e;
-  }
-}
 
 // ------------------------------------------------------------------- dkdv
 // Pack 8 floats (x[0..7]) as the bf16 B operand of one MFMA, and optionally
@@ -807,10 +769,46 @@ __global__ __launch_bounds__(KS ? 2 * kThreads : kThreads, KS ? 1 : 2) void dq_k
       qf[kk] = ok ? *reinterpret_cast<const u32x4*>(p.q + off + 16 * kk) : u32x4{0, 0, 0, 0};
       df[kk] = ok ? *reinterpret_cast<const u32x4*>(p.dout + off + 16 * kk) : u32x4{0, 0, 0, 0};
     }
+    // Dl = dO . O of the lane's row: this half-wave's dims 16kk + 8hh .. +7,
+    // then the other half's; with the base-2 logsumexp (+inf for a row with
+    // no visible key, so that every exponent is -inf) it goes to the
+    // workspace for the dK/dV pass, which runs after this kernel
+    float part = 0.f;
     if (ok) {
+      if (p.o_f32) {
+        const float* op = static_cast<const float*>(p.o) + off;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          const f32x4 o0 = *reinterpret_cast<const f32x4*>(op + 16 * kk);
+          const f32x4 o1 = *reinterpret_cast<const f32x4*>(op + 16 * kk + 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float olo = e < 2 ? o0[2 * e] : o1[2 * e - 4];
+            const float ohi = e < 2 ? o0[2 * e + 1] : o1[2 * e - 3];
+            part = fmaf(bf16lo_to_f32(df[kk][e]), olo, part);
+            part = fmaf(bf16hi_to_f32(df[kk][e]), ohi, part);
+          }
+        }
+      } else {
+        const uint16_t* op = static_cast<const uint16_t*>(p.o) + off;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          const u32x4 ov = *reinterpret_cast<const u32x4*>(op + 16 * kk);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            part = fmaf(bf16lo_to_f32(df[kk][e]), bf16lo_to_f32(ov[e]), part);
+            part = fmaf(bf16hi_to_f32(df[kk][e]), bf16hi_to_f32(ov[e]), part);
+          }
+        }
+      }
       const float l = p.lse[(int64_t(b) * p.Hq + head) * p.n + t];
       lse2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
-      dl = -p.rowdot[(int64_t(b) * p.Hq + head) * p.n + t];
+    }
+    dl = halves_sum(part);
+    if (ok && hh == 0 && grp == 0) {
+      const int64_t idx = (int64_t(b) * p.Hq + head) * p.n + t;
+      p.rowdot[idx] = -dl;   // stored negated: the dK/dV pass starts its dP accumulators from it
+      p.lse2[idx] = lse2;
     }
   }
 
@@ -989,15 +987,7 @@ hipError_t dispatch_grads(const BwdParams& p, int64_t kv_blocks, int64_t q_block
 }
 
 template <int D>
-hipError_t launch_bwd_d(const BwdParams& p, bool has_mask, bool o_f32, hipStream_t stream) {
-  const int64_t rows = int64_t(p.B) * p.n * p.Hq;
-  const int64_t rd_blocks = (rows + 15) / 16;
-  if (rd_blocks > 0x7fffffff) return hipErrorInvalidValue;
-  if (o_f32) hipLaunchKernelGGL((rowdot_kernel<D, true>), dim3(rd_blocks), dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL((rowdot_kernel<D, false>), dim3(rd_blocks), dim3(256), 0, stream, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-
+hipError_t launch_bwd_d(const BwdParams& p, bool has_mask, hipStream_t stream) {
   // causal: one workgroup per pair of key blocks (nkb-1-w, w); documents:
   // one per key block
   const int64_t kv_work = (p.causal && p.doc_start == nullptr) ? (int64_t(p.n_kblocks) + 1) / 2 : p.n_kblocks;
@@ -1042,6 +1032,7 @@ hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, con
   p.scale = s.scale;
   p.c = s.scale * kLog2e;
   p.causal = s.causal;
+  p.o_f32 = o_f32 != 0;
   int gh = 1;
   for (int c = kWaves; c >= 1; --c)
     if (p.g % c == 0 && kWaves % c == 0) { gh = c; break; }
@@ -1051,8 +1042,8 @@ hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, con
   p.n_hsub = p.g / gh;
   p.n_kblocks = int32_t((s.n + 127) / 128);
   if (int64_t(p.B) * p.n == 0) return hipSuccess;
-  if (s.D == 128) return launch_bwd_d<128>(p, valid != nullptr, o_f32 != 0, stream);
-  return launch_bwd_d<64>(p, valid != nullptr, o_f32 != 0, stream);
+  if (s.D == 128) return launch_bwd_d<128>(p, valid != nullptr, stream);
+  return launch_bwd_d<64>(p, valid != nullptr, stream);
 }
 
 }  // namespace ulysses
