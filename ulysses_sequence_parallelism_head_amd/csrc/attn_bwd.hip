@@ -157,10 +157,15 @@ __device__ __forceinline__ int docs_partner(const int32_t* rs, int kb, int n, in
   return (q0 == r0 && q1 == r1) ? partner : kb;
 }
 
-// Sum of the splits' partial dK (or dV) in split order: out[i] = sum_s part[s][i]
-// (a fixed order, so the result does not depend on scheduling).
-__global__ __launch_bounds__(256) void dkdv_reduce_kernel(const float* part, float* out, int64_t count, int32_t nsplit) {
-  const int64_t i = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
+// Sum of the splits' partial dK and dV in split order: out[i] = sum_s part[s][i]
+// (a fixed order, so the result does not depend on scheduling); the first
+// `blocks` workgroups take dK, the rest dV.
+__global__ __launch_bounds__(256) void dkdv_reduce_kernel(const float* part_k, float* out_k, const float* part_v,
+                                                          float* out_v, int64_t count, int32_t nsplit, int32_t blocks) {
+  const bool is_v = int32_t(blockIdx.x) >= blocks;
+  const float* part = is_v ? part_v : part_k;
+  float* out = is_v ? out_v : out_k;
+  const int64_t i = (int64_t(blockIdx.x) - (is_v ? blocks : 0)) * 1024 + int64_t(threadIdx.x) * 4;
   if (i >= count) return;
   f32x4 acc = *reinterpret_cast<const f32x4*>(part + i);
   for (int32_t sp = 1; sp < nsplit; ++sp) {
@@ -972,10 +977,9 @@ hipError_t launch_grads(const BwdParams& p, int64_t kv_blocks, int64_t q_blocks,
   if (e != hipSuccess || p.nsplit == 1) return e;
   const int64_t count = int64_t(p.B) * p.n * p.Hkv * D;   // a multiple of 4 (D is)
   const int64_t rblocks = (count / 4 + 255) / 256;
-  hipLaunchKernelGGL(dkdv_reduce_kernel, dim3(rblocks), dim3(256), 0, stream, p.dk_part, p.dk, count, p.nsplit);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(dkdv_reduce_kernel, dim3(rblocks), dim3(256), 0, stream, p.dv_part, p.dv, count, p.nsplit);
+  if (2 * rblocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(dkdv_reduce_kernel, dim3(2 * rblocks), dim3(256), 0, stream, p.dk_part, p.dk, p.dv_part, p.dv,
+                     count, p.nsplit, int32_t(rblocks));
   return hipGetLastError();
 }
 
