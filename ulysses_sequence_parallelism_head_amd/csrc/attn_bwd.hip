@@ -211,16 +211,21 @@ struct DkdvPairLayout {
 
 // DMA unit tile t0 .. t0+63 of query head `head` for the two-wave kernel: Q,
 // dO, the base-2 logsumexp, Dl (and the rows' bounds) into stage `st` (rows
-// past n read as zero).  All eight waves take part.
-template <int D, bool DOCS>
+// past n read as zero), by NWI waves (`wave` counts among them).
+template <int D, bool DOCS, int NWI = kPairWaves>
 __device__ __forceinline__ void dkdv_pair_issue(uint8_t* st, const BwdParams& p, int b, int head, int t0, int wave,
                                                 int lane) {
   using X = DkdvPairLayout<D, DOCS>;
   const int rows_ok = min(X::kRows, p.n - t0);
   const int64_t off = ((int64_t(b) * p.n + t0) * p.Hq + head) * D;
   const int stride = p.Hq * D * 2;
-  dma_tile<D, X::kRows, kPairWaves>(st + X::kSQ, p.q + off, stride, rows_ok, wave, lane);
-  dma_tile<D, X::kRows, kPairWaves>(st + X::kSDO, p.dout + off, stride, rows_ok, wave, lane);
+  // NWI issuing waves (8 or 4): each covers the shares of 8 / NWI waves of
+  // the 8-wave layout, one batch at a time
+#pragma unroll
+  for (int h = 0; h < kPairWaves / NWI; ++h) {
+    dma_tile<D, X::kRows, kPairWaves>(st + X::kSQ, p.q + off, stride, rows_ok, wave + h * NWI, lane);
+    dma_tile<D, X::kRows, kPairWaves>(st + X::kSDO, p.dout + off, stride, rows_ok, wave + h * NWI, lane);
+  }
   const int64_t roff = (int64_t(b) * p.Hq + head) * p.n + t0;
   if (wave == 0) dma4(buffer_rsrc(p.lse2 + roff, uint32_t(rows_ok) * 4u), st + X::kSLSE, lane * 4);
   if (wave == 1) dma4(buffer_rsrc(p.rowdot + roff, uint32_t(rows_ok) * 4u), st + X::kSDL, lane * 4);
@@ -359,7 +364,9 @@ __global__ __launch_bounds__(kPairThreads, 1) void dkdv_pair_kernel(const BwdPar
       bool key_ok = u < p.n;
       {
         const uint16_t* src = PW ? p.k : p.v;
-        const int64_t off = ((int64_t(b) * p.n + (key_ok ? u : 0)) * p.Hkv + kvh) * D + 8 * hh;
+        const int lk = opaque_lane_id();   // (the row address is formed here, not kept across phases)
+        const int uk = k0w + (lk & 31);
+        const int64_t off = ((int64_t(b) * p.n + (key_ok ? uk : 0)) * p.Hkv + kvh) * D + 8 * (lk >> 5);
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk)
           kv[kk] = key_ok ? *reinterpret_cast<const u32x4*>(src + off + 16 * kk) : u32x4{0, 0, 0, 0};
@@ -435,8 +442,13 @@ __global__ __launch_bounds__(kPairThreads, 1) void dkdv_pair_kernel(const BwdPar
         int ntile = tile_of(it0 + 1), nhead = (it0 + 1) % p.g;
         const int tstep = down ? -1 : 1;
         for (int it = it0; it < it1; ++it) {
-          if (it + 1 < u1)
-            dkdv_pair_issue<D, DOCS>(sbuf(it + 1), p, b, kvh * p.g + nhead, ntile * X::kRows, wave, lane);
+          // the dS waves alone stage the next unit: the P waves, which the SIMD
+          // issues first, go straight to the score products on the critical
+          // chain (1-3 % on most shapes)
+          if constexpr (!PW) {
+            if (it + 1 < u1)
+              dkdv_pair_issue<D, DOCS, 4>(sbuf(it + 1), p, b, kvh * p.g + nhead, ntile * X::kRows, wave - 4, lane);
+          }
           const int t0 = tile * X::kRows;
           const uint8_t* st = sbuf(it);
           const uint8_t* qs = st + X::kSQ;
