@@ -147,6 +147,28 @@ def test_bwd_full_size_sampled(stem, c, o_dtype):
         assert np.all(dk[0, pad] == 0.0) and np.all(dv[0, pad] == 0.0)
 
 
+@pytest.mark.parametrize("masked", [False, True])
+def test_bwd_wide_dq_ragged(masked):
+    """A causal backward long enough for the 8-wave dq workgroups (n = 4100,
+    32q/8kv heads, d128: 520 of them, the last 64-position block ragged),
+    with a bf16 O: dQ at stratified rows and at the last 70 rows, dK/dV at
+    16 keys around the middle and at the last 64 keys, against the oracle."""
+    n, Hq, Hkv, D = 4100, 32, 8, 128
+    say(f"bwd wide dq n={n} 32q/8kv masked={masked}")
+    q, k, v, do, valid = _inputs(4100 + masked, n, Hq, Hkv, D, masked)
+    g = synth.streams(77)
+    q_rows = np.unique(np.concatenate([synth.stratified_rows(g[6], n, 16, None if valid is None else valid[0]),
+                                       np.arange(n - 70, n)]))
+    k_rows = np.unique(np.concatenate([np.arange(2040, 2056), np.arange(n - 64, n)]))
+    scale = D ** -0.5
+    dQ, dK, dV = oracle.attn_bwd_sampled(to_f64(q), to_f64(k), to_f64(v), to_f64(do), scale, True, valid,
+                                         q_rows=q_rows, k_rows=k_rows)
+    dq, dk, dv = _gpu_fwd_bwd(q, k, v, do, valid, scale, True, torch.bfloat16)
+    assert_close("dQ rows", dq[:, q_rows], dQ, 1e-2)
+    assert_close("dK keys", dk[:, k_rows], dK, 1e-2)
+    assert_close("dV keys", dv[:, k_rows], dV, 1e-2)
+
+
 def test_bwd_deterministic():
     say("bwd determinism")
     q, k, v, do, valid = _inputs(77, 900, 8, 2, 128, True)

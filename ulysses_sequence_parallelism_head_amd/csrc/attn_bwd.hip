@@ -60,6 +60,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kSplitRows = 512;   // a multiple of both query tile heights (64)
 constexpr int kDqSplitBlocks = 512;   // dq grids up to this size take the key split
+constexpr int kDqWideBlocks = 512;    // 8-wave dq grids from this size on share each K/V tile
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct BwdParams {
@@ -616,16 +617,17 @@ struct DqLayout {
   static constexpr int kStageAligned = (kStage + 127) / 128 * 128;
 };
 
-template <int D, bool HAS_MASK>
+template <int D, bool HAS_MASK, int NW>
 __device__ __forceinline__ void dq_issue(uint8_t* stage, uint32_t& vbyte, const BwdParams& p, int b, int kvh,
                                          int tile, int wave, int lane, int tid) {
+  // (wave, tid: indices among the NW waves that stage this tile)
   using L = DqLayout<D>;
   const int key0 = tile * L::kBN;
   const int rows_ok = min(L::kBN, p.n - key0);
   const int64_t off = ((int64_t(b) * p.n + key0) * p.Hkv + kvh) * D;
   const int stride = p.Hkv * D * 2;
-  dma_tile<D, L::kBN, kWaves>(stage + L::kOffK, p.k + off, stride, rows_ok, wave, lane);
-  dma_tile<D, L::kBN, kWaves>(stage + L::kOffV, p.v + off, stride, rows_ok, wave, lane);
+  dma_tile<D, L::kBN, NW>(stage + L::kOffK, p.k + off, stride, rows_ok, wave, lane);
+  dma_tile<D, L::kBN, NW>(stage + L::kOffV, p.v + off, stride, rows_ok, wave, lane);
   if (HAS_MASK && tid < L::kBN) {
     const int key = key0 + tid;
     vbyte = (key < p.n) ? (p.valid[int64_t(b) * p.n + key] != 0 ? 1u : 0u) : 0u;
@@ -727,10 +729,16 @@ __device__ __forceinline__ void dq_half(const uint8_t* ks, const uint8_t* vs, co
 // key) sets the kernel's time, each block then lasts about half as long.
 // Blocks whose rows see fewer than kSplitRows keys (the hi/lo split and the
 // exact-Dl sweep) stay whole in the first group: they are short anyway.
-template <int D, bool HAS_MASK, bool CAUSAL, bool DOCS, bool KS = false>
-__global__ __launch_bounds__(KS ? 2 * kThreads : kThreads, KS ? 1 : 2) void dq_kernel(const BwdParams p) {
+// WIDE (8 waves, long plain causal grids): one group of 8 waves whose rows
+// (64 positions of the KV head's query heads) share every staged K/V tile,
+// half the staging per flop of two 4-wave workgroups, as in the forward.
+template <int D, bool HAS_MASK, bool CAUSAL, bool DOCS, bool KS = false, bool WIDE = false>
+__global__ __launch_bounds__((KS || WIDE) ? 2 * kThreads : kThreads, (KS || WIDE) ? 1 : 2) void dq_kernel(
+    const BwdParams p) {
   static_assert(CAUSAL || !DOCS, "documents are causal");
   static_assert(!KS || (CAUSAL && !DOCS), "the key split is for plain causal attention");
+  static_assert(!(KS && WIDE), "one 8-wave form at a time");
+  constexpr int GW = WIDE ? 2 * kWaves : kWaves;  // waves that share one staged tile
   using L = DqLayout<D>;
   constexpr int KK = D / 16;
   constexpr int DJ = D / 32;
@@ -741,7 +749,7 @@ __global__ __launch_bounds__(KS ? 2 * kThreads : kThreads, KS ? 1 : 2) void dq_k
   // must be wave-uniform to the compiler (MFMA does not honour EXEC)
   const int wave_all = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
   const int grp = KS ? wave_all / kWaves : 0;      // wave group
-  const int wave = wave_all - grp * kWaves;       // wave within its group
+  const int wave = wave_all - grp * kWaves;       // wave within its group (all 8 with WIDE)
   const int tid = int(threadIdx.x) - grp * kThreads;
   uint8_t* const gsmem = smem + grp * 2 * L::kStageAligned;   // the group's staging buffers
   const int lane = tid & 63;
@@ -875,7 +883,7 @@ __global__ __launch_bounds__(KS ? 2 * kThreads : kThreads, KS ? 1 : 2) void dq_k
       // addresses depend on the step counter only)
       uint32_t vbyte = 0;
       if (g_steps > 0) {
-        dq_issue<D, HAS_MASK>(gsmem, vbyte, p, b, kvh, g_first, wave, lane, tid);
+        dq_issue<D, HAS_MASK, GW>(gsmem, vbyte, p, b, kvh, g_first, wave, lane, tid);
         if (HAS_MASK && tid < L::kBN) reinterpret_cast<float*>(gsmem + L::kOffValid)[tid] = vbyte ? 0.f : -INFINITY;
       }
       wait_vmem();
@@ -887,7 +895,16 @@ __global__ __launch_bounds__(KS ? 2 * kThreads : kThreads, KS ? 1 : 2) void dq_k
           // prefetch tile it+1 into the other buffer while computing on this one
           uint8_t* cur = gsmem + (j & 1) * L::kStageAligned;
           uint8_t* nxt = gsmem + ((j + 1) & 1) * L::kStageAligned;
-          if (j + 1 < g_steps) dq_issue<D, HAS_MASK>(nxt, vbyte, p, b, kvh, it + 1, wave, lane, tid);
+          if (j + 1 < g_steps) {
+            if constexpr (WIDE) {
+              // waves 4-7 alone stage the tiles after the first: the SIMD issues
+              // waves 0-3 first, and they go straight to their products
+              if (wave >= kWaves)
+                dq_issue<D, HAS_MASK, kWaves>(nxt, vbyte, p, b, kvh, it + 1, wave - kWaves, lane, tid - kThreads);
+            } else {
+              dq_issue<D, HAS_MASK, GW>(nxt, vbyte, p, b, kvh, it + 1, wave, lane, tid);
+            }
+          }
           const int tile0 = it * L::kBN;
           if ((!KS || j < g_steps) && wave_live && !(CAUSAL && tile0 > wave_last) &&
               !(DOCS && tile0 + L::kBN <= lo_wave)) {
@@ -907,8 +924,12 @@ __global__ __launch_bounds__(KS ? 2 * kThreads : kThreads, KS ? 1 : 2) void dq_k
                                                                 hh, lane, dqa, dlacc);
             }
           }
-          if (HAS_MASK && j + 1 < g_steps && tid < L::kBN)
+          if constexpr (WIDE) {
+            if (HAS_MASK && j + 1 < g_steps && wave >= kWaves && tid - kThreads < L::kBN)
+              reinterpret_cast<float*>(nxt + L::kOffValid)[tid - kThreads] = vbyte ? 0.f : -INFINITY;
+          } else if (HAS_MASK && j + 1 < g_steps && tid < L::kBN) {
             reinterpret_cast<float*>(nxt + L::kOffValid)[tid] = vbyte ? 0.f : -INFINITY;
+          }
           wait_vmem();
           __syncthreads();
         }
@@ -969,14 +990,33 @@ __global__ __launch_bounds__(KS ? 2 * kThreads : kThreads, KS ? 1 : 2) void dq_k
   else run(std::false_type{});
 }
 
+// dq grid shape for NW waves per workgroup: query heads per workgroup (the
+// largest divisor of g that divides NW) and positions per workgroup
+void dq_shape(BwdParams& p, int nw) {
+  int gh = 1;
+  for (int c = nw; c >= 1; --c)
+    if (p.g % c == 0 && nw % c == 0) { gh = c; break; }
+  p.gh = gh;
+  p.pw = 32 * (nw / gh);
+  p.n_pblocks = int32_t((int64_t(p.n) + p.pw - 1) / p.pw);
+  p.n_hsub = p.g / gh;
+}
+
 template <int D, bool HAS_MASK, bool CAUSAL, bool DOCS>
 hipError_t launch_grads(const BwdParams& p, int64_t kv_blocks, int64_t q_blocks, hipStream_t stream) {
   // dq first: it rewrites Dl of the rows with few visible keys, which dkdv reads
   // short plain causal grids (every 4-wave block resident at once, two per
   // CU) take the key split: one 8-wave workgroup per block
+  // long ones take the 8-wave form whose waves share each K/V tile
   if constexpr (CAUSAL && !DOCS) {
+    BwdParams p8 = p;
+    dq_shape(p8, 2 * kWaves);
+    const int64_t q_blocks8 = int64_t(p8.n_pblocks) * p8.n_hsub * p8.Hkv * p8.B;
     if (q_blocks <= kDqSplitBlocks)
       hipLaunchKernelGGL((dq_kernel<D, HAS_MASK, true, false, true>), dim3(q_blocks), dim3(2 * kThreads), 0, stream, p);
+    else if (q_blocks8 >= kDqWideBlocks)
+      hipLaunchKernelGGL((dq_kernel<D, HAS_MASK, true, false, false, true>), dim3(q_blocks8), dim3(2 * kThreads), 0,
+                         stream, p8);
     else
       hipLaunchKernelGGL((dq_kernel<D, HAS_MASK, true, false>), dim3(q_blocks), dim3(kThreads), 0, stream, p);
   } else {
@@ -1049,13 +1089,7 @@ hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, con
   p.c = s.scale * kLog2e;
   p.causal = s.causal;
   p.o_f32 = o_f32 != 0;
-  int gh = 1;
-  for (int c = kWaves; c >= 1; --c)
-    if (p.g % c == 0 && kWaves % c == 0) { gh = c; break; }
-  p.gh = gh;
-  p.pw = 32 * (kWaves / gh);
-  p.n_pblocks = int32_t((s.n + p.pw - 1) / p.pw);
-  p.n_hsub = p.g / gh;
+  dq_shape(p, kWaves);
   p.n_kblocks = int32_t((s.n + 127) / 128);
   if (int64_t(p.B) * p.n == 0) return hipSuccess;
   if (s.D == 128) return launch_bwd_d<128>(p, valid != nullptr, stream);
