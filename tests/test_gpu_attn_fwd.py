@@ -172,6 +172,27 @@ def test_fwd_wide_workgroups_ragged(masked):
     assert np.array_equal(l16, l32)
 
 
+@pytest.mark.parametrize("masked", [False, True])
+def test_fwd_noncausal_wide_ragged(masked):
+    """A non-causal run long enough for the 8-wave workgroups (n = 16390,
+    32q/8kv heads, d128: 2056 of them, the last block ragged): stratified
+    rows and the last 70, against the oracle.  The scale 0.25 (scores of
+    standard deviation 2.8) concentrates each row's softmax on a few dozen
+    of its 16390 keys, so a tile left out or counted twice moves O and LSE
+    well past the tolerance."""
+    n, Hq, Hkv, D = 16390, 32, 8, 128
+    say(f"fwd non-causal wide workgroups n={n} masked={masked}")
+    q, k, v, valid = _inputs(16390 + masked, n, Hq, Hkv, D, masked)
+    g = synth.streams(98)
+    rows = np.unique(np.concatenate([synth.stratified_rows(g[6], n, 16, None if valid is None else valid[0]),
+                                     np.arange(n - 70, n)]))
+    scale = 0.25
+    O, L = oracle.attn_fwd(to_f64(q), to_f64(k), to_f64(v), scale, False, valid, rows=rows)
+    o32, l32 = _run(q, k, v, valid, scale, False, torch.float32)
+    assert_close("O(f32 out)", o32[:, rows], O, 1e-2)
+    assert_close("LSE", l32[:, :, rows], L, 1e-2)
+
+
 def test_fwd_96k_docs_workload_sampled():
     """Workload 4 forward: n=98304 with packed documents (padding keys masked)."""
     say("fwd workload 4 (96K, documents) sampled rows")
