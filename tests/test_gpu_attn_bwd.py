@@ -147,14 +147,14 @@ def test_bwd_full_size_sampled(stem, c, o_dtype):
         assert np.all(dk[0, pad] == 0.0) and np.all(dv[0, pad] == 0.0)
 
 
-@pytest.mark.parametrize("masked", [False, True])
-def test_bwd_wide_dq_ragged(masked):
+@pytest.mark.parametrize("D,masked", [(128, False), (128, True), (64, False)])
+def test_bwd_wide_dq_ragged(D, masked):
     """A causal backward long enough for the 8-wave dq workgroups (n = 4100,
-    32q/8kv heads, d128: 520 of them, the last 64-position block ragged),
-    with a bf16 O: dQ at stratified rows and at the last 70 rows, dK/dV at
-    16 keys around the middle and at the last 64 keys, against the oracle."""
-    n, Hq, Hkv, D = 4100, 32, 8, 128
-    say(f"bwd wide dq n={n} 32q/8kv masked={masked}")
+    32q/8kv heads: 520 of them, the last 64-position block ragged), with a
+    bf16 O: dQ at stratified rows and at the last 70 rows, dK/dV at 16 keys
+    around the middle and at the last 64 keys, against the oracle."""
+    n, Hq, Hkv = 4100, 32, 8
+    say(f"bwd wide dq n={n} 32q/8kv d{D} masked={masked}")
     q, k, v, do, valid = _inputs(4100 + masked, n, Hq, Hkv, D, masked)
     g = synth.streams(77)
     q_rows = np.unique(np.concatenate([synth.stratified_rows(g[6], n, 16, None if valid is None else valid[0]),
