@@ -628,10 +628,10 @@ __device__ __forceinline__ void dq_issue(uint8_t* stage, uint32_t& vbyte, const 
   const int stride = p.Hkv * D * 2;
   dma_tile<D, L::kBN, NW>(stage + L::kOffK, p.k + off, stride, rows_ok, wave, lane);
   dma_tile<D, L::kBN, NW>(stage + L::kOffV, p.v + off, stride, rows_ok, wave, lane);
-  if (HAS_MASK && tid < L::kBN) {
-    const int key = key0 + tid;
-    vbyte = (key < p.n) ? (p.valid[int64_t(b) * p.n + key] != 0 ? 1u : 0u) : 0u;
-  }
+  // the key-valid byte as loaded (keys past n read key n-1's: the tail
+  // compare masks them); nothing is computed on it before the tile's end, so
+  // the wave does not wait here for this load and the tile's DMA with it
+  if (HAS_MASK && tid < L::kBN) vbyte = p.valid[int64_t(b) * p.n + min(key0 + tid, p.n - 1)];
 }
 
 // One 32-key half of a staged K/V tile against this wave's 32 query rows:

@@ -99,8 +99,11 @@ struct FwdParams {
 
 // DMA the K and V rows of 64-key tile `tile` into the swizzled row-major
 // tiles of `stage` (keys past n read as zero), and load the tile's key-valid
-// bytes into a register of the first 64 threads (stored by the caller once
-// the buffer is free).
+// bytes into a register of the first 64 threads (keys past nk read key
+// nk-1's byte: the tail compare masks them).  The caller turns them into the
+// tile's score bias once the buffer is free; nothing is computed on the byte
+// here, since a use would make the wave wait for this load, and with it for
+// the whole tile's DMA, at the start of its tile.
 template <int NW, int D, bool HAS_MASK>
 __device__ __forceinline__ void fwd_issue(uint8_t* stage, uint32_t& vbyte, const FwdParams& p, int b, int kvh,
                                           int tile, int wave, int lane, int tid) {
@@ -112,10 +115,7 @@ __device__ __forceinline__ void fwd_issue(uint8_t* stage, uint32_t& vbyte, const
   const int stride = p.Hkv * D * 2;
   dma_tile<D, kBN, NW>(stage, p.k + off, stride, rows_ok, wave, lane);
   dma_tile<D, kBN, NW>(stage + L::kBytesK, p.v + off, stride, rows_ok, wave, lane);
-  if (HAS_MASK && tid < kBN) {
-    const int key = key0 + tid;
-    vbyte = (key < p.nk) ? (p.valid[int64_t(b) * p.nk + key] != 0 ? 1u : 0u) : 0u;
-  }
+  if (HAS_MASK && tid < kBN) vbyte = p.valid[int64_t(b) * p.nk + min(key0 + tid, p.nk - 1)];
 }
 
 // KS (key split, 8 waves): two groups of 4 waves take the same rows, the
